@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs for the five workloads (host numpy arrays).
+
+This module only draws random numbers and lays them out in memory; it holds none
+of the arithmetic of the method. Both the HIP path (tests, benchmark) and the CPU
+oracle consume exactly these arrays. Every generator is numpy's default_rng (PCG64)
+with a fixed seed; tensors are drawn in the order listed. 16-bit floats are
+produced from float32 draws by round-to-nearest-even (torch's CPU conversion).
+
+Workloads (sizes are the ones the benchmark runs):
+  gemm_f16_128      M=N=128, K=64 fp16, A and B (N,K) both K-major, U(-1,1), seed 0.
+  add_one_tile      float32 arange(768) viewed as (2,32,3,4).
+  box_copy_bf16     bf16 16381x8190 tensors in a 8192-element row pitch, (128,64)
+                    boxes, 128-byte swizzle; src and the reduce-add target N(0,1),
+                    seed 2; padding and the plain-store target hold a sentinel.
+  gemm_bf16_8192    M=N=K=8192 bf16, A K-major, B stored (K,N) (MN-major),
+                    N(0,1)/sqrt(K), accumulate onto D0 ~ N(0,1) float32, seed 3.
+  mxfp8_8192_16384  M=N=8192, K=16384, E4M3 codes uniform over the 254 finite codes,
+                    E8M0 scales 127+U{-4..4}, both K-major, fresh D, seed 4.
+  mxfp4_16384_8192  M=16384, N=8192, K=8192, E2M1 bytes uniform (two uniform nibbles),
+                    E8M0 scales 127+U{-6..6}, neg_a, fresh D, seed 5.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SENTINEL_BF16 = 0x7FC1  # a NaN payload no kernel produces: marks bytes that must stay untouched
+
+# All E4M3 codes except the two NaN encodings 0x7F and 0xFF (OCP E4M3 "fn").
+FINITE_E4M3 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def to_half_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> raw uint16 bits of fp16/bf16 (round to nearest even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.to(torch.float16 if dtype == "f16" else torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def gemm_f16_128(seed: int = 0, M: int = 128, N: int = 128, K: int = 64):
+    rng = np.random.default_rng(seed)
+    a = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    b = rng.uniform(-1, 1, (N, K)).astype(np.float32)
+    return {"M": M, "N": N, "K": K, "A": to_half_bits(a, "f16"), "B": to_half_bits(b, "f16"),
+            "a_major": "k", "b_major": "k", "accum": 0, "neg_a": 0, "neg_b": 0, "dtype": "f16"}
+
+
+def add_one_tile():
+    return np.arange(768, dtype=np.float32).reshape(2, 32, 3, 4)
+
+
+def box_copy_bf16(seed: int = 2, rows: int = 16381, cols: int = 8190, pitch: int = 8192):
+    """Three (rows, pitch) uint16 buffers holding bf16 bits: src, dst (sentinel), dst_add."""
+    rng = np.random.default_rng(seed)
+    src = np.full((rows, pitch), SENTINEL_BF16, dtype=np.uint16)
+    src[:, :cols] = to_half_bits(rng.standard_normal((rows, cols), dtype=np.float32), "bf16")
+    add = np.full((rows, pitch), SENTINEL_BF16, dtype=np.uint16)
+    add[:, :cols] = to_half_bits(rng.standard_normal((rows, cols), dtype=np.float32), "bf16")
+    dst = np.full((rows, pitch), SENTINEL_BF16, dtype=np.uint16)
+    return {"rows": rows, "cols": cols, "pitch": pitch, "src": src, "dst": dst, "dst_add": add,
+            "box": (128, 64), "estr": (1, 1), "swizzle": 3, "fill": 0, "dtype": "bf16"}
+
+
+def gemm_bf16(seed: int = 3, M: int = 8192, N: int = 8192, K: int = 8192):
+    """A (M,K) K-major, B stored (K,N) (MN-major), D0 (M,N) float32, accumulate."""
+    rng = np.random.default_rng(seed)
+    s = np.float32(1.0 / np.sqrt(K))
+    a = to_half_bits(rng.standard_normal((M, K), dtype=np.float32) * s, "bf16")
+    b = to_half_bits(rng.standard_normal((K, N), dtype=np.float32) * s, "bf16")
+    d0 = rng.standard_normal((M, N), dtype=np.float32)
+    return {"M": M, "N": N, "K": K, "A": a, "B": b, "D0": d0, "lda": K, "ldb": N,
+            "a_major": "k", "b_major": "n", "accum": 1, "neg_a": 0, "neg_b": 0, "dtype": "bf16"}
+
+
+def mxfp8(seed: int = 4, M: int = 8192, N: int = 8192, K: int = 16384, exp_range: int = 4):
+    rng = np.random.default_rng(seed)
+    a = FINITE_E4M3[rng.integers(0, FINITE_E4M3.size, (M, K), dtype=np.int16)]
+    b = FINITE_E4M3[rng.integers(0, FINITE_E4M3.size, (N, K), dtype=np.int16)]
+    sfa = (127 + rng.integers(-exp_range, exp_range + 1, (M, K // 32), dtype=np.int16)).astype(np.uint8)
+    sfb = (127 + rng.integers(-exp_range, exp_range + 1, (N, K // 32), dtype=np.int16)).astype(np.uint8)
+    return {"M": M, "N": N, "K": K, "A": a, "B": b, "SFA": sfa, "SFB": sfb, "lda": K, "ldb": K,
+            "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": "e4m3", "accum": 0, "neg_a": 0, "neg_b": 0}
+
+
+def mxfp4(seed: int = 5, M: int = 16384, N: int = 8192, K: int = 8192, exp_range: int = 6):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    b = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sfa = (127 + rng.integers(-exp_range, exp_range + 1, (M, K // 32), dtype=np.int16)).astype(np.uint8)
+    sfb = (127 + rng.integers(-exp_range, exp_range + 1, (N, K // 32), dtype=np.int16)).astype(np.uint8)
+    return {"M": M, "N": N, "K": K, "A": a, "B": b, "SFA": sfa, "SFB": sfb, "lda": K, "ldb": K,
+            "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": "e2m1", "accum": 0, "neg_a": 1, "neg_b": 0}
+
+
+def sample_points(M: int, N: int, n: int, seed: int = 99):
+    """Output coordinates checked one by one at full size: the four corners, the last
+    row and column, and uniform random points."""
+    rng = np.random.default_rng(seed)
+    pm = [0, 0, M - 1, M - 1] + list(rng.integers(0, M, n)) + [M - 1] * 8 + list(rng.integers(0, M, 8))
+    pn = [0, N - 1, 0, N - 1] + list(rng.integers(0, N, n)) + list(rng.integers(0, N, 8)) + [N - 1] * 8
+    return np.array(pm, dtype=np.int64), np.array(pn, dtype=np.int64)

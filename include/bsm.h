@@ -1,0 +1,199 @@
+/* bsm.h - block-scaled tile-matrix kernels for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsm.so. Every entry point:
+ *   - takes plain host structs, plain device pointers and sizes (no framework types);
+ *   - checks the whole call contract on the host first; on a violation it returns a
+ *     negative bsm_status, records a message for bsm_last_error() and launches nothing;
+ *   - otherwise enqueues its kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and returns BSM_OK without synchronising;
+ *   - never allocates, frees or keeps a pointer after it returns (other than in
+ *     the enqueued work). The caller owns every buffer, keeps it alive until the
+ *     stream work completes, and owns all synchronisation.
+ * Device faults surface asynchronously at the caller's next synchronisation.
+ *
+ * Pages cited (web documentation of Apache TVM "TIRx"):
+ *   [TP]  "Explicit CUDA tile patterns"
+ *   [TMA] "cp.async.bulk.tensor / cp.reduce.async.bulk.tensor"
+ *   [LDM] "ldmatrix / stmatrix"
+ *   [TOE] "Tile Operands and Execution"
+ *   [MMA] "tcgen05.mma"
+ * Storage formats follow the OCP Microscaling Formats (MX) v1.0 specification.
+ */
+#ifndef BSM_H
+#define BSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element storage formats. */
+typedef enum bsm_dtype {
+  BSM_U8 = 0, BSM_U16 = 1, BSM_U32 = 2,
+  BSM_F16 = 3,   /* IEEE binary16 */
+  BSM_BF16 = 4,  /* bfloat16 */
+  BSM_F32 = 5,   /* IEEE binary32 */
+  BSM_E4M3 = 6,  /* OCP fp8 E4M3 ("fn": no infinities, 0x7F/0xFF NaN, max 448) */
+  BSM_E2M1 = 7,  /* OCP fp4 E2M1, two per byte, even element in the low nibble */
+  BSM_E8M0 = 8   /* OCP 8-bit power-of-two scale: 2^(code-127), 0xFF NaN */
+} bsm_dtype;
+
+/* Status codes: one per violated rule. */
+typedef enum bsm_status {
+  BSM_OK = 0,
+  BSM_E_NULL = -1,     /* a required pointer is NULL */
+  BSM_E_RANK = -2,     /* rank not in 1..5, or box rank != tensor rank */
+  BSM_E_BOX = -3,      /* a box extent not in 1..256, or an image larger than 160 KiB */
+  BSM_E_ESTRIDE = -4,  /* an element stride not in 1..8, or the inner one != 1 */
+  BSM_E_ALIGN = -5,    /* base / stride / leading-dimension / image alignment */
+  BSM_E_SWIZZLE = -6,  /* swizzle not in 0..3, or inner image row not allowed for it */
+  BSM_E_FILL = -7,     /* oob_fill not 0/1, or NaN fill on a format without NaN */
+  BSM_E_DTYPE = -8,    /* storage format not supported by this call */
+  BSM_E_SHAPE = -9,    /* negative size, dimension out of range, K not a block multiple */
+  BSM_E_MAJOR = -10,   /* major-order selector not recognised */
+  BSM_E_ALIAS = -11,   /* an output overlaps an input it must not overlap */
+  BSM_E_HIP = -12,     /* the HIP runtime reported an error at launch */
+  BSM_E_ARG = -13      /* any other out-of-contract argument (flags not 0/1, ...) */
+} bsm_status;
+
+/* A rectangular global tensor view ([TMA] "Operand specification": rank, shape and
+ * outer byte strides of the global operand, unit innermost stride).
+ *   base:    device pointer, 16-byte aligned;
+ *   dtype:   a bsm_dtype of whole bytes (E2M1 data is viewed as U8);
+ *   rank:    1..5;
+ *   dims:    extents, outer to inner, each 1..2^31-1;
+ *   strides: byte strides, outer to inner; strides[rank-1] == element size; every
+ *            outer stride a positive multiple of 16.
+ * Element (g_0..g_{r-1}) lives at base + sum_i g_i * strides[i]. */
+typedef struct bsm_tensor {
+  void* base;
+  int32_t dtype;
+  int32_t rank;
+  int64_t dims[5];
+  int64_t strides[5];
+} bsm_tensor;
+
+/* A box and its shared-memory image ([TMA] "Call parameters", "Data representation";
+ * [TP] "TMA").
+ *   box:             extents outer to inner, each 1..256;
+ *   element_strides: sampling steps outer to inner, each 1..8, the inner one 1;
+ *   swizzle:         0/1/2/3 = none / 32 B / 64 B / 128 B;
+ *   oob_fill:        0 = zero, 1 = canonical NaN (F32, F16, BF16, E4M3 only).
+ * The image has extents n_i = ceil(box_i / element_strides_i), is compact row-major
+ * (outer to inner) before swizzling, and image element j holds global coordinate
+ * coords + j * element_strides (the fill value if any coordinate is outside
+ * [0, dims)). Byte offset o of the compact image is stored at swizzle(o), where
+ * swizzle(o) = o ^ ((o >> 3) & m) with m = 0, 16, 48, 112 for modes 0..3 ([TP]
+ * "Shared matrix descriptors" gives mode 3; modes 1 and 2 take the same form over
+ * their 256- and 512-byte periods). The inner image row (n_inner * element size)
+ * must be a multiple of 16 bytes and, when swizzled, at most 16 << swizzle bytes;
+ * the whole image must fit in 160 KiB (one workgroup's LDS). */
+typedef struct bsm_box {
+  int32_t rank;
+  int32_t box[5];
+  int32_t element_strides[5];
+  int32_t swizzle;
+  int32_t oob_fill;
+} bsm_box;
+
+/* Bytes one image occupies in an image buffer: the compact image rounded up to
+ * 128 bytes ([TMA] "Operand specification": every atom origin is 128-byte aligned)
+ * or, when swizzled, to the whole period 2^(7+swizzle). Returns a negative status
+ * for an invalid box or dtype. */
+int64_t bsm_image_stride(const bsm_box* box, int32_t dtype);
+
+/* Box load, global -> image ([TMA] "Call parameters", "Operand specification",
+ * "Example: two explicit 8x16 boxes").
+ *   src:        the global tensor;
+ *   coords_dev: DEVICE array of n_boxes * rank int32 starting coordinates, box t's
+ *               coordinates at [t*rank .. t*rank+rank), outer to inner; any value,
+ *               out-of-range elements take the fill;
+ *   images:     DEVICE buffer, n_boxes * bsm_image_stride() bytes, aligned to 128
+ *               bytes (to the swizzle period when swizzled); image t at
+ *               t * bsm_image_stride(); padding bytes between images are not written.
+ * n_boxes == 0 is a no-op. images must not overlap src's byte range. */
+int bsm_tile_box_load(const bsm_tensor* src, const bsm_box* box, const int32_t* coords_dev,
+                      int64_t n_boxes, void* images, void* stream);
+
+/* Box store or add-reduction, image -> global ([TMA] "Stores, reductions, and
+ * completion").  Same box, coordinate and image contract as bsm_tile_box_load.
+ * Elements whose coordinate is out of range are not written. reduce_add = 1 adds
+ * each image element into the destination, dst <- round_to_nearest_even(dst + x) in
+ * the destination format (F32, F16, BF16); the destination holds its starting value.
+ * Boxes that overlap in global memory race (store) or are summed in an unspecified
+ * order (reduce). images must not overlap dst's byte range. */
+int bsm_tile_box_store(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev,
+                       int64_t n_boxes, const void* images, int reduce_add, void* stream);
+
+/* Grid round trip through LDS: for every tile coordinate t*box (t over
+ * ceil(dims/box) per axis) the box of `src` is loaded into a swizzled LDS image,
+ * which is then stored to `dst` and/or add-reduced into `dst_add` at the same
+ * coordinates ([TMA] "Operand specification" and "Stores, reductions, and
+ * completion"). dst or dst_add may be NULL, not both. All three tensors share
+ * dtype, rank and dims (strides may differ) and must not overlap one another.
+ * The boxes do not overlap, so the result is unique. */
+int bsm_tile_box_copy(const bsm_tensor* src, const bsm_tensor* dst, const bsm_tensor* dst_add,
+                      const bsm_box* box, void* stream);
+
+/* Dense GEMM ([MMA] "Call parameters", "Operand specification", "Code generation",
+ * "Example: four K16 issues"; [TP] "Warp MMA", "tcgen05 MMA"):
+ *   D[m,n] = (accum ? D[m,n] : 0) + s * sum_k A(m,k) * B(n,k),  s = (-1)^(neg_a+neg_b),
+ * products and sums in float32, D float32 row-major (D[m*ldd + n]).
+ *   ab:      BSM_F16 or BSM_BF16 (both operands);
+ *   a_major: 'k': A(m,k) = A[m*lda + k] (lda >= K);  'm': A(m,k) = A[k*lda + m] (lda >= M);
+ *   b_major: 'k': B(n,k) = B[n*ldb + k] (ldb >= K);  'n': B(n,k) = B[k*ldb + n] (ldb >= N);
+ *   A, B 16-byte aligned, lda and ldb multiples of 8; D 16-byte aligned, ldd >= N and
+ *   a multiple of 4; M, N, K >= 0 (M or N == 0: no-op; K == 0: D = accum ? D : 0);
+ *   neg_a, neg_b, accum in {0, 1}. With accum == 0, D is never read. A and B must
+ *   not overlap D. */
+int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab,
+             const void* A, int64_t lda, char a_major,
+             const void* B, int64_t ldb, char b_major,
+             float* D, int64_t ldd, int neg_a, int neg_b, int accum, void* stream);
+
+/* Block-scaled GEMM ([MMA] "Weight-stationary and block scaling", "Call parameters";
+ * [TP] "tcgen05 MMA"), both operands K-major:
+ *   A(m,k) = dec(A[m*lda + k]) * 2^(SFA[m*ld_sfa + k/32] - 127),
+ *   B(n,k) = dec(B[n*ldb + k]) * 2^(SFB[n*ld_sfb + k/32] - 127),
+ *   D[m,n] = (accum ? D[m,n] : 0) + s * sum_k A(m,k) * B(n,k), float32 accumulation.
+ * One E8M0 scale per 32 consecutive K elements (OCP MX block size 32); a scale code
+ * of 0xFF (NaN) makes every product of its block NaN.
+ *   a_fmt, b_fmt: BSM_E4M3 or BSM_E2M1, equal (mixed formats are rejected);
+ *   lda, ldb in elements; E2M1 element index i is the (i & 1) nibble of byte i/2
+ *   (low nibble first); rows 16-byte aligned (lda bytes a multiple of 16);
+ *   K a multiple of 32; ld_sfa >= K/32, ld_sfb >= K/32;
+ *   D as for bsm_gemm. A, B, SFA, SFB must not overlap D. */
+int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K,
+                         int32_t a_fmt, const void* A, int64_t lda, const uint8_t* SFA, int64_t ld_sfa,
+                         int32_t b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
+                         float* D, int64_t ldd, int neg_a, int neg_b, int accum, void* stream);
+
+/* Element-wise scalar add on float32 ([TOE] "A Load, Compute, and Store Example"
+ * adds one to a (2,32,3,4) tile; [TP] "Scalar compositions"): dst[i] = src[i] + s,
+ * i < n, each lane moving 16-byte vectors. src, dst 16-byte aligned; they may be
+ * equal (in place) but must not otherwise overlap. n >= 0. */
+int bsm_tile_add_scalar_f32(const float* src, float* dst, int64_t n, float s, void* stream);
+
+/* Diagnostic: the LDS -> register fragment load of the dense GEMM ([LDM]
+ * "Address providers and result owners", "Transpose and stores"; [TP] "ldmatrix
+ * with interleaved rows and separated registers"). One operand tile of
+ * bsm_debug_fragment_shape() rows x kdim 16-bit elements is read from `src`
+ * (major 'k': src[r*kdim + k]; major 'm': src[k*rows + r]), staged into LDS with
+ * the GEMM's own loader and swizzle, and read back with the GEMM's own fragment
+ * reads (16-byte reads for 'k', transposing 16-bit reads for 'm'). For every
+ * 32-row block b, 16-wide K step s, lane l and element e, the value the lane holds
+ * for operand (row 32b + l%32, k 16s + 8(l/32) + e) is written to
+ * dump[((b * (kdim/16) + s) * 64 + l) * 8 + e]. rows/kdim must equal the shape
+ * returned by bsm_debug_fragment_shape. */
+int bsm_debug_fragments(const uint16_t* src, int64_t rows, int64_t kdim, char major,
+                        uint16_t* dump, void* stream);
+void bsm_debug_fragment_shape(int64_t* rows, int64_t* kdim);
+
+/* Message describing the last nonzero status returned on this thread. */
+const char* bsm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSM_H */

@@ -1,0 +1,124 @@
+"""Pins of the oracle's decoders and encoders against independent libraries and closed forms.
+
+Decoders are checked code by code against torch's / numpy's own conversions (for
+e4m3 and e8m0: torch.float8_e4m3fn / float8_e8m0fnu, the OCP formats), and the
+e2m1 table against the value list of the OCP MX v1.0 specification (section 5.3.3).
+Encoders (round to nearest even) are checked against numpy / torch float64 casts on
+values chosen to hit ties, subnormals, carries and overflow.
+"""
+import numpy as np
+import pytest
+import torch
+
+
+def _same(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    both_nan = np.isnan(a) & np.isnan(b)
+    eq = (a == b) & (np.signbit(a) == np.signbit(b))
+    return bool(np.all(both_nan | eq))
+
+
+def test_e4m3_all_codes_vs_torch(O):
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.decode("e4m3", codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert _same(got, ref)
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.isfinite(got).sum() == 254
+
+
+def test_e8m0_all_codes_vs_torch_and_closed_form(O):
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.decode("e8m0", codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert _same(got, ref)
+    assert all(got[c] == 2.0 ** (c - 127) for c in range(255)) and np.isnan(got[255])
+
+
+def test_e2m1_table_and_nibble_order(O):
+    # OCP MX v1.0 E2M1 values for codes 0..7; bit 3 is the sign.
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    packed = np.array([(2 * i + 1) << 4 | (2 * i) for i in range(8)], dtype=np.uint8)  # codes 0..15
+    got = O.decode("e2m1", packed, 16)
+    exp = np.array(table + [-v for v in table])
+    assert _same(got, exp)
+    assert np.signbit(got[8])  # code 8 is -0
+    # low nibble is element 0: byte 0x2F -> element0 = code 0xF (-6), element1 = code 2 (1.0)
+    assert list(O.decode("e2m1", np.array([0x2F], np.uint8), 2)) == [-6.0, 1.0]
+
+
+def test_f16_bf16_f32_decoders(O):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    assert _same(O.decode("f16", h), h.view(np.float16).astype(np.float64))
+    ref_bf = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert _same(O.decode("bf16", h), ref_bf)
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    u[:6] = [0, 0x80000000, 1, 0x7F800000, 0xFF800000, 0x007FFFFF]
+    assert _same(O.decode("f32", u), u.view(np.float32).astype(np.float64))
+
+
+def _encode_cases():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(20000) * np.exp2(rng.integers(-150, 130, 20000)),
+        np.exp2(rng.integers(-160, 140, 3000).astype(np.float64)) * (1 + rng.integers(0, 512, 3000) / 512.0),
+        [0.0, -0.0, np.inf, -np.inf, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -11, 1 + 3 * 2 ** -11,
+         1 + 2 ** -24, 1 + 3 * 2 ** -24, 65504.0, 65520.0, 65519.99, 2 ** -25, 2 ** -24 * 1.5, 3.4e38, 3.5e38],
+    ])
+    return x.astype(np.float64)
+
+
+def test_enc_bf16_vs_torch(O):
+    # torch rounds float64 -> bfloat16 through float32 (two roundings), so the library
+    # reference is taken on float32-representable inputs, where it rounds once.
+    with np.errstate(over="ignore"):
+        x = _encode_cases().astype(np.float32).astype(np.float64)
+    got = O.enc("bf16", x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_enc_bf16_single_rounding_exact(O):
+    # Exact rational check on random doubles: the encoded value is the nearer of the
+    # two bfloat16 neighbours (ties to even mantissa), never a double-rounded one.
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    xs = list(rng.uniform(1, 2, 300) * np.exp2(rng.integers(-120, 120, 300))) + [1.2074678329077994e-34]
+    for x in xs:
+        b = int(O.enc("bf16", [x])[0])
+        v = Fraction(float(np.array([b << 16], np.uint32).view(np.float32)[0]))
+        up = Fraction(float(np.array([(b + 1) << 16], np.uint32).view(np.float32)[0]))
+        dn = Fraction(float(np.array([(b - 1) << 16], np.uint32).view(np.float32)[0]))
+        fx = Fraction(x)
+        assert abs(fx - v) <= abs(fx - up) and abs(fx - v) <= abs(fx - dn)
+        if abs(fx - v) == abs(fx - up) or abs(fx - v) == abs(fx - dn):
+            assert b % 2 == 0
+
+
+def test_enc_f16_vs_numpy(O):
+    x = _encode_cases()
+    got = O.enc("f16", x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_enc_f32_vs_numpy(O):
+    x = _encode_cases()
+    got = O.enc("f32", x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32).view(np.uint32)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_encode_decode_roundtrip(O, dt):
+    rng = np.random.default_rng(3)
+    n = 5000
+    bits = rng.integers(0, 2 ** (32 if dt == "f32" else 16), n, dtype=np.uint64)
+    bits = bits.astype(np.uint32 if dt == "f32" else np.uint16)
+    vals = O.decode(dt, bits)
+    keep = ~np.isnan(vals)
+    back = O.enc(dt, vals[keep])
+    assert np.array_equal(back, bits[keep])

@@ -1,0 +1,222 @@
+"""Benchmark of the block-scaled tile-matrix hot path on one MI355X.
+
+One step runs every row of the hot path once, on seeded synthetic inputs already
+resident in HBM, on one HIP stream:
+  box_copy   bf16 16381x8190 (8192-element pitch), (128,64) boxes, 128-byte swizzle:
+             load every box into LDS, store it to a second tensor, add-reduce it into a third
+  gemm_bf16  M=N=K=8192 bf16, A K-major, B MN-major, accumulate onto float32 D
+  gemm_mxfp8 M=N=8192, K=16384, E4M3 + E8M0 scales per 32 K, fresh D
+  gemm_mxfp4 M=16384, N=8192, K=8192, E2M1 + E8M0 scales per 32 K, neg_a, fresh D
+  add_one    the (2,32,3,4) float32 tile plus one
+Prints one JSON line. `value` is the step's GEMM work (sum of 2*M*N*K of the three
+GEMMs) divided by the measured step time; every kernel's own rate and roofline
+fraction is in `per_kernel`, from HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm_GBs": 8000.0, "bf16_TFs": 2516.6, "fp8_TFs": 5033.2, "fp4_TFs": 10066.3}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def make_inputs():
+    import numpy as np
+    import torch
+
+    from block_scaled_matrix_amd import workloads as W
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t0 = time.time()
+    inp = {}
+    bc = W.box_copy_bf16()
+    inp["box"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in bc.items()}
+    log(f"box_copy inputs {time.time() - t0:.1f}s")
+    g = W.gemm_bf16()
+    inp["bf16"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    log(f"gemm_bf16 inputs {time.time() - t0:.1f}s")
+    g = W.mxfp8()
+    inp["fp8"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    inp["fp8"]["D"] = torch.empty((g["M"], g["N"]), dtype=torch.float32, device="cuda")
+    log(f"mxfp8 inputs {time.time() - t0:.1f}s")
+    g = W.mxfp4()
+    inp["fp4"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    inp["fp4"]["D"] = torch.empty((g["M"], g["N"]), dtype=torch.float32, device="cuda")
+    log(f"mxfp4 inputs {time.time() - t0:.1f}s")
+    inp["add"] = dev(W.add_one_tile())
+    inp["add_out"] = torch.empty_like(inp["add"])
+    return inp
+
+
+def kernels(inp):
+    """(name, launch callable, work, unit, peak) for each row of the step."""
+    import block_scaled_matrix_amd as bsm
+
+    b = inp["box"]
+    rows, cols, pitch = b["rows"], b["cols"], b["pitch"]
+    st = (pitch * 2, 2)
+    td = lambda t: bsm.tensor_desc(t, "bf16", (rows, cols), st)
+    src, dst, add = td(b["src"]), td(b["dst"]), td(b["dst_add"])
+    box = bsm.box_desc(b["box"], (1, 1), 3, 0)
+    box_bytes = 4 * rows * cols * 2            # read src + write dst + read/write dst_add (logical elements)
+
+    g = inp["bf16"]
+    M, N, K = g["M"], g["N"], g["K"]
+    f8, f4 = inp["fp8"], inp["fp4"]
+    ks = [
+        ("box_copy", lambda: bsm.bsm_tile_box_copy(src, dst, add, box), box_bytes, "GB/s", PEAK["hbm_GBs"]),
+        ("gemm_bf16", lambda: bsm.bsm_gemm(M, N, K, "bf16", g["A"], K, "k", g["B"], N, "n", g["D0"], N, 0, 0, 1),
+         2.0 * M * N * K, "TFLOP/s", PEAK["bf16_TFs"]),
+        ("gemm_mxfp8", lambda: bsm.bsm_gemm_block_scale(
+            f8["M"], f8["N"], f8["K"], "e4m3", f8["A"], f8["lda"], f8["SFA"], f8["ld_sfa"], "e4m3", f8["B"], f8["ldb"],
+            f8["SFB"], f8["ld_sfb"], f8["D"], f8["N"], 0, 0, 0), 2.0 * f8["M"] * f8["N"] * f8["K"], "TFLOP/s",
+         PEAK["fp8_TFs"]),
+        ("gemm_mxfp4", lambda: bsm.bsm_gemm_block_scale(
+            f4["M"], f4["N"], f4["K"], "e2m1", f4["A"], f4["lda"], f4["SFA"], f4["ld_sfa"], "e2m1", f4["B"], f4["ldb"],
+            f4["SFB"], f4["ld_sfb"], f4["D"], f4["N"], 1, 0, 0), 2.0 * f4["M"] * f4["N"] * f4["K"], "TFLOP/s",
+         PEAK["fp4_TFs"]),
+        ("add_one", lambda: bsm.bsm_tile_add_scalar_f32(inp["add"], inp["add_out"], 768, 1.0), 2 * 768 * 4, "GB/s",
+         PEAK["hbm_GBs"]),
+    ]
+    return ks
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded sample of the same workloads."""
+    import numpy as np
+
+    from block_scaled_matrix_amd import workloads as W
+    from oracle import oracle as O
+
+    O.lib()
+    flops = 0.0
+    t_gemm = 0.0
+    g = W.gemm_bf16()
+    rows = 8
+    t0 = time.perf_counter()
+    O.gemm(g["M"], g["N"], g["K"], "bf16", g["A"], g["K"], "k", g["B"], g["N"], "n", g["D0"], g["N"], 0, 0, 1, 0, rows)
+    t_gemm += time.perf_counter() - t0
+    flops += 2.0 * rows * g["N"] * g["K"]
+    del g
+    g = W.mxfp8()
+    t0 = time.perf_counter()
+    O.gemm_block_scale(g["M"], g["N"], g["K"], "e4m3", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e4m3", g["B"], g["K"],
+                       g["SFB"], g["ld_sfb"], None, 0, 0, 0, 0, 0, 2)
+    t_gemm += time.perf_counter() - t0
+    flops += 2.0 * 2 * g["N"] * g["K"]
+    del g
+    g = W.mxfp4()
+    t0 = time.perf_counter()
+    O.gemm_block_scale(g["M"], g["N"], g["K"], "e2m1", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e2m1", g["B"], g["K"],
+                       g["SFB"], g["ld_sfb"], None, 0, 1, 0, 0, 0, 4)
+    t_gemm += time.perf_counter() - t0
+    flops += 2.0 * 4 * g["N"] * g["K"]
+    del g
+    # box round trip on a 1024-row band of the copy workload (128 boxes wide)
+    b = W.box_copy_bf16(rows=1024)
+    t0 = time.perf_counter()
+    O.box_copy_grid(b["src"], b["dst"], b["dst_add"], "bf16", (1024, b["cols"]), (b["pitch"] * 2, 2), b["box"], (1, 1),
+                    3, 0)
+    t_box = time.perf_counter() - t0
+    box_gbs = 4 * 1024 * b["cols"] * 2 / t_box / 1e9
+    return {"value": flops / t_gemm / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"GEMM rows: bf16 8 of 8192, mxfp8 2 of 8192, mxfp4 4 of 16384 (full N and K), "
+                      f"{t_gemm:.1f} s; box copy on a 1024x8190 band: {box_gbs:.3f} GB/s in {t_box:.1f} s",
+            "box_copy_GBs": box_gbs}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); every workload here fits one MI355X and "
+              "no multi-GPU path is part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_matrix_amd as bsm
+    bsm.lib()
+    torch.cuda.set_device(0)
+    inp = make_inputs()
+    ks = kernels(inp)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for _, fn, *_ in ks:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
+          for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for i, (_, fn, *_) in enumerate(ks):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms)")
+
+    per = {}
+    for i, (name, _, work, unit, peak) in enumerate(ks):
+        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        per[name] = {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
+                     "frac": round(rate / peak, 4), "work_per_launch": work}
+        log(f"{name}: {ms:.4f} ms  {rate:.1f} {unit}  ({100 * rate / peak:.1f}% of {peak})")
+    dom = max((n for n in per if n != "add_one"), key=lambda n: per[n]["ms"])
+    d = per[dom]
+    gemm_flops = sum(k[2] for k in ks if k[0].startswith("gemm"))
+    value = gemm_flops / (ms_step * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": "GEMM TFLOP/s (% MFMA peak) bf16/MXFP8/MXFP4; box-copy GB/s (% HBM)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 / e4m3 / e2m1 operands, f32 accumulate; bf16 box copy", "data": "synthetic",
+        "config": {"workload": "box_copy bf16 16381x8190 (128,64) swz128 + gemm bf16 8192^3 (B MN-major, accum) + "
+                               "mxfp8 8192x8192x16384 + mxfp4 16384x8192x8192 (neg_a) + add_one (2,32,3,4)",
+                   "seeds": {"box_copy": 2, "gemm_bf16": 3, "mxfp8": 4, "mxfp4": 5}},
+        "per_kernel": per,
+        "roofline": {"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
+                     "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,45 @@
+"""Builds libbsm.so (the gfx950 HIP library) in place with hipcc."""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libbsm.so")
+SOURCES = ["bsm_api.hip", "k_tile.hip", "k_gemm_dense.hip", "k_gemm_mx.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -packed-fp32-ops: never emit packed fp32 arithmetic (v_pk_*_f32).
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _compile(src: str, obj: str) -> None:
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    for line in r.stderr.splitlines():
+        if "warning" in line and "packed-fp32-ops" not in line:
+            print(line)
+
+
+def build(jobs: int = 4) -> str:
+    """Compile every source for gfx950 and link libbsm.so next to this file."""
+    with tempfile.TemporaryDirectory(prefix="bsm_build_") as tmp:
+        objs = [os.path.join(tmp, s.replace(".hip", ".o")) for s in SOURCES]
+        with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(_compile, SOURCES, objs))
+        out = LIB + ".tmp"
+        r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(out, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

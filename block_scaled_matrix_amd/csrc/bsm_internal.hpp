@@ -1,0 +1,61 @@
+// bsm_internal.hpp - launch interface between the validated C ABI (bsm_api.hip) and
+// the kernels. Arguments reaching these functions have passed every contract check.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsm {
+
+// Geometry of one box over one global tensor, as the kernels consume it.
+struct BoxGeom {
+  int32_t rank;
+  int32_t esize;        // element bytes: 1, 2 or 4
+  int32_t dtype;        // bsm_dtype
+  int32_t swizzle;      // 0..3
+  int32_t fill;         // 0 zero, 1 NaN
+  uint32_t fill_bits;   // the fill element's bit pattern
+  int32_t row_bytes;    // inner image row: ext[rank-1] * esize (multiple of 16)
+  int32_t nrows;        // product of the outer image extents
+  int64_t image_bytes;  // compact image bytes = nrows * row_bytes
+  int64_t image_stride; // bytes between consecutive images in an image buffer
+  int64_t dims[5];
+  int64_t strides[5];   // bytes
+  int32_t box[5];
+  int32_t estr[5];
+  int32_t ext[5];       // image extents ceil(box / estr)
+};
+
+// D[m*ldd + n] = 0 for m < M, n < N (a kernel, so the call can be graph-captured).
+hipError_t launch_zero_f32_2d(float* D, int64_t ldd, int64_t M, int64_t N, hipStream_t st);
+
+hipError_t launch_add_scalar_f32(const float* src, float* dst, int64_t n, float s, hipStream_t st);
+
+hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coords, int64_t n_boxes,
+                           void* images, hipStream_t st);
+hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, int64_t n_boxes,
+                            const void* images, int reduce_add, hipStream_t st);
+// Grid round trip; dst_strides / add_strides describe dst and dst_add (NULL allowed).
+hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const int64_t* dst_strides,
+                           void* dst_add, const int64_t* add_strides, hipStream_t st);
+
+struct GemmArgs {
+  int64_t M, N, K;
+  int32_t dtype;        // BSM_F16 / BSM_BF16 (dense) or BSM_E4M3 / BSM_E2M1 (block scaled)
+  const void* A; int64_t lda; int32_t a_kmajor;
+  const void* B; int64_t ldb; int32_t b_kmajor;
+  const uint8_t* SFA; int64_t ld_sfa;
+  const uint8_t* SFB; int64_t ld_sfb;
+  float* D; int64_t ldd;
+  int32_t negate;       // neg_a xor neg_b
+  int32_t accum;
+};
+
+hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
+
+// Operand-tile geometry of the dense GEMM (rows x K elements per LDS stage).
+constexpr int kDenseTileRows = 256;
+constexpr int kDenseTileK = 64;
+hipError_t launch_debug_fragments(const uint16_t* src, int kmajor, uint16_t* dump, hipStream_t st);
+
+}  // namespace bsm

@@ -1,0 +1,288 @@
+// k_tile.hip - element-wise tile kernel and the box load / store / reduce-add kernels.
+//
+// Box semantics ("cp.async.bulk.tensor / cp.reduce.async.bulk.tensor", Call
+// parameters, Data representation, Operand specification, Stores, reductions and
+// completion): image element j holds global coordinate coords + j*element_strides,
+// out-of-range coordinates read the fill value and are never written; the image is
+// compact row-major before a 16-byte-chunk XOR swizzle.
+//
+// Work mapping: one workgroup (256 lanes) per box; the image is cut into 16-byte
+// chunks (an image row is a whole number of them) and lane i moves chunks
+// i, i+256, ... . A chunk whose 16 global bytes are in range and 16-byte aligned
+// moves with one 128-bit access; any other chunk is assembled element by element.
+#include "bsm_device.hpp"
+#include "bsm_internal.hpp"
+#include "../../include/bsm.h"
+
+namespace bsm {
+
+// ------------------------------------------------------------------ add scalar
+// "Tile Operands and Execution", A Load, Compute, and Store Example: 64 lanes,
+// each with three 4-word loads, twelve scalar adds and three 4-word stores.
+// One wave64 covers a (2,32,3,4) float32 tile; lane t owns floats 12t..12t+11.
+__global__ __launch_bounds__(64) void k_add_scalar_f32(const float* __restrict__ src, float* dst, int64_t n, float s) {
+  const int64_t base = (int64_t)blockIdx.x * 768 + 12 * threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < 3; r++) {
+    const int64_t i = base + 4 * r;
+    if (i + 4 <= n) {
+      float4 v = *(const float4*)(src + i);
+      v.x += s; v.y += s; v.z += s; v.w += s;
+      *(float4*)(dst + i) = v;
+    } else {
+      for (int64_t e = i; e < n && e < i + 4; e++) dst[e] = src[e] + s;
+    }
+  }
+}
+
+hipError_t launch_add_scalar_f32(const float* src, float* dst, int64_t n, float s, hipStream_t st) {
+  const int64_t blocks = (n + 767) / 768;
+  hipLaunchKernelGGL(k_add_scalar_f32, dim3((unsigned)blocks), dim3(64), 0, st, src, dst, n, s);
+  return hipGetLastError();
+}
+
+// Grid-stride over (row, 256-column block) pairs.
+__global__ __launch_bounds__(256) void k_zero_f32_2d(float* D, int64_t ldd, int64_t M, int64_t N) {
+  const int64_t cb = (N + 255) / 256;
+  for (int64_t b = blockIdx.x; b < M * cb; b += gridDim.x) {
+    const int64_t row = b / cb, col = (b - row * cb) * 256 + threadIdx.x;
+    if (col < N) D[row * ldd + col] = 0.0f;
+  }
+}
+
+hipError_t launch_zero_f32_2d(float* D, int64_t ldd, int64_t M, int64_t N, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int64_t blocks = M * ((N + 255) / 256);
+  const unsigned g = (unsigned)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(k_zero_f32_2d, dim3(g), dim3(256), 0, st, D, ldd, M, N);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ box helpers
+struct RowPos {
+  bool ok;       // every outer coordinate in range
+  int64_t off;   // byte offset of the row's outer coordinates (valid when ok)
+};
+
+// Outer coordinates of image row r: unravel r over ext[0..rank-2] (row-major),
+// g_i = c_i + j_i * estr_i.
+__device__ __forceinline__ RowPos row_pos(const BoxGeom& g, const int32_t* c, const int64_t* strides, int r) {
+  RowPos p{true, 0};
+  const int in = g.rank - 1;
+  int rem = r;
+#pragma unroll
+  for (int i = 3; i >= 0; i--) {
+    if (i < in) {
+      const int j = rem % g.ext[i];
+      rem /= g.ext[i];
+      const int64_t gi = (int64_t)c[i] + (int64_t)j * g.estr[i];
+      if (gi < 0 || gi >= g.dims[i]) p.ok = false;
+      else p.off += gi * strides[i];
+    }
+  }
+  return p;
+}
+
+__device__ __forceinline__ uint32_t load_elem(const uint8_t* p, int esize) {
+  if (esize == 1) return *p;
+  if (esize == 2) return *(const uint16_t*)p;
+  return *(const uint32_t*)p;
+}
+
+__device__ __forceinline__ void store_elem(uint8_t* p, int esize, uint32_t v) {
+  if (esize == 1) *p = (uint8_t)v;
+  else if (esize == 2) *(uint16_t*)p = (uint16_t)v;
+  else *(uint32_t*)p = v;
+}
+
+__device__ __forceinline__ uint32_t get_elem(const uint4& v, int esize, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int bit = e * esize * 8;
+  const uint32_t word = w[bit >> 5];
+  if (esize == 4) return word;
+  const uint32_t mask = esize == 2 ? 0xFFFFu : 0xFFu;
+  return (word >> (bit & 31)) & mask;
+}
+
+__device__ __forceinline__ void put_elem(uint4& v, int esize, int e, uint32_t x) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int bit = e * esize * 8;
+  if (esize == 4) w[bit >> 5] = x;
+  else {
+    const uint32_t mask = (esize == 2 ? 0xFFFFu : 0xFFu) << (bit & 31);
+    w[bit >> 5] = (w[bit >> 5] & ~mask) | ((x << (bit & 31)) & mask);
+  }
+  v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Element-wise add of two elements of a float format, rounded once (RNE) to the format.
+__device__ __forceinline__ uint32_t add_elem(int dtype, uint32_t a, uint32_t b) {
+  if (dtype == BSM_F32) return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+  if (dtype == BSM_BF16) return f32_to_bf16_bits(bf16_bits_to_f32((uint16_t)a) + bf16_bits_to_f32((uint16_t)b));
+  return f32_to_f16_bits(f16_bits_to_f32((uint16_t)a) + f16_bits_to_f32((uint16_t)b));
+}
+
+__device__ __forceinline__ uint4 add_chunk(int dtype, uint4 a, uint4 b) {
+  if (dtype == BSM_F32) {
+    return make_uint4(add_elem(dtype, a.x, b.x), add_elem(dtype, a.y, b.y), add_elem(dtype, a.z, b.z),
+                      add_elem(dtype, a.w, b.w));
+  }
+  uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w}, wr[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t lo = add_elem(dtype, wa[i] & 0xFFFFu, wb[i] & 0xFFFFu);
+    const uint32_t hi = add_elem(dtype, wa[i] >> 16, wb[i] >> 16);
+    wr[i] = lo | (hi << 16);
+  }
+  return make_uint4(wr[0], wr[1], wr[2], wr[3]);
+}
+
+// Global -> 16-byte image chunk (row r, chunk cc of the row).
+__device__ __forceinline__ uint4 gather_chunk(const BoxGeom& g, const uint8_t* src, const int32_t* c, int r, int cc) {
+  const RowPos rp = row_pos(g, c, g.strides, r);
+  const int in = g.rank - 1;
+  const int epc = 16 / g.esize;
+  const int64_t g0 = (int64_t)c[in] + (int64_t)cc * epc;
+  const uint8_t* p = src + rp.off + g0 * g.esize;
+  if (rp.ok && g0 >= 0 && g0 + epc <= g.dims[in] && (((uintptr_t)p) & 15) == 0) return *(const uint4*)p;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  for (int e = 0; e < epc; e++) {
+    const int64_t gi = g0 + e;
+    const bool ok = rp.ok && gi >= 0 && gi < g.dims[in];
+    put_elem(v, g.esize, e, ok ? load_elem(src + rp.off + gi * g.esize, g.esize) : g.fill_bits);
+  }
+  return v;
+}
+
+// 16-byte image chunk -> global (store or add-reduce), in-range elements only.
+__device__ __forceinline__ void scatter_chunk(const BoxGeom& g, uint8_t* dst, const int64_t* strides, const int32_t* c,
+                                              int r, int cc, uint4 v, bool reduce) {
+  const RowPos rp = row_pos(g, c, strides, r);
+  if (!rp.ok) return;
+  const int in = g.rank - 1;
+  const int epc = 16 / g.esize;
+  const int64_t g0 = (int64_t)c[in] + (int64_t)cc * epc;
+  uint8_t* p = dst + rp.off + g0 * g.esize;
+  if (g0 >= 0 && g0 + epc <= g.dims[in] && (((uintptr_t)p) & 15) == 0) {
+    if (reduce) v = add_chunk(g.dtype, *(const uint4*)p, v);
+    *(uint4*)p = v;
+    return;
+  }
+  for (int e = 0; e < epc; e++) {
+    const int64_t gi = g0 + e;
+    if (gi < 0 || gi >= g.dims[in]) continue;
+    uint8_t* q = dst + rp.off + gi * g.esize;
+    uint32_t x = get_elem(v, g.esize, e);
+    if (reduce) x = add_elem(g.dtype, load_elem(q, g.esize), x);
+    store_elem(q, g.esize, x);
+  }
+}
+
+// ------------------------------------------------------------------ box load / store
+__global__ __launch_bounds__(256) void k_box_load(BoxGeom g, const uint8_t* __restrict__ src,
+                                                  const int32_t* __restrict__ coords, uint8_t* __restrict__ images) {
+  const int64_t t = blockIdx.x;
+  int32_t c[5];
+#pragma unroll
+  for (int i = 0; i < 5; i++) c[i] = i < g.rank ? coords[t * g.rank + i] : 0;
+  uint8_t* img = images + t * g.image_stride;
+  const int cpr = g.row_bytes >> 4;
+  const int nchunks = g.nrows * cpr;
+  for (int q = threadIdx.x; q < nchunks; q += 256) {
+    const int r = q / cpr, cc = q - r * cpr;
+    const uint4 v = gather_chunk(g, src, c, r, cc);
+    *(uint4*)(img + image_swizzle((uint32_t)(r * g.row_bytes + cc * 16), g.swizzle)) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_box_store(BoxGeom g, uint8_t* dst, const int32_t* __restrict__ coords,
+                                                   const uint8_t* __restrict__ images, int reduce) {
+  const int64_t t = blockIdx.x;
+  int32_t c[5];
+#pragma unroll
+  for (int i = 0; i < 5; i++) c[i] = i < g.rank ? coords[t * g.rank + i] : 0;
+  const uint8_t* img = images + t * g.image_stride;
+  const int cpr = g.row_bytes >> 4;
+  const int nchunks = g.nrows * cpr;
+  for (int q = threadIdx.x; q < nchunks; q += 256) {
+    const int r = q / cpr, cc = q - r * cpr;
+    const uint4 v = *(const uint4*)(img + image_swizzle((uint32_t)(r * g.row_bytes + cc * 16), g.swizzle));
+    scatter_chunk(g, dst, g.strides, c, r, cc, v, reduce != 0);
+  }
+}
+
+hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coords, int64_t n_boxes, void* images,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(k_box_load, dim3((unsigned)n_boxes), dim3(256), 0, st, g, (const uint8_t*)src, coords,
+                     (uint8_t*)images);
+  return hipGetLastError();
+}
+
+hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, int64_t n_boxes, const void* images,
+                            int reduce_add, hipStream_t st) {
+  hipLaunchKernelGGL(k_box_store, dim3((unsigned)n_boxes), dim3(256), 0, st, g, (uint8_t*)dst, coords,
+                     (const uint8_t*)images, reduce_add);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ grid round trip
+struct CopyOut {
+  int64_t dst_strides[5];
+  int64_t add_strides[5];
+};
+
+// One workgroup per tile coordinate t*box: global -> swizzled LDS image -> dst / dst_add.
+__global__ __launch_bounds__(256) void k_box_copy(BoxGeom g, CopyOut o, const uint8_t* __restrict__ src,
+                                                  uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_add) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t image[];
+  int32_t c[5];
+  int64_t rem = blockIdx.x;
+#pragma unroll
+  for (int i = 4; i >= 0; i--) {
+    c[i] = 0;
+    if (i < g.rank) {
+      const int64_t tiles = (g.dims[i] + g.box[i] - 1) / g.box[i];
+      c[i] = (int32_t)((rem % tiles) * g.box[i]);
+      rem /= tiles;
+    }
+  }
+  const int cpr = g.row_bytes >> 4;
+  const int nchunks = g.nrows * cpr;
+  for (int q = threadIdx.x; q < nchunks; q += 256) {
+    const int r = q / cpr, cc = q - r * cpr;
+    const uint4 v = gather_chunk(g, src, c, r, cc);
+    lds_write_b128(image + image_swizzle((uint32_t)(r * g.row_bytes + cc * 16), g.swizzle), v);
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < nchunks; q += 256) {
+    const int r = q / cpr, cc = q - r * cpr;
+    const uint4 v = lds_read_b128(image + image_swizzle((uint32_t)(r * g.row_bytes + cc * 16), g.swizzle));
+    if (dst) scatter_chunk(g, dst, o.dst_strides, c, r, cc, v, false);
+    if (dst_add) scatter_chunk(g, dst_add, o.add_strides, c, r, cc, v, true);
+  }
+}
+
+hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const int64_t* dst_strides, void* dst_add,
+                           const int64_t* add_strides, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_box_copy, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  CopyOut o{};
+  for (int i = 0; i < g.rank; i++) {
+    o.dst_strides[i] = dst_strides ? dst_strides[i] : 0;
+    o.add_strides[i] = add_strides ? add_strides[i] : 0;
+  }
+  int64_t tiles = 1;
+  for (int i = 0; i < g.rank; i++) tiles *= (g.dims[i] + g.box[i] - 1) / g.box[i];
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // LDS holds the whole swizzle period: a swizzled offset of the image can land past
+  // image_bytes (up to image_stride).
+  hipLaunchKernelGGL(k_box_copy, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, g, o,
+                     (const uint8_t*)src, (uint8_t*)dst, (uint8_t*)dst_add);
+  return hipGetLastError();
+}
+
+}  // namespace bsm

@@ -1,0 +1,292 @@
+"""GPU parity: dense fp16/bf16 GEMM, block-scaled MXFP8/MXFP4 GEMM and the fragment loads.
+
+Tolerances (the stated bound of the method, written out):
+  dense:        |D - ref| <= 2e-3 * sum_k |a_mk b_nk|  (+ half an ulp of the float32 result)
+  block scaled: |D - ref| <= 1e-5 * sum_k |a_mk b_nk|  (+ half an ulp)
+Inputs whose every partial sum is exact in float32 must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_matrix_amd as bsm
+from block_scaled_matrix_amd import workloads as W
+from gpu_util import dev, dev_f32, host, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_DENSE, TOL_MX = 2e-3, 1e-5
+
+
+def run_dense(M, N, K, dt, A, lda, amaj, B, ldb, bmaj, D0=None, neg_a=0, neg_b=0, accum=0, ldd=None):
+    ldd = ldd or ((N + 3) // 4 * 4)
+    d = np.full((M, ldd), np.nan, np.float32)
+    if D0 is not None:
+        d[:, :N] = D0
+    dD = dev_f32(d)
+    bsm.bsm_gemm(M, N, K, dt, dev(A), lda, amaj, dev(B), ldb, bmaj, dD, ldd, neg_a, neg_b, accum)
+    return dD.cpu().numpy()
+
+
+def pad_cols(a, ld):
+    out = np.zeros((a.shape[0], ld), a.dtype)
+    out[:, :a.shape[1]] = a
+    return out
+
+
+def dense_case(rng, M, N, K, dt, amaj, bmaj, exact=False):
+    if exact:
+        a = (rng.integers(-4, 5, (M, K)) / 4).astype(np.float32)
+        b = (rng.integers(-4, 5, (N, K)) / 4).astype(np.float32)
+    else:
+        a = rng.standard_normal((M, K)).astype(np.float32)
+        b = rng.standard_normal((N, K)).astype(np.float32)
+    a, b = W.to_half_bits(a, dt), W.to_half_bits(b, dt)
+    if amaj == "k":
+        lda = (K + 7) // 8 * 8
+        A = pad_cols(a, lda)
+    else:
+        lda = (M + 7) // 8 * 8
+        A = pad_cols(np.ascontiguousarray(a.T), lda)
+    if bmaj == "k":
+        ldb = (K + 7) // 8 * 8
+        B = pad_cols(b, ldb)
+    else:
+        ldb = (N + 7) // 8 * 8
+        B = pad_cols(np.ascontiguousarray(b.T), ldb)
+    return A, lda, B, ldb
+
+
+def test_pages_tcgen05_example_bit_exact(O):
+    """tcgen05.mma Example: 128x64x64 fp16, integers(-4,5)/4, D = a @ b.T (exact sums)."""
+    rng = np.random.default_rng(0)
+    a = (rng.integers(-4, 5, (128, 64)) / 4).astype(np.float16).view(np.uint16)
+    b = (rng.integers(-4, 5, (64, 64)) / 4).astype(np.float16).view(np.uint16)
+    say("gemm pages example")
+    D = run_dense(128, 64, 64, "f16", a, 64, "k", b, 64, "k")
+    ref, _ = O.gemm(128, 64, 64, "f16", a, 64, "k", b, 64, "k")
+    assert np.array_equal(D[:, :64], ref.astype(np.float32))
+    np.testing.assert_allclose(D[:, :64], a.view(np.float16).astype(np.float32) @ b.view(np.float16).astype(np.float32).T,
+                               rtol=2e-4, atol=2e-4)
+
+
+def test_gemm_f16_128_workload(O):
+    w = W.gemm_f16_128()
+    say("gemm f16 128x128x64")
+    D = run_dense(128, 128, 64, "f16", w["A"], 64, "k", w["B"], 64, "k")
+    assert not np.isnan(D).any()
+    ref, bound = O.gemm(128, 128, 64, "f16", w["A"], 64, "k", w["B"], 64, "k")
+    nb, first, worst = O.check_gemm(D, ref, bound, TOL_DENSE)
+    assert nb == 0, (first, worst)
+
+
+SHAPES = [(1, 1, 1), (7, 9, 5), (17, 33, 9), (64, 64, 64), (255, 257, 130), (300, 520, 200), (513, 130, 64),
+          (96, 272, 1000)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("amaj,bmaj", [("k", "k"), ("k", "n"), ("m", "k"), ("m", "n")])
+def test_dense_vs_oracle(O, dt, amaj, bmaj):
+    rng = np.random.default_rng([ord(c) for c in dt + amaj + bmaj])
+    for i, (M, N, K) in enumerate(SHAPES):
+        neg_a, neg_b, accum = i & 1, (i >> 1) & 1, (i >> 2) & 1
+        A, lda, B, ldb = dense_case(rng, M, N, K, dt, amaj, bmaj)
+        d0 = rng.standard_normal((M, N)).astype(np.float32)
+        say("dense", dt, amaj, bmaj, M, N, K, neg_a, neg_b, accum)
+        D = run_dense(M, N, K, dt, A, lda, amaj, B, ldb, bmaj, d0 if accum else None, neg_a, neg_b, accum)
+        ref, bound = O.gemm(M, N, K, dt, A, lda, amaj, B, ldb, bmaj, d0, N, neg_a, neg_b, accum)
+        nb, first, worst = O.check_gemm(D, ref, bound, TOL_DENSE)
+        assert nb == 0, (M, N, K, first, worst)
+        assert np.isnan(D[:, N:]).all()  # columns past N of the padded D are never written
+
+
+@pytest.mark.parametrize("amaj,bmaj", [("k", "k"), ("k", "n"), ("m", "n")])
+def test_dense_exact_sums_bit_exact(O, amaj, bmaj):
+    rng = np.random.default_rng(5)
+    for M, N, K in [(256, 256, 64), (130, 300, 96), (512, 256, 200)]:
+        A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", amaj, bmaj, exact=True)
+        say("dense exact", amaj, bmaj, M, N, K)
+        D = run_dense(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj)
+        ref, _ = O.gemm(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj)
+        assert np.array_equal(D[:, :N], ref.astype(np.float32))
+
+
+def test_dense_accum_zero_A_and_determinism(O):
+    rng = np.random.default_rng(6)
+    M, N, K = 300, 260, 128
+    A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", "k", "n")
+    d0 = rng.standard_normal((M, N)).astype(np.float32)
+    say("dense accum with A = 0")
+    D = run_dense(M, N, K, "bf16", np.zeros_like(A), lda, "k", B, ldb, "n", d0, 1, 0, 1)
+    assert np.array_equal(D[:, :N], d0)
+    say("dense determinism")
+    D1 = run_dense(M, N, K, "bf16", A, lda, "k", B, ldb, "n", d0, 0, 0, 1)
+    D2 = run_dense(M, N, K, "bf16", A, lda, "k", B, ldb, "n", d0, 0, 0, 1)
+    assert np.array_equal(D1.view(np.uint32), D2.view(np.uint32))
+    Dn = run_dense(M, N, K, "bf16", A, lda, "k", B, ldb, "n", None, 1, 0, 0)
+    Dp = run_dense(M, N, K, "bf16", A, lda, "k", B, ldb, "n", None, 0, 0, 0)
+    assert np.array_equal(Dn[:, :N], -Dp[:, :N])
+
+
+def test_dense_k_zero():
+    say("dense K = 0")
+    D = run_dense(5, 6, 0, "bf16", np.zeros((5, 8), np.uint16), 8, "k", np.zeros((6, 8), np.uint16), 8, "k")
+    assert (D[:, :6] == 0).all()
+    d0 = np.arange(30, dtype=np.float32).reshape(5, 6)
+    D = run_dense(5, 6, 0, "bf16", np.zeros((5, 8), np.uint16), 8, "k", np.zeros((6, 8), np.uint16), 8, "k", d0,
+                  accum=1)
+    assert np.array_equal(D[:, :6], d0)
+
+
+def test_gemm_bf16_8192_sampled(O):
+    """M = N = K = 8192 bf16, A K-major, B MN-major, accumulate onto D0: sampled outputs."""
+    w = W.gemm_bf16()
+    M, N, K = w["M"], w["N"], w["K"]
+    say("gemm bf16 8192 full")
+    dA, dB = dev(w["A"]), dev(w["B"])
+    dD = dev_f32(w["D0"])
+    bsm.bsm_gemm(M, N, K, "bf16", dA, K, "k", dB, N, "n", dD, N, 0, 0, 1)
+    D = dD.cpu().numpy()
+    pm, pn = W.sample_points(M, N, 2000)
+    ref, bound = O.gemm_points(M, N, K, "bf16", w["A"], K, "k", w["B"], N, "n", w["D0"], N, 0, 0, 1, pm, pn)
+    nb, first, worst = O.check_gemm(D[pm, pn].reshape(1, -1), ref.reshape(1, -1), bound.reshape(1, -1), TOL_DENSE)
+    assert nb == 0, (first, worst)
+    assert np.isfinite(D).all()
+
+
+# ----------------------------------------------------------------------------- fragments
+@pytest.mark.parametrize("major", ["k", "m"])
+def test_fragment_loads_vs_oracle_ldmatrix_image(O, major):
+    """The dense kernel's LDS->register fragment reads, mapped back through the MFMA
+    operand lane map, equal the oracle's 8x8 b16 matrix images (transposed for the
+    MN-major storage: the .trans image rule)."""
+    rows, kdim = bsm.bsm_debug_fragment_shape()
+    rng = np.random.default_rng(3)
+    op = rng.integers(0, 2 ** 16, (rows, kdim), dtype=np.uint64).astype(np.uint16)   # logical operand (row, k)
+    stored = op if major == "k" else np.ascontiguousarray(op.T)                     # storage order
+    dump = torch.zeros((rows // 32) * (kdim // 16) * 64 * 8, dtype=torch.int16, device="cuda")
+    say("fragments", major)
+    bsm.bsm_debug_fragments(dev(stored), rows, kdim, major, dump)
+    got = host(dump, np.uint16).reshape(rows // 32, kdim // 16, 64, 8)
+    # oracle: 8x8 matrices of the stored array; with transpose for MN-major storage
+    sb = stored.view(np.uint8).reshape(-1)
+    row_pitch = stored.shape[1] * 2
+    for b in range(rows // 32):
+        for s in range(kdim // 16):
+            for lane in range(64):
+                r, kb = 32 * b + lane % 32, 16 * s + 8 * (lane // 32)
+                if major == "k":   # matrix rows are operand rows r8..r8+7, columns k8..k8+7
+                    r8, k8 = r - r % 8, kb
+                    offs = [(r8 + j) * row_pitch + k8 * 2 for j in range(8)]
+                    regs = O.ldmatrix(sb, offs, 1, 0)
+                else:              # stored rows are k: matrix rows k8.., columns r8..; transpose
+                    r8, k8 = r - r % 8, kb
+                    offs = [(k8 + j) * row_pitch + r8 * 2 for j in range(8)]
+                    regs = O.ldmatrix(sb, offs, 1, 1)
+                j = r % 8       # image row j (operand row r) owned by lanes 4j..4j+3
+                vals = []
+                for w in range(4):
+                    word = int(regs[4 * j + w, 0])
+                    vals += [word & 0xFFFF, word >> 16]
+                assert list(got[b, s, lane]) == vals, (b, s, lane)
+                assert vals == list(op[r, kb:kb + 8])
+
+
+# ----------------------------------------------------------------------------- block scaled
+def run_mx(M, N, K, fmt, g, D0=None, neg_a=0, neg_b=0, accum=0):
+    ldd = (N + 3) // 4 * 4
+    d = np.full((M, ldd), np.nan, np.float32)
+    if D0 is not None:
+        d[:, :N] = D0
+    dD = dev_f32(d)
+    bsm.bsm_gemm_block_scale(M, N, K, fmt, dev(g["A"]), g["lda"], dev(g["SFA"]), g["ld_sfa"], fmt, dev(g["B"]),
+                             g["ldb"], dev(g["SFB"]), g["ld_sfb"], dD, ldd, neg_a, neg_b, accum)
+    return dD.cpu().numpy()
+
+
+def mx_case(fmt, seed, M, N, K, exp_range=4, ld_pad=0):
+    g = (W.mxfp8 if fmt == "e4m3" else W.mxfp4)(seed=seed, M=M, N=N, K=K, exp_range=exp_range)
+    if ld_pad:
+        epb = 2 if fmt == "e2m1" else 1
+        lda = K + ld_pad
+        g["A"] = pad_cols(g["A"].reshape(M, -1), lda // epb)
+        g["B"] = pad_cols(g["B"].reshape(N, -1), lda // epb)
+        g["lda"] = g["ldb"] = lda
+        g["SFA"] = pad_cols(g["SFA"], K // 32 + 3)
+        g["SFB"] = pad_cols(g["SFB"], K // 32 + 3)
+        g["ld_sfa"] = g["ld_sfb"] = K // 32 + 3
+    return g
+
+
+MX_SHAPES = [(1, 1, 32), (9, 17, 64), (33, 40, 96), (256, 256, 128), (300, 260, 288), (130, 513, 512),
+             (64, 96, 1056)]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_block_scale_vs_oracle(O, fmt):
+    for i, (M, N, K) in enumerate(MX_SHAPES):
+        neg_a, neg_b, accum = i & 1, (i >> 1) & 1, (i >> 2) & 1
+        g = mx_case(fmt, 10 + i, M, N, K, ld_pad=64 if i % 3 == 2 else 0)
+        rng = np.random.default_rng(i)
+        d0 = rng.standard_normal((M, N)).astype(np.float32)
+        say("mx", fmt, M, N, K, neg_a, neg_b, accum)
+        D = run_mx(M, N, K, fmt, g, d0 if accum else None, neg_a, neg_b, accum)
+        ref, bound = O.gemm_block_scale(M, N, K, fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], fmt, g["B"], g["ldb"],
+                                        g["SFB"], g["ld_sfb"], d0, N, neg_a, neg_b, accum)
+        nb, first, worst = O.check_gemm(D, ref, bound, TOL_MX)
+        assert nb == 0, (M, N, K, first, worst)
+        assert np.isnan(D[:, N:]).all()
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_block_scale_exact_sums_bit_exact(O, fmt):
+    # narrow scales and small codes: every partial sum is exact in float32
+    for M, N, K in [(256, 256, 128), (300, 200, 256)]:
+        g = mx_case(fmt, 3, M, N, K, exp_range=2)
+        if fmt == "e4m3":   # codes of +-{0, 0.5, 1, 1.5, 2}
+            pick = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0xB0, 0xB8, 0xBC, 0xC0], np.uint8)
+            rng = np.random.default_rng(1)
+            g["A"] = pick[rng.integers(0, 9, g["A"].shape)]
+            g["B"] = pick[rng.integers(0, 9, g["B"].shape)]
+        say("mx exact", fmt, M, N, K)
+        D = run_mx(M, N, K, fmt, g)
+        ref, _ = O.gemm_block_scale(M, N, K, fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], fmt, g["B"], g["ldb"],
+                                    g["SFB"], g["ld_sfb"])
+        assert np.array_equal(D[:, :N], ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_block_scale_nan_scale_poisons_row(O, fmt):
+    M, N, K = 64, 64, 128
+    g = mx_case(fmt, 4, M, N, K)
+    g["SFA"][5, 2] = 255
+    say("mx nan scale", fmt)
+    D = run_mx(M, N, K, fmt, g)
+    assert np.isnan(D[5, :N]).all()
+    assert np.isfinite(np.delete(D[:, :N], 5, 0)).all()
+
+
+def test_mxfp8_full_size_sampled(O):
+    g = W.mxfp8()
+    M, N, K = g["M"], g["N"], g["K"]
+    say("mxfp8 full", M, N, K)
+    D = run_mx(M, N, K, "e4m3", g)
+    pm, pn = W.sample_points(M, N, 1000)
+    ref, bound = O.gemm_block_scale_points(M, N, K, "e4m3", g["A"], K, g["SFA"], K // 32, "e4m3", g["B"], K,
+                                           g["SFB"], K // 32, None, 0, 0, 0, 0, pm, pn)
+    nb, first, worst = O.check_gemm(D[pm, pn].reshape(1, -1), ref.reshape(1, -1), bound.reshape(1, -1), TOL_MX)
+    assert nb == 0, (first, worst)
+    assert np.isfinite(D[:, :N]).all()
+
+
+def test_mxfp4_full_size_sampled(O):
+    g = W.mxfp4()
+    M, N, K = g["M"], g["N"], g["K"]
+    say("mxfp4 full", M, N, K)
+    D = run_mx(M, N, K, "e2m1", g, neg_a=1)
+    pm, pn = W.sample_points(M, N, 1000)
+    ref, bound = O.gemm_block_scale_points(M, N, K, "e2m1", g["A"], K, g["SFA"], K // 32, "e2m1", g["B"], K,
+                                           g["SFB"], K // 32, None, 0, 1, 0, 0, pm, pn)
+    nb, first, worst = O.check_gemm(D[pm, pn].reshape(1, -1), ref.reshape(1, -1), bound.reshape(1, -1), TOL_MX)
+    assert nb == 0, (first, worst)
+    assert np.isfinite(D[:, :N]).all()

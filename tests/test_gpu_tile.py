@@ -1,0 +1,177 @@
+"""GPU parity: add-scalar tile and box load / store / reduce-add / grid copy vs the oracle.
+
+Copies and images are compared bit for bit (they are unique results); the
+add-reduction is compared bit for bit too (one rounding of the exact sum).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_matrix_amd as bsm
+from block_scaled_matrix_amd import workloads as W
+from gpu_util import dev, dev_like, host, say
+
+pytestmark = pytest.mark.gpu
+
+NPDT = {"u8": np.uint8, "u16": np.uint16, "u32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f32": np.uint32,
+        "e4m3": np.uint8}
+
+
+def test_add_one_pages_example(O):
+    say("add_one (2,32,3,4)")
+    a = W.add_one_tile()
+    da = torch.from_numpy(a).cuda()
+    db = torch.empty_like(da)
+    bsm.bsm_tile_add_scalar_f32(da, db, a.size, 1.0)
+    got = db.cpu().numpy()
+    assert np.array_equal(got, O.add_scalar_f32(a, 1.0))
+    assert np.array_equal(got, np.arange(1, 769, dtype=np.float32).reshape(2, 32, 3, 4))
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 767, 768, 769, 1000, 12345, 1 << 20])
+def test_add_scalar_ragged(O, n):
+    say("add_scalar n", n)
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
+    dx = torch.from_numpy(x).cuda()
+    out = torch.full((n + 8,), 7.0, device="cuda")
+    bsm.bsm_tile_add_scalar_f32(dx, out, n, -0.75)
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:n].view(np.uint32), O.add_scalar_f32(x, -0.75).view(np.uint32))
+    assert (got[n:] == 7.0).all()
+    bsm.bsm_tile_add_scalar_f32(dx, dx, n, 1.0)   # in place
+    assert np.array_equal(dx.cpu().numpy(), O.add_scalar_f32(x, 1.0))
+
+
+def _rand_case(rng, rank, dtype):
+    esz = bsm.ESIZE[dtype]
+    dims = tuple(int(v) for v in rng.integers(1, 40 if rank <= 3 else 12, rank))
+    inner_box = (16 // esz) * int(rng.integers(1, 9))
+    box = tuple(int(v) for v in rng.integers(1, 10 if rank <= 3 else 4, rank - 1)) + (min(inner_box, 256),)
+    estr = tuple(int(v) for v in rng.integers(1, 4, rank - 1)) + (1,)
+    swz = int(rng.integers(0, 4))
+    if swz and box[-1] * esz > (16 << swz):
+        swz = 0
+    pitch_b = (dims[-1] * esz + 15) // 16 * 16 + 16 * int(rng.integers(0, 3))
+    shape = dims[:-1] + (pitch_b // esz,)
+    mem = rng.integers(0, 2 ** (8 * esz), shape, dtype=np.uint64).astype(NPDT[dtype])
+    strides = [mem.strides[i] for i in range(rank)]
+    return dims, box, estr, swz, mem, strides
+
+
+@pytest.mark.parametrize("dtype", ["u8", "bf16", "f32"])
+@pytest.mark.parametrize("rank", [1, 2, 3, 5])
+def test_box_load_store_vs_oracle(O, dtype, rank):
+    rng = np.random.default_rng(1000 * rank + bsm.DTYPE[dtype])
+    for trial in range(6):
+        dims, box, estr, swz, mem, strides = _rand_case(rng, rank, dtype)
+        fill = int(rng.integers(0, 2)) if dtype != "u8" else 0
+        nb = 7
+        coords = rng.integers(-12, 45, (nb, rank)).astype(np.int32)
+        if trial == 0:
+            coords[:] = 0
+        say("box_load", dtype, rank, dims, box, estr, swz, fill)
+        stride = O.image_stride(dtype, box, estr, swz)
+        dsrc = dev(mem)
+        dimg = dev_like(nb * stride, 0xA5)
+        dco = torch.from_numpy(coords.reshape(-1)).cuda()
+        td = bsm.tensor_desc(dsrc, dtype, dims, strides)
+        bd = bsm.box_desc(box, estr, swz, fill)
+        assert bsm.bsm_image_stride(bd, dtype) == stride
+        bsm.bsm_tile_box_load(td, bd, dco, nb, dimg)
+        got = host(dimg, np.uint8).reshape(nb, stride)
+        nbytes = int(np.prod(O.image_extents(box, estr))) * bsm.ESIZE[dtype]
+        for t in range(nb):
+            exp = O.box_load(mem, dtype, dims, strides, box, estr, coords[t], swz, fill)
+            written = np.zeros(stride, bool)
+            written[[O.swizzle(o, swz) for o in range(nbytes)]] = True
+            assert np.array_equal(got[t][written], exp[written]), (t, coords[t])
+            assert (got[t][~written] == 0xA5).all()
+        # store the images back into a sentinel-filled tensor; reduce-add into a second one
+        say("box_store", dtype, rank)
+        sent = np.full_like(mem, 0x3C if dtype == "u8" else 0x3C00)
+        dst = dev(sent)
+        bsm.bsm_tile_box_store(bsm.tensor_desc(dst, dtype, dims, strides), bd, dco, nb, dimg, 0)
+        exp = sent.copy()
+        for t in range(nb):
+            O.box_store(exp, dtype, dims, strides, box, estr, coords[t], got[t], swz, 0)
+        assert np.array_equal(host(dst, NPDT[dtype], mem.shape), exp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_box_reduce_add_vs_oracle(O, dtype):
+    rng = np.random.default_rng(77 + bsm.DTYPE[dtype])
+    esz = bsm.ESIZE[dtype]
+    rows, cols = 70, 100
+    pitch = (cols * esz + 31) // 16 * 16 // esz
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    ib = torch.int32 if dtype == "f32" else torch.int16
+
+    def bits(x):
+        m = np.zeros((rows, pitch), NPDT[dtype])
+        m[:, :cols] = torch.from_numpy(x).to(tdt).view(ib).numpy().view(NPDT[dtype])
+        return m
+
+    src = bits(rng.standard_normal((rows, cols)).astype(np.float32))
+    acc = bits((rng.standard_normal((rows, cols)) * 4).astype(np.float32))
+    box = (16, 128 // esz)
+    coords = np.array([[r, c] for r in range(-8, rows, 16) for c in range(-24, cols, box[1])], np.int32)
+    coords = coords[(coords[:, 0] % 16 == 8) & ((coords[:, 1] + 24) % box[1] == 0)]  # non-overlapping grid
+    nb = len(coords)
+    strides = (pitch * esz, esz)
+    stride = O.image_stride(dtype, box, (1, 1), 3)
+    say("reduce_add", dtype, nb)
+    dsrc, dacc = dev(src), dev(acc)
+    dimg = dev_like(nb * stride)
+    dco = torch.from_numpy(coords.reshape(-1)).cuda()
+    bd = bsm.box_desc(box, (1, 1), 3, 0)
+    bsm.bsm_tile_box_load(bsm.tensor_desc(dsrc, dtype, (rows, cols), strides), bd, dco, nb, dimg)
+    bsm.bsm_tile_box_store(bsm.tensor_desc(dacc, dtype, (rows, cols), strides), bd, dco, nb, dimg, 1)
+    imgs = host(dimg, np.uint8).reshape(nb, stride)
+    exp = acc.copy()
+    for t in range(nb):
+        O.box_store(exp, dtype, (rows, cols), strides, box, (1, 1), coords[t], imgs[t], 3, 1)
+    assert np.array_equal(host(dacc, NPDT[dtype], acc.shape), exp)
+
+
+def _copy_case(O, rows, cols, pitch, box, swz, seed):
+    rng = np.random.default_rng(seed)
+    src = np.full((rows, pitch), W.SENTINEL_BF16, np.uint16)
+    src[:, :cols] = W.to_half_bits(rng.standard_normal((rows, cols)).astype(np.float32), "bf16")
+    add = np.full((rows, pitch), W.SENTINEL_BF16, np.uint16)
+    add[:, :cols] = W.to_half_bits(rng.standard_normal((rows, cols)).astype(np.float32), "bf16")
+    dst = np.full((rows, pitch), W.SENTINEL_BF16, np.uint16)
+    return src, dst, add
+
+
+@pytest.mark.parametrize("rows,cols,pitch,box,swz", [
+    (45, 70, 72, (16, 32), 2), (128, 64, 64, (128, 64), 3), (300, 190, 192, (128, 64), 3),
+    (257, 8190 // 8, 1024, (128, 64), 3), (33, 17, 24, (8, 8), 0)])
+def test_box_copy_grid_vs_oracle(O, rows, cols, pitch, box, swz):
+    src, dst, add = _copy_case(O, rows, cols, pitch, box, swz, rows)
+    say("box_copy", rows, cols, pitch, box, swz)
+    ds, dd, da = dev(src), dev(dst), dev(add)
+    st = (pitch * 2, 2)
+    bsm.bsm_tile_box_copy(bsm.tensor_desc(ds, "bf16", (rows, cols), st), bsm.tensor_desc(dd, "bf16", (rows, cols), st),
+                          bsm.tensor_desc(da, "bf16", (rows, cols), st), bsm.box_desc(box, (1, 1), swz, 0))
+    O.box_copy_grid(src, dst, add, "bf16", (rows, cols), st, box, (1, 1), swz, 0)
+    assert np.array_equal(host(dd, np.uint16, dst.shape), dst)
+    assert np.array_equal(host(da, np.uint16, add.shape), add)
+
+
+def test_box_copy_full_size_vs_oracle(O):
+    """The 16381 x 8190 bf16 workload (8192-element pitch, (128,64) boxes, 128-byte swizzle)."""
+    w = W.box_copy_bf16()
+    rows, cols, pitch = w["rows"], w["cols"], w["pitch"]
+    say("box_copy full", rows, cols)
+    ds, dd, da = dev(w["src"]), dev(w["dst"]), dev(w["dst_add"])
+    st = (pitch * 2, 2)
+    bsm.bsm_tile_box_copy(bsm.tensor_desc(ds, "bf16", (rows, cols), st), bsm.tensor_desc(dd, "bf16", (rows, cols), st),
+                          bsm.tensor_desc(da, "bf16", (rows, cols), st), bsm.box_desc(w["box"], (1, 1), 3, 0))
+    got_d = host(dd, np.uint16, (rows, pitch))
+    got_a = host(da, np.uint16, (rows, pitch))
+    dst, add = w["dst"], w["dst_add"]
+    O.box_copy_grid(w["src"], dst, add, "bf16", (rows, cols), st, w["box"], (1, 1), 3, 0)
+    assert np.array_equal(got_d, dst)
+    assert np.array_equal(got_a, add)
+    assert np.array_equal(got_d[:, :cols], w["src"][:, :cols]) and (got_d[:, cols:] == W.SENTINEL_BF16).all()

@@ -252,6 +252,8 @@ int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, int64_t
     const int64_t amin = a_major == 'k' ? K : M, bmin = b_major == 'k' ? K : N;
     if (lda < amin || lda % 8) return fail(BSM_E_ALIGN, "lda = %lld must be >= %lld and a multiple of 8", (long long)lda, (long long)amin);
     if (ldb < bmin || ldb % 8) return fail(BSM_E_ALIGN, "ldb = %lld must be >= %lld and a multiple of 8", (long long)ldb, (long long)bmin);
+    if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22))
+      return fail(BSM_E_SHAPE, "lda, ldb must be at most 2^22 elements (32-bit in-tile offsets)");
     const Range rd{(uintptr_t)D, (uintptr_t)(D + (M - 1) * ldd + N)};
     const int64_t arows = a_major == 'k' ? M : K, brows = b_major == 'k' ? N : K;
     const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(((arows - 1) * lda + amin) * 2)};
@@ -291,11 +293,16 @@ int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const v
     if (lda % (16 * per_byte) || ldb % (16 * per_byte))
       return fail(BSM_E_ALIGN, "lda = %lld, ldb = %lld: rows must start 16-byte aligned", (long long)lda, (long long)ldb);
     if (ld_sfa < K / 32 || ld_sfb < K / 32) return fail(BSM_E_ALIGN, "ld_sfa, ld_sfb must be >= K/32");
+    if (ld_sfa % 4 || ld_sfb % 4 || (uintptr_t)SFA % 4 || (uintptr_t)SFB % 4)
+      return fail(BSM_E_ALIGN, "scale rows must start 4-byte aligned (SFA, SFB 4-byte aligned, ld_sfa, ld_sfb multiples of 4)");
+    if (lda / per_byte > (int64_t(1) << 23) || ldb / per_byte > (int64_t(1) << 23) || ld_sfa > (int64_t(1) << 24) ||
+        ld_sfb > (int64_t(1) << 24))
+      return fail(BSM_E_SHAPE, "leading dimensions too large for 32-bit in-tile offsets");
     const Range rd{(uintptr_t)D, (uintptr_t)(D + (M - 1) * ldd + N)};
     const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(((M - 1) * lda + K) / per_byte)};
     const Range rb{(uintptr_t)B, (uintptr_t)B + (uintptr_t)(((N - 1) * ldb + K) / per_byte)};
-    const Range rsa{(uintptr_t)SFA, (uintptr_t)SFA + (uintptr_t)((M - 1) * ld_sfa + K / 32)};
-    const Range rsb{(uintptr_t)SFB, (uintptr_t)SFB + (uintptr_t)((N - 1) * ld_sfb + K / 32)};
+    const Range rsa{(uintptr_t)SFA, (uintptr_t)SFA + (uintptr_t)(M * ld_sfa)};
+    const Range rsb{(uintptr_t)SFB, (uintptr_t)SFB + (uintptr_t)(N * ld_sfb)};
     if (overlap(rd, ra) || overlap(rd, rb) || overlap(rd, rsa) || overlap(rd, rsb))
       return fail(BSM_E_ALIAS, "an operand or scale tensor overlaps D");
   }

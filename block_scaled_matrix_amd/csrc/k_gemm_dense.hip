@@ -7,9 +7,11 @@
 //
 // gfx950 design:
 //  - workgroup tile 256 x 256, K tile 64, four wave64s in a 2 x 2 grid, each owning a
-//    128 x 128 sub-tile as 4 x 4 v_mfma_f32_32x32x16 accumulators (256 fp32 per lane);
+//    128 x 128 sub-tile as 4 x 4 v_mfma_f32_32x32x16 accumulators (256 fp32 per lane,
+//    held in AGPRs);
 //  - operand tiles stream HBM -> LDS with global_load_lds_dwordx4 (no register
-//    staging), two LDS stages (2 x 64 KiB), one barrier per K tile;
+//    staging): an SGPR tile base plus per-lane 32-bit offsets that stay fixed over the
+//    whole K loop; two LDS stages (2 x 64 KiB), one barrier per K tile;
 //  - K-major tiles: 128-byte rows, 16-byte chunk c of row r stored at chunk
 //    c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group reads with ds_read_b128
 //    cover all 64 LDS banks;
@@ -17,10 +19,11 @@
 //    stored at c ^ (4 * (kr & 3)); fragments come from ds_read_b64_tr_b16, the LDS
 //    transpose read (the analog of ldmatrix .trans in "ldmatrix / stmatrix",
 //    Transpose and stores), whose 32-lane groups again cover all banks;
+//  - software pipeline: the 16 MFMAs of one K step overlap the LDS reads of the next
+//    step and the DMA of the next K tile; the stage barrier sits inside the last step;
 //  - M/N edges clamp the rows that are loaded and mask the stores; a ragged last K
 //    tile is loaded through registers with the elements past K zeroed.
-#include "bsm_device.hpp"
-#include "bsm_internal.hpp"
+#include "gemm_common.hpp"
 #include "../../include/bsm.h"
 
 namespace bsm {
@@ -28,33 +31,44 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int TILE_BYTES = 256 * BK * 2;  // one operand tile: 32 KiB
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 
-__device__ __forceinline__ uint32_t kmaj_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4)); }
-__device__ __forceinline__ uint32_t mnmaj_off(int kr, int c) { return (uint32_t)(kr * 512 + ((c ^ ((kr & 3) << 2)) << 4)); }
-
-// Direct HBM -> LDS copy of one 256-row x 64-k operand tile (32 wave instructions of
-// 1 KiB; wave w issues instructions w, w+4, ..., w+28). Rows past `rows` are clamped.
+// Per-lane byte offsets (relative to the tile's global base) of the 8 direct LDS copies
+// a wave issues for one operand tile. Copy j of wave w fills LDS bytes
+// [1024 * (w + 4j), +1024): lane l writes 16 bytes at 1024 * (w + 4j) + 16 * l.
+//  K-major: LDS row r = 8(w+4j) + l/8 holds global row row0 + r (clamped to the last
+//           row), its physical chunk l%8 holds logical chunk (l%8) ^ ((r >> 1) & 7);
+//  MN-major: LDS k-row kr = 2(w+4j) + l/32 holds global k-row k0 + kr, its physical
+//           chunk l%32 holds logical chunk (l%32) ^ (4 (kr & 3)) (columns clamped to
+//           the last 8-aligned chunk).
 template <bool KMAJ>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ p, int64_t ld, int64_t row0, int64_t rows,
-                                           int64_t k0, uint8_t* tile, int w, int lane) {
+__device__ __forceinline__ void dma_offsets(int64_t ld, int64_t row0, int64_t rows, int w, int lane,
+                                            uint32_t (&off)[8]) {
   if (KMAJ) {
     const int c = (lane & 7) ^ (((8 * w + (lane >> 3)) >> 1) & 7);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const int i = w + 4 * j;
-      const int64_t rg = min(row0 + 8 * i + (lane >> 3), rows - 1);
-      load_lds_16(p + rg * ld + k0 + 8 * c, tile + 1024 * i);
+      const int64_t rg = min(row0 + 8 * w + 32 * j + (lane >> 3), rows - 1);
+      off[j] = (uint32_t)(((rg - row0) * ld + 8 * c) * 2);
     }
   } else {
     const int kr0 = 2 * w + (lane >> 5);
     const int c = (lane & 31) ^ ((kr0 & 3) << 2);
     const int64_t col = min(row0 + 8 * c, (rows - 1) & ~int64_t(7));
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int i = w + 4 * j;
-      load_lds_16(p + (k0 + kr0 + 8 * j) * ld + col, tile + 1024 * i);
-    }
+    for (int j = 0; j < 8; j++) off[j] = (uint32_t)(((kr0 + 8 * j) * ld + (col - row0)) * 2);
   }
+}
+
+// Global base (wave-uniform) of the operand tile whose K range starts at k0.
+template <bool KMAJ>
+__device__ __forceinline__ const uint16_t* tile_base(const uint16_t* p, int64_t ld, int64_t row0, int64_t k0) {
+  return KMAJ ? p + row0 * ld + k0 : p + k0 * ld + row0;
+}
+
+__device__ __forceinline__ void issue_tile(const uint16_t* base, const uint32_t (&off)[8], uint32_t lds_tile, int w) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) gemm::dma16s(base, off[j], lds_tile + 1024 * (w + 4 * j));
 }
 
 // The same tile for a partial K tile: through registers, elements with k >= K zeroed.
@@ -96,24 +110,38 @@ struct Frag<BSM_BF16> { typedef bf16x8 T; };
 template <>
 struct Frag<BSM_F16> { typedef f16x8 T; };
 
-// Operand fragment of v_mfma_f32_32x32x16: lane l holds (row rbase + l%32,
-// k 16*ks + 8*(l/32) + e), e = 0..7.
+// LDS read addresses of the v_mfma_f32_32x32x16 operand fragments. Lane l must hold
+// operand (row wbase + 32t + l%32, k 16ks + 8(l/32) + e), e = 0..7.
+//  K-major: one ds_read_b128 at 128 wbase + 4096t + base[ks];
+//  MN-major: two ds_read_b64_tr_b16 (h = 0, 1) at 2 wbase + base[t] + 8192ks + 2048h,
+//   where within each 16-lane group (i = l%16, G = l/16) lane i provides k-row
+//   16ks + 8(G/2) + 4h + i/4 and columns 16(G%2) + 4(i%4)..+3, and receives the
+//   transposed 4 x 16 block as column 16(G%2) + i, k-rows +0..3. The 32-column block t
+//   enters the swizzled address as an XOR of bits 6..7 (chunk bits 2..3).
 template <bool KMAJ>
-__device__ __forceinline__ uint4 read_frag(const uint8_t* tile, int rbase, int ks, int lane) {
+__device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[4]) {
   if (KMAJ) {
-    return lds_read_b128(tile + kmaj_off(rbase + (lane & 31), 2 * ks + (lane >> 5)));
+    const int r = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) base[ks] = (uint32_t)(r * 128 + (((2 * ks + (lane >> 5)) ^ ((r >> 1) & 7)) << 4));
   } else {
     const int i = lane & 15, G = lane >> 4;
-    const int kb = 16 * ks + 8 * (G >> 1) + (i >> 2);
-    const int n = rbase + 16 * (G & 1) + 4 * (i & 3);
-    const i16x4 lo = lds_read_tr16(tile + mnmaj_off(kb, n >> 3) + (n & 7) * 2);
-    const i16x4 hi = lds_read_tr16(tile + mnmaj_off(kb + 4, n >> 3) + (n & 7) * 2);
-    uint4 v;
-    v.x = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-    v.y = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-    v.z = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-    v.w = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-    return v;
+    const uint32_t L = (uint32_t)((8 * (G >> 1) + (i >> 2)) * 512 + 16 * (2 * (G & 1) + ((i & 3) >> 1)) + 8 * (i & 1) +
+                                  64 * ((i >> 2) & 3));
+#pragma unroll
+    for (int t = 0; t < 4; t++) base[t] = L ^ (uint32_t)(t << 6);
+  }
+}
+
+template <bool KMAJ>
+__device__ __forceinline__ uint4 read_frag(const uint8_t* tile, int wbase, const uint32_t (&base)[4], int ks, int t) {
+  if (KMAJ) {
+    return lds_read_b128(tile + wbase * 128 + 4096 * t + base[ks]);
+  } else {
+    const uint8_t* p = tile + 2 * wbase + base[t] + 8192 * ks;
+    const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
+    const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(p + 2048));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
@@ -125,42 +153,31 @@ __device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
   else return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
 }
 
-template <int DT, bool AK, bool BKM>
-__device__ __forceinline__ void compute_tile(const uint8_t* ta, const uint8_t* tb, int nsteps, int wm, int wn,
-                                             int lane, f32x16 (&acc)[4][4]) {
-  for (int ks = 0; ks < nsteps; ks++) {
-    uint4 af[4], bf[4];
+template <bool AK, bool BKM>
+__device__ __forceinline__ void read_step(const uint8_t* ta, const uint8_t* tb, int ks, int wa, int wb,
+                                          const uint32_t (&ab)[4], const uint32_t (&bb)[4], uint4 (&af)[4],
+                                          uint4 (&bf)[4]) {
 #pragma unroll
-    for (int t = 0; t < 4; t++) af[t] = read_frag<AK>(ta, 128 * wm + 32 * t, ks, lane);
+  for (int t = 0; t < 4; t++) af[t] = read_frag<AK>(ta, wa, ab, ks, t);
 #pragma unroll
-    for (int t = 0; t < 4; t++) bf[t] = read_frag<BKM>(tb, 128 * wn + 32 * t, ks, lane);
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-      for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma<DT>(af[mt], bf[nt], acc[mt][nt]);
-  }
+  for (int t = 0; t < 4; t++) bf[t] = read_frag<BKM>(tb, wb, bb, ks, t);
 }
 
-// Tile order: consecutive workgroup ids walk a column of GROUP tile rows so that
-// workgroups running together share A row panels and B column panels in L2.
-__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * tiles_n;
-  const int g = pid / per_group;
-  const int first = g * GROUP;
-  const int gsize = min(tiles_m - first, GROUP);
-  const int in = pid - g * per_group;
-  tm = first + in % gsize;
-  tn = in / gsize;
+template <int DT>
+__device__ __forceinline__ void mfma_step(const uint4 (&af)[4], const uint4 (&bf)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma<DT>(af[mt], bf[nt], acc[mt][nt]);
 }
 
 template <int DT, bool AK, bool BKM>
 __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE_BYTES];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  gemm::tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const uint16_t* A = (const uint16_t*)a.A;
   const uint16_t* B = (const uint16_t*)a.B;
@@ -173,52 +190,72 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
 
+  uint32_t aoff[8], boff[8], abase[4], bbase[4];
+  dma_offsets<AK>(a.lda, m0, a.M, w, lane, aoff);
+  dma_offsets<BKM>(a.ldb, n0, a.N, w, lane, boff);
+  frag_bases<AK>(lane, abase);
+  frag_bases<BKM>(lane, bbase);
+  const int wa = 128 * wm, wb = 128 * wn;
+
   const int nfull = (int)(a.K / BK);
   const int tail = (int)(a.K % BK);
+  const uint32_t lds0 = gemm::lds_addr(lds);
+  uint4 a0[4], b0[4], a1[4], b1[4];
   if (nfull > 0) {
-    issue_tile<AK>(A, a.lda, m0, a.M, 0, lds[0][0], w, lane);
-    issue_tile<BKM>(B, a.ldb, n0, a.N, 0, lds[0][1], w, lane);
+    issue_tile(tile_base<AK>(A, a.lda, m0, 0), aoff, lds0, w);
+    issue_tile(tile_base<BKM>(B, a.ldb, n0, 0), boff, lds0 + TILE_BYTES, w);
+    gemm::wait_dma();
+    __syncthreads();
+    read_step<AK, BKM>(lds, lds + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
   }
-  wait_vmem();
-  __syncthreads();
+  // Software pipeline over K tiles (two LDS stages, two fragment register sets): while
+  // the 16 MFMAs of K step s run, the fragments of step s+1 are in flight and the DMA of
+  // the next K tile streams into the other stage. The stage barrier sits before the
+  // MFMAs of step 3, when every wave holds all fragments of the current stage.
+  // The loop body is branch-free so that the scheduling fences hold: on the last K tile
+  // the prefetch re-reads the last tile (clamped index) into the stage nobody reads again.
   for (int kt = 0; kt < nfull; kt++) {
     const int cur = kt & 1;
-    if (kt + 1 < nfull) {
-      issue_tile<AK>(A, a.lda, m0, a.M, (int64_t)(kt + 1) * BK, lds[cur ^ 1][0], w, lane);
-      issue_tile<BKM>(B, a.ldb, n0, a.N, (int64_t)(kt + 1) * BK, lds[cur ^ 1][1], w, lane);
+    const uint8_t* ta = lds + cur * STAGE_BYTES;
+    const uint8_t* tb = ta + TILE_BYTES;
+    const uint8_t* na = lds + (cur ^ 1) * STAGE_BYTES;
+    read_step<AK, BKM>(ta, tb, 1, wa, wb, abase, bbase, a1, b1);
+    {
+      const uint32_t nxt = lds0 + (cur ^ 1) * STAGE_BYTES;
+      const int64_t k1 = (int64_t)min(kt + 1, nfull - 1) * BK;
+      issue_tile(tile_base<AK>(A, a.lda, m0, k1), aoff, nxt, w);
+      issue_tile(tile_base<BKM>(B, a.ldb, n0, k1), boff, nxt + TILE_BYTES, w);
     }
-    compute_tile<DT, AK, BKM>(lds[cur][0], lds[cur][1], BK / 16, wm, wn, lane, acc);
-    wait_vmem();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<DT>(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step<AK, BKM>(ta, tb, 2, wa, wb, abase, bbase, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<DT>(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step<AK, BKM>(ta, tb, 3, wa, wb, abase, bbase, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<DT>(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm::wait_dma();
     __syncthreads();
+    read_step<AK, BKM>(na, na + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<DT>(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (tail) {
-    const int st = nfull & 1;
+    uint8_t* st = lds + (nfull & 1) * STAGE_BYTES;
     const int64_t k0 = (int64_t)nfull * BK;
-    fill_tile_masked<AK>(A, a.lda, m0, a.M, k0, a.K, lds[st][0], w, lane);
-    fill_tile_masked<BKM>(B, a.ldb, n0, a.N, k0, a.K, lds[st][1], w, lane);
+    fill_tile_masked<AK>(A, a.lda, m0, a.M, k0, a.K, st, w, lane);
+    fill_tile_masked<BKM>(B, a.ldb, n0, a.N, k0, a.K, st + TILE_BYTES, w, lane);
     __syncthreads();
-    compute_tile<DT, AK, BKM>(lds[st][0], lds[st][1], (tail + 15) / 16, wm, wn, lane, acc);
-  }
-
-  // Epilogue: D = s * acc (+ D). Accumulator register r of a 32x32 block holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  const float sgn = a.negate ? -1.0f : 1.0f;
-#pragma unroll
-  for (int mt = 0; mt < 4; mt++) {
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-      const int64_t col = n0 + 128 * wn + 32 * nt + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t row = m0 + 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < a.M && col < a.N) {
-          float* d = a.D + row * a.ldd + col;
-          const float v = sgn * acc[mt][nt][r];
-          *d = a.accum ? *d + v : v;
-        }
-      }
+    for (int ks = 0; ks < (tail + 15) / 16; ks++) {
+      read_step<AK, BKM>(st, st + TILE_BYTES, ks, wa, wb, abase, bbase, a0, b0);
+      mfma_step<DT>(a0, b0, acc);
     }
   }
+  gemm::store_tile(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
 }
 
 template <int DT, bool AK, bool BKM>
@@ -242,13 +279,17 @@ hipError_t launch_dt(const GemmArgs& a, hipStream_t st) {
 template <bool KMAJ>
 __global__ __launch_bounds__(256) void k_debug_fragments(const uint16_t* __restrict__ src, uint16_t* dump) {
   __shared__ __attribute__((aligned(1024))) uint8_t tile[TILE_BYTES];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  issue_tile<KMAJ>(src, KMAJ ? BK : BM, 0, BM, 0, tile, w, lane);
-  wait_vmem();
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t off[8], base[4];
+  dma_offsets<KMAJ>(KMAJ ? BK : BM, 0, BM, w, lane, off);
+  issue_tile(src, off, gemm::lds_addr(tile), w);
+  gemm::wait_dma();
   __syncthreads();
+  frag_bases<KMAJ>(lane, base);
   for (int mb = 2 * w; mb < 2 * w + 2; mb++) {
     for (int ks = 0; ks < BK / 16; ks++) {
-      const uint4 v = read_frag<KMAJ>(tile, 32 * mb, ks, lane);
+      // rows 32 mb ..: wave base 128 (mb / 4), 32-row block mb % 4
+      const uint4 v = read_frag<KMAJ>(tile, 128 * (mb >> 2), base, ks, mb & 3);
       *(uint4*)(dump + ((mb * (BK / 16) + ks) * 64 + lane) * 8) = v;
     }
   }

@@ -111,18 +111,22 @@ def test_gemm_contract_violations(L):
     expect("BSM_E_NULL", g, 64, 64, 64, "bf16", A, 64, "k", B, 64, "k", 0, 64)
     expect("BSM_E_ALIAS", g, 64, 64, 64, "bf16", D + 1024, 64, "k", B, 64, "k", D, 64)
     expect("BSM_E_ARG", g, 64, 64, 64, "bf16", A, 64, "k", B, 64, "k", D, 64, 2)
+    expect("BSM_E_SHAPE", g, 64, 64, 64, "bf16", A, 1 << 23, "k", B, 64, "k", D, 64)    # 32-bit tile offsets
     expect("BSM_E_ARG", g, 64, 64, 64, "bf16", A, 64, "k", B, 64, "k", D, 64, 0, 0, 3)
     bsm.bsm_gemm(0, 64, 64, "bf16", 0, 0, "k", 0, 0, "k", 0, 0, stream=0)      # M == 0: no-op
     s = lambda *a: bsm.bsm_gemm_block_scale(*a, stream=0)
     SA, SB = FAKE + (3 << 32), FAKE + (4 << 32)
-    expect("BSM_E_DTYPE", s, 64, 64, 64, "bf16", A, 64, SA, 2, "bf16", B, 64, SB, 2, D, 64)
-    expect("BSM_E_DTYPE", s, 64, 64, 64, "e4m3", A, 64, SA, 2, "e2m1", B, 64, SB, 2, D, 64)
-    expect("BSM_E_SHAPE", s, 64, 64, 48, "e4m3", A, 64, SA, 2, "e4m3", B, 64, SB, 2, D, 64)
-    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 72, SA, 2, "e4m3", B, 64, SB, 2, D, 64)
-    expect("BSM_E_ALIGN", s, 64, 64, 64, "e2m1", A, 80, SA, 2, "e2m1", B, 64, SB, 2, D, 64)   # 40-byte rows
-    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 64, SA, 1, "e4m3", B, 64, SB, 2, D, 64)
-    expect("BSM_E_NULL", s, 64, 64, 64, "e4m3", A, 64, 0, 2, "e4m3", B, 64, SB, 2, D, 64)
-    expect("BSM_E_ALIAS", s, 64, 64, 64, "e4m3", A, 64, D + 64, 2, "e4m3", B, 64, SB, 2, D, 64)
+    expect("BSM_E_DTYPE", s, 64, 64, 64, "bf16", A, 64, SA, 4, "bf16", B, 64, SB, 4, D, 64)
+    expect("BSM_E_DTYPE", s, 64, 64, 64, "e4m3", A, 64, SA, 4, "e2m1", B, 64, SB, 4, D, 64)
+    expect("BSM_E_SHAPE", s, 64, 64, 48, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 72, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e2m1", A, 80, SA, 4, "e2m1", B, 64, SB, 4, D, 64)   # 40-byte rows
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 64, SA, 1, "e4m3", B, 64, SB, 4, D, 64)   # ld_sfa < K/32
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 64, SA, 2, "e4m3", B, 64, SB, 4, D, 64)   # ld_sfa % 4
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 64, SA + 2, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_NULL", s, 64, 64, 64, "e4m3", A, 64, 0, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ALIAS", s, 64, 64, 64, "e4m3", A, 64, D + 64, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_SHAPE", s, 64, 64, 64, "e4m3", A, 1 << 24, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
     a = lambda *x: bsm.bsm_tile_add_scalar_f32(*x, stream=0)
     expect("BSM_E_SHAPE", a, A, B, -1, 1.0)
     expect("BSM_E_ALIGN", a, A + 4, B, 8, 1.0)

@@ -23,6 +23,20 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (they
+// complete in issue order), i.e. every copy issued before the last N has landed.
+#define BSM_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
+// Direct HBM -> LDS copy of 4 bytes per lane (lane l lands at lds_addr + 4 * l).
+__device__ __forceinline__ void dma4s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb), "s"(a) : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(BSM_LDS const void*)p;
 }
@@ -45,24 +59,127 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   tn = in / gsize;
 }
 
-// D = s * acc (+ D) for a 128 x 128 wave sub-tile held as 4 x 4 blocks of
-// v_mfma 32x32 accumulators: register r of block (mt, nt) is row
-// 32mt + 8(r/4) + 4(l/32) + r%4, column 32nt + l%32.
-__device__ __forceinline__ void store_tile(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
-                                           int64_t col0, int lane, float sgn, int accum, const f32x16 (&acc)[4][4]) {
+// Waits until at most N of this wave's vector-memory operations are outstanding (they
+// complete in issue order) and all of its LDS operations are done, then joins the
+// workgroup barrier. The compiler does not count the inline-assembly copies, so the
+// kernels place these waits themselves.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Instruction-order fences. The MFMA builtins are pure, so instruction selection may
+// place them on either side of the scheduling fences and barriers; an empty volatile asm
+// that claims to rewrite a value pins the computations around it: pin_acc after MFMAs
+// that must issue before a barrier, pin_frag on the operands of MFMAs that must issue
+// after the LDS reads that precede them.
+__device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) asm volatile("" : "+a"(acc[i][j])::"memory");
+}
+__device__ __forceinline__ void pin_frag(uint4& x) {
+  u32x4 v = {x.x, x.y, x.z, x.w};
+  asm volatile("" : "+v"(v)::"memory");
+  x = make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void pin_word(uint32_t& x) { asm volatile("" : "+v"(x)::"memory"); }
+
+// ---- K-major operand tiles: 256 rows x 64 bytes of K, 16 KiB per tile -------------
+// The 16-byte chunk c of LDS row r is stored at physical chunk c ^ ((r >> 2) & 3): the
+// 16 rows that one 16-lane group of a 16-byte LDS read touches then cover all 64 banks
+// (4 rows per 256-byte bank window, 4 distinct chunks per row position).
+constexpr int kKRowBytes = 64;
+constexpr int kKTileBytes = 256 * kKRowBytes;
+
+// Per-lane offsets (bytes, relative to the tile's first row at the tile's first K byte)
+// of the 4 direct LDS copies a wave issues per tile. Copy j of wave w fills LDS bytes
+// [1024 (w + 4j), +1024), i.e. rows 16 (w + 4j) .. +15: lane l writes row
+// 16 (w + 4j) + l/4, physical chunk l%4, which holds logical chunk (l%4) ^ (l/16).
+// Rows past the operand's last row re-read the last row (their results are not stored).
+__device__ __forceinline__ void kmajor_dma_offsets(int64_t ld_bytes, int64_t row0, int64_t rows, int w, int lane,
+                                                   uint32_t (&off)[4]) {
+  const int c = (lane & 3) ^ (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int64_t rg = min(row0 + 16 * (w + 4 * j) + (lane >> 2), rows - 1);
+    off[j] = (uint32_t)((rg - row0) * ld_bytes + 16 * c);
+  }
+}
+
+__device__ __forceinline__ void issue_tile4(const void* base, const uint32_t (&off)[4], uint32_t lds_tile, int w) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) dma16s(base, off[j], lds_tile + 1024 * (w + 4 * j));
+}
+
+// Byte offset inside a K-major tile of logical chunk `chunk` of the row that lane l
+// reads for a 32-row fragment block (block and wave offsets are multiples of 16 rows,
+// so they add to this without changing the swizzle).
+__device__ __forceinline__ uint32_t kmajor_frag_base(int lane, int chunk) {
+  const int r = lane & 31;
+  return (uint32_t)(r * kKRowBytes + ((chunk ^ ((r >> 2) & 3)) << 4));
+}
+
+// The same tile for a partial last K tile, through registers: bytes at or past kb_end
+// (relative to the row start) are zero. Same row / chunk assignment as the copies.
+__device__ __forceinline__ void kmajor_fill_masked(const uint8_t* __restrict__ p, int64_t ld_bytes, int64_t row0,
+                                                   int64_t rows, int64_t kb0, int64_t kb_end, uint8_t* tile,
+                                                   int w, int lane) {
+  const int c = (lane & 3) ^ (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int i = w + 4 * j;
+    const int64_t rg = min(row0 + 16 * i + (lane >> 2), rows - 1);
+    const int64_t kb = kb0 + 16 * c;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (kb < kb_end) {
+      v = *(const uint4*)(p + rg * ld_bytes + kb);
+      const int64_t valid = kb_end - kb;  // bytes kept
+      uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const int64_t nb = valid - 4 * d;
+        wd[d] &= nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
+      }
+      v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    lds_write_b128(tile + 1024 * i + 16 * lane, v);
+  }
+}
+
+// D = s * acc (+ D) for a 128 x 128 wave sub-tile held as 4 x 4 blocks of v_mfma 32x32
+// accumulators computed with the operands swapped (the MFMA row index runs over N):
+// register 4q + e of block (mt, nt) is output row 32mt + l%32, column
+// 32nt + 8q + 4(l/32) + e, so each group of four registers is 16 contiguous bytes of a
+// row of D and moves with one dwordx4 load / store (element-wise only at a ragged N).
+__device__ __forceinline__ void store_tile_t(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
+                                             int64_t col0, int lane, float sgn, int accum,
+                                             const f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
+    const int64_t row = row0 + 32 * mt + (lane & 31);
+    if (row >= M) continue;
+    float* drow = D + row * ldd;
 #pragma unroll
     for (int nt = 0; nt < 4; nt++) {
-      const int64_t col = col0 + 32 * nt + (lane & 31);
-      const bool cok = col < N;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t row = row0 + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (cok && row < M) {
-          float* d = D + row * ldd + col;
-          const float v = sgn * acc[mt][nt][r];
-          *d = accum ? *d + v : v;
+      for (int q = 0; q < 4; q++) {
+        const int64_t col = col0 + 32 * nt + 8 * q + 4 * (lane >> 5);
+        float4 v = make_float4(sgn * acc[mt][nt][4 * q], sgn * acc[mt][nt][4 * q + 1], sgn * acc[mt][nt][4 * q + 2],
+                               sgn * acc[mt][nt][4 * q + 3]);
+        if (col + 3 < N) {
+          float4* d = (float4*)(drow + col);
+          if (accum) {
+            const float4 o = *d;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *d = v;
+        } else {
+          const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            if (col + i < N) drow[col + i] = accum ? drow[col + i] + e[i] : e[i];
         }
       }
     }

@@ -6,21 +6,24 @@
 // first K step starts from D when accumulating and from zero otherwise.
 //
 // gfx950 design:
-//  - workgroup tile 256 x 256, K tile 64, four wave64s in a 2 x 2 grid, each owning a
+//  - workgroup tile 256 x 256, K tile 32, four wave64s in a 2 x 2 grid, each owning a
 //    128 x 128 sub-tile as 4 x 4 v_mfma_f32_32x32x16 accumulators (256 fp32 per lane,
-//    held in AGPRs);
+//    held in AGPRs). The MFMA is issued with the operands swapped (B fragment first), so
+//    a lane ends up holding four consecutive output columns per register group and the
+//    epilogue moves D in 16-byte pieces;
 //  - operand tiles stream HBM -> LDS with global_load_lds_dwordx4 (no register
 //    staging): an SGPR tile base plus per-lane 32-bit offsets that stay fixed over the
-//    whole K loop; two LDS stages (2 x 64 KiB), one barrier per K tile;
-//  - K-major tiles: 128-byte rows, 16-byte chunk c of row r stored at chunk
-//    c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group reads with ds_read_b128
+//    whole K loop; four LDS stages (4 x 32 KiB) with K tile kt+3 in flight while tile kt
+//    is consumed, and one barrier per K tile that waits only for tile kt+1;
+//  - K-major tiles: 64-byte rows, 16-byte chunk c of row r stored at chunk
+//    c ^ ((r >> 2) & 3), so the 16 rows one 16-lane group reads with ds_read_b128
 //    cover all 64 LDS banks;
 //  - MN-major tiles (the transposed storage): 512-byte k-rows, chunk c of k-row kr
 //    stored at c ^ (4 * (kr & 3)); fragments come from ds_read_b64_tr_b16, the LDS
 //    transpose read (the analog of ldmatrix .trans in "ldmatrix / stmatrix",
 //    Transpose and stores), whose 32-lane groups again cover all banks;
-//  - software pipeline: the 16 MFMAs of one K step overlap the LDS reads of the next
-//    step and the DMA of the next K tile; the stage barrier sits inside the last step;
+//  - software pipeline: the 16 MFMAs of one K step overlap the LDS reads of the other
+//    step; the stage barrier sits between the two steps of a K tile;
 //  - M/N edges clamp the rows that are loaded and mask the stores; a ragged last K
 //    tile is loaded through registers with the elements past K zeroed.
 #include "gemm_common.hpp"
@@ -29,34 +32,32 @@
 namespace bsm {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int TILE_BYTES = 256 * BK * 2;  // one operand tile: 32 KiB
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int TILE_BYTES = 256 * BK * 2;  // one operand tile: 16 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int NST = 4;                    // LDS stages
+constexpr int PF = NST - 1;               // K tiles in flight ahead of the one consumed
+constexpr int DMA_PER_TILE = 8;           // copies per wave per K tile (4 A + 4 B)
+static_assert(TILE_BYTES == gemm::kKTileBytes, "K-major tile geometry");
 
-// Per-lane byte offsets (relative to the tile's global base) of the 8 direct LDS copies
-// a wave issues for one operand tile. Copy j of wave w fills LDS bytes
-// [1024 * (w + 4j), +1024): lane l writes 16 bytes at 1024 * (w + 4j) + 16 * l.
-//  K-major: LDS row r = 8(w+4j) + l/8 holds global row row0 + r (clamped to the last
-//           row), its physical chunk l%8 holds logical chunk (l%8) ^ ((r >> 1) & 7);
+// Per-lane byte offsets (relative to the tile's global base) of the 4 direct LDS copies
+// a wave issues for one operand tile; copy j of wave w fills LDS bytes
+// [1024 (w + 4j), +1024).
+//  K-major: the shared 64-byte-row layout (gemm::kmajor_dma_offsets);
 //  MN-major: LDS k-row kr = 2(w+4j) + l/32 holds global k-row k0 + kr, its physical
 //           chunk l%32 holds logical chunk (l%32) ^ (4 (kr & 3)) (columns clamped to
 //           the last 8-aligned chunk).
 template <bool KMAJ>
 __device__ __forceinline__ void dma_offsets(int64_t ld, int64_t row0, int64_t rows, int w, int lane,
-                                            uint32_t (&off)[8]) {
+                                            uint32_t (&off)[4]) {
   if (KMAJ) {
-    const int c = (lane & 7) ^ (((8 * w + (lane >> 3)) >> 1) & 7);
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int64_t rg = min(row0 + 8 * w + 32 * j + (lane >> 3), rows - 1);
-      off[j] = (uint32_t)(((rg - row0) * ld + 8 * c) * 2);
-    }
+    gemm::kmajor_dma_offsets(2 * ld, row0, rows, w, lane, off);
   } else {
     const int kr0 = 2 * w + (lane >> 5);
     const int c = (lane & 31) ^ ((kr0 & 3) << 2);
     const int64_t col = min(row0 + 8 * c, (rows - 1) & ~int64_t(7));
 #pragma unroll
-    for (int j = 0; j < 8; j++) off[j] = (uint32_t)(((kr0 + 8 * j) * ld + (col - row0)) * 2);
+    for (int j = 0; j < 4; j++) off[j] = (uint32_t)(((kr0 + 8 * j) * ld + (col - row0)) * 2);
   }
 }
 
@@ -66,39 +67,22 @@ __device__ __forceinline__ const uint16_t* tile_base(const uint16_t* p, int64_t 
   return KMAJ ? p + row0 * ld + k0 : p + k0 * ld + row0;
 }
 
-__device__ __forceinline__ void issue_tile(const uint16_t* base, const uint32_t (&off)[8], uint32_t lds_tile, int w) {
-#pragma unroll
-  for (int j = 0; j < 8; j++) gemm::dma16s(base, off[j], lds_tile + 1024 * (w + 4 * j));
-}
-
 // The same tile for a partial K tile: through registers, elements with k >= K zeroed.
 template <bool KMAJ>
 __device__ __forceinline__ void fill_tile_masked(const uint16_t* __restrict__ p, int64_t ld, int64_t row0,
                                                  int64_t rows, int64_t k0, int64_t K, uint8_t* tile, int w, int lane) {
+  if (KMAJ) {
+    gemm::kmajor_fill_masked((const uint8_t*)p, 2 * ld, row0, rows, 2 * k0, 2 * K, tile, w, lane);
+    return;
+  }
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
+  for (int j = 0; j < 4; j++) {
     const int i = w + 4 * j;
+    const int kr = 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ ((kr & 3) << 2);
+    const int64_t col = min(row0 + 8 * c, (rows - 1) & ~int64_t(7));
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (KMAJ) {
-      const int r = 8 * i + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const int64_t rg = min(row0 + r, rows - 1);
-      const int64_t k = k0 + 8 * c;
-      if (k < K) {
-        v = *(const uint4*)(p + rg * ld + k);
-        const int64_t valid = K - k;  // elements k..k+7 kept while < K
-        uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-          if (e >= valid) wd[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      }
-    } else {
-      const int kr = 2 * i + (lane >> 5);
-      const int c = (lane & 31) ^ ((kr & 3) << 2);
-      const int64_t col = min(row0 + 8 * c, (rows - 1) & ~int64_t(7));
-      if (k0 + kr < K) v = *(const uint4*)(p + (k0 + kr) * ld + col);
-    }
+    if (k0 + kr < K) v = *(const uint4*)(p + (k0 + kr) * ld + col);
     lds_write_b128(tile + 1024 * i + 16 * lane, v);
   }
 }
@@ -112,7 +96,7 @@ struct Frag<BSM_F16> { typedef f16x8 T; };
 
 // LDS read addresses of the v_mfma_f32_32x32x16 operand fragments. Lane l must hold
 // operand (row wbase + 32t + l%32, k 16ks + 8(l/32) + e), e = 0..7.
-//  K-major: one ds_read_b128 at 128 wbase + 4096t + base[ks];
+//  K-major: one ds_read_b128 at 64 wbase + 2048t + base[ks] (logical chunk 2ks + l/32);
 //  MN-major: two ds_read_b64_tr_b16 (h = 0, 1) at 2 wbase + base[t] + 8192ks + 2048h,
 //   where within each 16-lane group (i = l%16, G = l/16) lane i provides k-row
 //   16ks + 8(G/2) + 4h + i/4 and columns 16(G%2) + 4(i%4)..+3, and receives the
@@ -121,9 +105,9 @@ struct Frag<BSM_F16> { typedef f16x8 T; };
 template <bool KMAJ>
 __device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[4]) {
   if (KMAJ) {
-    const int r = lane & 31;
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) base[ks] = (uint32_t)(r * 128 + (((2 * ks + (lane >> 5)) ^ ((r >> 1) & 7)) << 4));
+    for (int ks = 0; ks < 2; ks++) base[ks] = gemm::kmajor_frag_base(lane, 2 * ks + (lane >> 5));
+    base[2] = base[3] = 0;
   } else {
     const int i = lane & 15, G = lane >> 4;
     const uint32_t L = (uint32_t)((8 * (G >> 1) + (i >> 2)) * 512 + 16 * (2 * (G & 1) + ((i & 3) >> 1)) + 8 * (i & 1) +
@@ -136,7 +120,7 @@ __device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[4]) {
 template <bool KMAJ>
 __device__ __forceinline__ uint4 read_frag(const uint8_t* tile, int wbase, const uint32_t (&base)[4], int ks, int t) {
   if (KMAJ) {
-    return lds_read_b128(tile + wbase * 128 + 4096 * t + base[ks]);
+    return lds_read_b128(tile + wbase * 64 + 2048 * t + base[ks]);
   } else {
     const uint8_t* p = tile + 2 * wbase + base[t] + 8192 * ks;
     const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
@@ -145,12 +129,15 @@ __device__ __forceinline__ uint4 read_frag(const uint8_t* tile, int wbase, const
   }
 }
 
+// One 32x32x16 MFMA with the B fragment as the first source: the result block is
+// indexed [n][m], so lane l holds output row m = l%32 and, in registers 4q..4q+3,
+// columns n = 8q + 4(l/32) + 0..3.
 template <int DT>
-__device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma(uint4 b, uint4 a, f32x16 c) {
   typedef typename Frag<DT>::T T;
-  const T av = __builtin_bit_cast(T, a), bv = __builtin_bit_cast(T, b);
-  if constexpr (DT == BSM_BF16) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
-  else return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
+  const T bv = __builtin_bit_cast(T, b), av = __builtin_bit_cast(T, a);
+  if constexpr (DT == BSM_BF16) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, av, c, 0, 0, 0);
 }
 
 template <bool AK, bool BKM>
@@ -168,12 +155,29 @@ __device__ __forceinline__ void mfma_step(const uint4 (&af)[4], const uint4 (&bf
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-    for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma<DT>(af[mt], bf[nt], acc[mt][nt]);
+    for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma<DT>(bf[nt], af[mt], acc[mt][nt]);
+}
+
+__device__ __forceinline__ void pin_step(uint4 (&af)[4], uint4 (&bf)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    gemm::pin_frag(af[t]);
+    gemm::pin_frag(bf[t]);
+  }
+}
+
+template <bool AK, bool BKM>
+__device__ __forceinline__ void issue_stage(const uint16_t* A, int64_t lda, int64_t m0, const uint16_t* B,
+                                            int64_t ldb, int64_t n0, int kt, const uint32_t (&aoff)[4],
+                                            const uint32_t (&boff)[4], uint32_t stage, int w) {
+  const int64_t k0 = (int64_t)kt * BK;
+  gemm::issue_tile4(tile_base<AK>(A, lda, m0, k0), aoff, stage, w);
+  gemm::issue_tile4(tile_base<BKM>(B, ldb, n0, k0), boff, stage + TILE_BYTES, w);
 }
 
 template <int DT, bool AK, bool BKM>
 __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
 
-  uint32_t aoff[8], boff[8], abase[4], bbase[4];
+  uint32_t aoff[4], boff[4], abase[4], bbase[4];
   dma_offsets<AK>(a.lda, m0, a.M, w, lane, aoff);
   dma_offsets<BKM>(a.ldb, n0, a.N, w, lane, boff);
   frag_bases<AK>(lane, abase);
@@ -202,60 +206,52 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
   const uint32_t lds0 = gemm::lds_addr(lds);
   uint4 a0[4], b0[4], a1[4], b1[4];
   if (nfull > 0) {
-    issue_tile(tile_base<AK>(A, a.lda, m0, 0), aoff, lds0, w);
-    issue_tile(tile_base<BKM>(B, a.ldb, n0, 0), boff, lds0 + TILE_BYTES, w);
-    gemm::wait_dma();
-    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PF; p++)
+      issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(p, nfull - 1), aoff, boff, lds0 + p * STAGE_BYTES, w);
+    gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
     read_step<AK, BKM>(lds, lds + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
   }
-  // Software pipeline over K tiles (two LDS stages, two fragment register sets): while
-  // the 16 MFMAs of K step s run, the fragments of step s+1 are in flight and the DMA of
-  // the next K tile streams into the other stage. The stage barrier sits before the
-  // MFMAs of step 3, when every wave holds all fragments of the current stage.
-  // The loop body is branch-free so that the scheduling fences hold: on the last K tile
-  // the prefetch re-reads the last tile (clamped index) into the stage nobody reads again.
+  // K tile kt lives in stage kt % NST. Iteration kt: read step 1 of tile kt and start
+  // the copy of tile kt + PF into the stage that tile kt - 1 used (every wave finished
+  // reading it before the previous barrier); 16 MFMAs of step 0; barrier once this
+  // wave's copies of tile kt + 1 have landed (and its LDS reads are done); read step 0
+  // of tile kt + 1; 16 MFMAs of step 1. The body is branch-free so that the scheduling
+  // fences hold: past the last tile the copies re-read the last tile (clamped index)
+  // into stages nobody reads again.
   for (int kt = 0; kt < nfull; kt++) {
-    const int cur = kt & 1;
-    const uint8_t* ta = lds + cur * STAGE_BYTES;
-    const uint8_t* tb = ta + TILE_BYTES;
-    const uint8_t* na = lds + (cur ^ 1) * STAGE_BYTES;
-    read_step<AK, BKM>(ta, tb, 1, wa, wb, abase, bbase, a1, b1);
-    {
-      const uint32_t nxt = lds0 + (cur ^ 1) * STAGE_BYTES;
-      const int64_t k1 = (int64_t)min(kt + 1, nfull - 1) * BK;
-      issue_tile(tile_base<AK>(A, a.lda, m0, k1), aoff, nxt, w);
-      issue_tile(tile_base<BKM>(B, a.ldb, n0, k1), boff, nxt + TILE_BYTES, w);
-    }
+    const uint8_t* ta = lds + (kt % NST) * STAGE_BYTES;
+    const uint8_t* na = lds + ((kt + 1) % NST) * STAGE_BYTES;
+    read_step<AK, BKM>(ta, ta + TILE_BYTES, 1, wa, wb, abase, bbase, a1, b1);
+    issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(kt + PF, nfull - 1), aoff, boff,
+                         lds0 + ((kt + PF) % NST) * STAGE_BYTES, w);
+    pin_step(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step<DT>(a0, b0, acc);
+    gemm::pin_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
-    read_step<AK, BKM>(ta, tb, 2, wa, wb, abase, bbase, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<DT>(a1, b1, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    read_step<AK, BKM>(ta, tb, 3, wa, wb, abase, bbase, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<DT>(a0, b0, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    gemm::wait_dma();
-    __syncthreads();
+    gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
     read_step<AK, BKM>(na, na + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
+    pin_step(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step<DT>(a1, b1, acc);
+    gemm::pin_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // Every copy has landed and every wave is done with LDS before the stage is refilled
+  // (and before the workgroup can end with copies in flight).
+  gemm::stage_barrier<0>();
   if (tail) {
-    uint8_t* st = lds + (nfull & 1) * STAGE_BYTES;
     const int64_t k0 = (int64_t)nfull * BK;
-    fill_tile_masked<AK>(A, a.lda, m0, a.M, k0, a.K, st, w, lane);
-    fill_tile_masked<BKM>(B, a.ldb, n0, a.N, k0, a.K, st + TILE_BYTES, w, lane);
+    fill_tile_masked<AK>(A, a.lda, m0, a.M, k0, a.K, lds, w, lane);
+    fill_tile_masked<BKM>(B, a.ldb, n0, a.N, k0, a.K, lds + TILE_BYTES, w, lane);
     __syncthreads();
     for (int ks = 0; ks < (tail + 15) / 16; ks++) {
-      read_step<AK, BKM>(st, st + TILE_BYTES, ks, wa, wb, abase, bbase, a0, b0);
+      read_step<AK, BKM>(lds, lds + TILE_BYTES, ks, wa, wb, abase, bbase, a0, b0);
       mfma_step<DT>(a0, b0, acc);
     }
   }
-  gemm::store_tile(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
+  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
 }
 
 template <int DT, bool AK, bool BKM>
@@ -280,11 +276,10 @@ template <bool KMAJ>
 __global__ __launch_bounds__(256) void k_debug_fragments(const uint16_t* __restrict__ src, uint16_t* dump) {
   __shared__ __attribute__((aligned(1024))) uint8_t tile[TILE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t off[8], base[4];
+  uint32_t off[4], base[4];
   dma_offsets<KMAJ>(KMAJ ? BK : BM, 0, BM, w, lane, off);
-  issue_tile(src, off, gemm::lds_addr(tile), w);
-  gemm::wait_dma();
-  __syncthreads();
+  gemm::issue_tile4(src, off, gemm::lds_addr(tile), w);
+  gemm::stage_barrier<0>();
   frag_bases<KMAJ>(lane, base);
   for (int mb = 2 * w; mb < 2 * w + 2; mb++) {
     for (int ks = 0; ks < BK / 16; ks++) {

@@ -13,12 +13,16 @@
 //    [16(l/32), +16) and [32 + 16(l/32), +16) of the 64-K step;
 //  - fp4 operand (16 bytes per lane, two elements per byte, low nibble first): lane l
 //    holds row l%32 with k in [32(l/32), +32);
-//  - workgroup tile 256 x 256 x (128 bytes of K per row), four wave64s with 128 x 128
-//    sub-tiles (4 x 4 accumulators of 16 fp32 in AGPRs); operand tiles HBM -> LDS with
-//    global_load_lds_dwordx4 into two stages (same 128-byte-row XOR swizzle as the
-//    dense kernel); scales go straight to registers one K tile ahead as dword loads;
-//  - the MFMAs of one 64-K step overlap the LDS reads of the next step and the DMA of
-//    the next K tile; the stage barrier sits before the MFMAs of the last step.
+//  - the MFMA is issued with the operands swapped (B first, with B's scales), so a lane
+//    holds four consecutive output columns per register group (16-byte epilogue);
+//  - workgroup tile 256 x 256 x (64 bytes of K per row), four wave64s with 128 x 128
+//    sub-tiles (4 x 4 accumulators of 16 fp32 in AGPRs); operand tiles and the scale
+//    word of each row stream HBM -> LDS with global_load_lds_dwordx4 / _dword into four
+//    stages (64-byte-row XOR swizzle shared with the dense kernel), three K tiles ahead
+//    of the one consumed; one barrier per K tile waits only for the next tile;
+//  - fp4 (two 64-K steps per tile): the MFMAs of one step overlap the LDS reads of the
+//    other; fp8 (one step per tile): the barrier sits after the first 8 MFMAs of a tile
+//    and the next tile's fragments are read while the last 8 run (two register sets).
 #include "gemm_common.hpp"
 #include "../../include/bsm.h"
 
@@ -26,164 +30,177 @@ namespace bsm {
 namespace {
 
 constexpr int BM = 256, BN = 256;
-constexpr int ROWB = 128;                  // bytes of K per row per K tile
-constexpr int TILE_BYTES = 256 * ROWB;     // 32 KiB per operand tile
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int ROWB = 64;                                    // bytes of K per row per K tile
+constexpr int TILE_BYTES = 256 * ROWB;                      // 16 KiB per operand tile
+constexpr int SF_BYTES = 256 * 4;                           // one scale word per row
+constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * SF_BYTES;  // A, B, SFA, SFB
+constexpr int NST = 4;                                      // LDS stages
+constexpr int PF = NST - 1;                                 // K tiles in flight ahead
+constexpr int DMA_PER_TILE = 10;                            // per wave: 4 A + 4 B + 1 + 1 scale
+static_assert(TILE_BYTES == gemm::kKTileBytes, "K-major tile geometry");
 
 template <int FMT>
 struct Fmt {
-  static constexpr int KT = FMT == 4 ? 256 : 128;  // K elements per K tile
-  static constexpr int STEPS = FMT == 4 ? 4 : 2;    // 64-K MFMA steps per K tile
-  static constexpr int SFW = FMT == 4 ? 2 : 1;      // scale dwords per row per K tile
-  static constexpr int EPB = FMT == 4 ? 2 : 1;      // elements per byte
+  static constexpr int KT = FMT == 4 ? 128 : 64;  // K elements per K tile
+  static constexpr int STEPS = FMT == 4 ? 2 : 1;  // 64-K MFMA steps per K tile
+  static constexpr int EPB = FMT == 4 ? 2 : 1;    // elements per byte
+  static constexpr int BPT = KT / 32;             // scale blocks per K tile
 };
 
-// Per-lane byte offsets of the 8 direct LDS copies of one operand tile (relative to the
-// tile's global base): LDS row r = 8(w+4j) + l/8 holds global row row0 + r (clamped),
-// physical chunk l%8 holds logical chunk (l%8) ^ ((r >> 1) & 7).
-__device__ __forceinline__ void dma_offsets(int64_t ldb, int64_t row0, int64_t rows, int w, int lane,
-                                            uint32_t (&off)[8]) {
-  const int c = (lane & 7) ^ (((8 * w + (lane >> 3)) >> 1) & 7);
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int64_t rg = min(row0 + 8 * w + 32 * j + (lane >> 3), rows - 1);
-    off[j] = (uint32_t)((rg - row0) * ldb + 16 * c);
-  }
-}
-
-__device__ __forceinline__ void issue_tile(const uint8_t* base, const uint32_t (&off)[8], uint32_t lds_tile, int w) {
-#pragma unroll
-  for (int j = 0; j < 8; j++) gemm::dma16s(base, off[j], lds_tile + 1024 * (w + 4 * j));
-}
-
-// Partial last K tile: chunks at or past kb_end (bytes) are zero.
-__device__ __forceinline__ void fill_tile_masked(const uint8_t* __restrict__ p, int64_t ldb, int64_t row0,
-                                                 int64_t rows, int64_t kb0, int64_t kb_end, uint8_t* tile, int w,
-                                                 int lane) {
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int i = w + 4 * j;
-    const int r = 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int64_t rg = min(row0 + r, rows - 1);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (kb0 + 16 * c < kb_end) v = *(const uint4*)(p + rg * ldb + kb0 + 16 * c);
-    lds_write_b128(tile + 1024 * i + 16 * lane, v);
-  }
-}
-
-// LDS address bases of the operand fragments (row wbase + 32t + l%32): the 16-byte
-// chunk of the fragment of step s sits at 128 wbase + 4096t + base[.].
-//  fp8: chunks 4s + l/32 (k 16(l/32)..) and 4s + 2 + l/32 (k 32 + 16(l/32)..) -> base[2s + h];
-//  fp4: chunk 2s + l/32 -> base[s].
+// Byte offset inside a scale row of the aligned 32-bit word holding the first block of
+// K tile kt (fp4: the tile's 4 blocks; fp8: a pair of tiles, this one at byte 2 (kt&1)).
 template <int FMT>
-__device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[4]) {
-  const int r = lane & 31, sw = (r >> 1) & 7, hi = lane >> 5;
+__device__ __forceinline__ int64_t sf_word(int kt) {
+  return FMT == 4 ? 4 * (int64_t)kt : 4 * (int64_t)(kt >> 1);
+}
+
+struct Ops {
+  const uint8_t* A; int64_t lda_b; uint32_t aoff[4];
+  const uint8_t* B; int64_t ldb_b; uint32_t boff[4];
+  const uint8_t* SFA; int64_t ld_sfa; uint32_t sfa_off;
+  const uint8_t* SFB; int64_t ld_sfb; uint32_t sfb_off;
+};
+
+// Copies of K tile kt (operand rows from the tile's first row, scale rows 64w + l).
+template <int FMT>
+__device__ __forceinline__ void issue_stage(const Ops& o, int kt, uint32_t stage, int w) {
+  const int64_t kb = (int64_t)kt * ROWB;
+  gemm::issue_tile4(o.A + kb, o.aoff, stage, w);
+  gemm::issue_tile4(o.B + kb, o.boff, stage + TILE_BYTES, w);
+  gemm::dma4s(o.SFA + sf_word<FMT>(kt), o.sfa_off, stage + 2 * TILE_BYTES + 256 * w);
+  gemm::dma4s(o.SFB + sf_word<FMT>(kt), o.sfb_off, stage + 2 * TILE_BYTES + SF_BYTES + 256 * w);
+}
+
+// Fragments (and raw scale words) of one K tile for one wave: af/bf[t][0..1] are the
+// 16-byte chunks of 32-row block t, sa/sb[t] the scale word of the lane's row.
+template <int FMT>
+struct Set {
+  uint4 af[4][2], bf[4][2];
+  uint32_t sa[4], sb[4];
+};
+
+// LDS offsets of the fragment chunks: logical chunk 2q + l/32 of the lane's row. fp8
+// uses q = 0, 1 (k 16(l/32).. and 32 + 16(l/32)..) of its single step; fp4 uses q = s.
+__device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[2]) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int chunk = FMT == 4 ? 2 * q + hi : 4 * (q >> 1) + 2 * (q & 1) + hi;
-    base[q] = (uint32_t)(r * 128 + ((chunk ^ sw) << 4));
+  for (int q = 0; q < 2; q++) base[q] = gemm::kmajor_frag_base(lane, 2 * q + (lane >> 5));
+}
+
+// Reads the fragments of 64-K step s of the stage at `st` (fp8: s = 0) for this wave.
+template <int FMT>
+__device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wa, int wb, const uint32_t (&base)[2],
+                                           uint4 (&af)[4][2], uint4 (&bf)[4][2]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint8_t* pa = st + wa * 64 + 2048 * t;
+    const uint8_t* pb = st + TILE_BYTES + wb * 64 + 2048 * t;
+    if (FMT == 4) {
+      const uint32_t bs = s ? base[1] : base[0];
+      af[t][0] = lds_read_b128(pa + bs);
+      bf[t][0] = lds_read_b128(pb + bs);
+    } else {
+      af[t][0] = lds_read_b128(pa + base[0]);
+      af[t][1] = lds_read_b128(pa + base[1]);
+      bf[t][0] = lds_read_b128(pb + base[0]);
+      bf[t][1] = lds_read_b128(pb + base[1]);
+    }
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void read_frag(const uint8_t* tile, int wbase, const uint32_t (&base)[4], int s, int t,
-                                          uint4 (&f)[2]) {
-  const uint8_t* p = tile + wbase * 128 + 4096 * t;
-  if (FMT == 4) {
-    f[0] = lds_read_b128(p + base[s]);
-  } else {
-    f[0] = lds_read_b128(p + base[2 * s]);
-    f[1] = lds_read_b128(p + base[2 * s + 1]);
+__device__ __forceinline__ void read_scales(const uint8_t* st, int wa, int wb, int lane, uint32_t (&sa)[4],
+                                            uint32_t (&sb)[4]) {
+  const uint8_t* pa = st + 2 * TILE_BYTES;
+  const uint8_t* pb = pa + SF_BYTES;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    sa[t] = *(const BSM_LDS uint32_t*)(pa + 4 * (wa + 32 * t + (lane & 31)));
+    sb[t] = *(const BSM_LDS uint32_t*)(pb + 4 * (wb + 32 * t + (lane & 31)));
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void read_step(const uint8_t* ta, const uint8_t* tb, int s, int wa, int wb,
-                                          const uint32_t (&ab)[4], const uint32_t (&bb)[4], uint4 (&af)[4][2],
-                                          uint4 (&bf)[4][2]) {
+// Right-shift so that byte 0 (and byte 2 for fp4's second step) holds the block this
+// lane feeds: lanes 32..63 carry the second 32-K block of each 64-K step.
+__device__ __forceinline__ void shift_scales(uint32_t (&sa)[4], uint32_t (&sb)[4], int sh) {
 #pragma unroll
-  for (int t = 0; t < 4; t++) read_frag<FMT>(ta, wa, ab, s, t, af[t]);
-#pragma unroll
-  for (int t = 0; t < 4; t++) read_frag<FMT>(tb, wb, bb, s, t, bf[t]);
+  for (int t = 0; t < 4; t++) {
+    sa[t] >>= sh;
+    sb[t] >>= sh;
+  }
 }
 
 template <int FMT, int SEL>
-__device__ __forceinline__ f32x16 mfma_sc(const uint4 (&a)[2], const uint4 (&b)[2], f32x16 c, uint32_t sa,
-                                          uint32_t sb) {
+__device__ __forceinline__ f32x16 mfma_sc(const uint4 (&b)[2], const uint4 (&a)[2], f32x16 c, uint32_t sb,
+                                          uint32_t sa) {
   i32x8 av, bv;
-  av[0] = a[0].x; av[1] = a[0].y; av[2] = a[0].z; av[3] = a[0].w;
   bv[0] = b[0].x; bv[1] = b[0].y; bv[2] = b[0].z; bv[3] = b[0].w;
+  av[0] = a[0].x; av[1] = a[0].y; av[2] = a[0].z; av[3] = a[0].w;
   if (FMT == 4) {
     av[4] = av[5] = av[6] = av[7] = 0;
     bv[4] = bv[5] = bv[6] = bv[7] = 0;
   } else {
-    av[4] = a[1].x; av[5] = a[1].y; av[6] = a[1].z; av[7] = a[1].w;
     bv[4] = b[1].x; bv[5] = b[1].y; bv[6] = b[1].z; bv[7] = b[1].w;
+    av[4] = a[1].x; av[5] = a[1].y; av[6] = a[1].z; av[7] = a[1].w;
   }
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FMT, FMT, SEL, (int)sa, SEL, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, FMT, FMT, SEL, (int)sb, SEL, (int)sa);
 }
 
-// 16 MFMAs of 64-K step s. Scale word s/2 of each row block holds, after the per-lane
-// shift, the block of step 2q in byte 0 and of step 2q+1 in byte 2 (op_sel 0 / 2).
-template <int FMT>
-__device__ __forceinline__ void mfma_step(const uint4 (&af)[4][2], const uint4 (&bf)[4][2], int s,
-                                          const uint32_t (&sa)[4][2], const uint32_t (&sb)[4][2],
-                                          f32x16 (&acc)[4][4]) {
-  const int q = s >> 1;
+template <int FMT, int MT0, int MT1>
+__device__ __forceinline__ void pin_set(uint4 (&af)[4][2], uint4 (&bf)[4][2], uint32_t (&sa)[4], uint32_t (&sb)[4]) {
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-      if (s & 1) acc[mt][nt] = mfma_sc<FMT, 2>(af[mt], bf[nt], acc[mt][nt], sa[mt][q], sb[nt][q]);
-      else acc[mt][nt] = mfma_sc<FMT, 0>(af[mt], bf[nt], acc[mt][nt], sa[mt][q], sb[nt][q]);
+  for (int t = 0; t < 4; t++) {
+    if (t >= MT0 && t < MT1) {
+      gemm::pin_frag(af[t][0]);
+      if (FMT != 4) gemm::pin_frag(af[t][1]);
+      gemm::pin_word(sa[t]);
     }
-}
-
-// Scale words of one K tile for this lane's 4 row blocks: word q holds the scales of
-// blocks blk0 + 4q .. +3 of each row (rows start 4-byte aligned). A word that would lie
-// wholly past the last block (nblk) is not read: its slot re-reads word 0 and
-// prep_scales replaces its bytes. Loaded one K tile ahead and only consumed after the
-// next stage barrier (prep_scales), so the loads never stall.
-template <int FMT>
-__device__ __forceinline__ void load_scales(const uint8_t* __restrict__ sf_rows, const uint32_t (&roff)[4],
-                                            int64_t blk0, int64_t nblk, uint32_t (&raw)[4][2]) {
-#pragma unroll
-  for (int q = 0; q < Fmt<FMT>::SFW; q++) {
-    const int64_t blk = blk0 + 4 * q < nblk ? blk0 + 4 * q : blk0;
-#pragma unroll
-    for (int t = 0; t < 4; t++) raw[t][q] = *(const uint32_t*)(sf_rows + roff[t] + blk);
+    gemm::pin_frag(bf[t][0]);
+    if (FMT != 4) gemm::pin_frag(bf[t][1]);
+    gemm::pin_word(sb[t]);
   }
 }
 
-// Shift right by 8 * (l/32) so that bytes 0 and 2 are the blocks this lane feeds to
-// steps 2q and 2q+1. Blocks at or past nblk (beyond K) read as 127 (2^0): the matching
-// operand bytes are zero, and a NaN scale code in the row padding must not poison them.
-template <int FMT>
-__device__ __forceinline__ void prep_scales(const uint32_t (&raw)[4][2], int64_t blk0, int64_t nblk, int lane,
-                                            uint32_t (&out)[4][2]) {
-  const int sh = 8 * (lane >> 5);
+// MFMAs of accumulator rows mt in [MT0, MT1) for one 64-K step.
+template <int FMT, int SEL, int MT0, int MT1>
+__device__ __forceinline__ void mfma_rows(const uint4 (&af)[4][2], const uint4 (&bf)[4][2], const uint32_t (&sa)[4],
+                                          const uint32_t (&sb)[4], f32x16 (&acc)[4][4]) {
 #pragma unroll
-  for (int q = 0; q < Fmt<FMT>::SFW; q++) {
-    const int64_t valid = nblk - blk0 - 4 * q;
-    const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : (1u << (8 * valid)) - 1u);
+  for (int mt = MT0; mt < MT1; mt++)
 #pragma unroll
-    for (int t = 0; t < 4; t++) out[t][q] = ((raw[t][q] & keep) | (0x7F7F7F7Fu & ~keep)) >> sh;
-  }
+    for (int nt = 0; nt < 4; nt++) acc[mt][nt] = mfma_sc<FMT, SEL>(bf[nt], af[mt], acc[mt][nt], sb[nt], sa[mt]);
+}
+
+// One fp8 K tile kt from register set X (fragments + shifted scales of tile kt) while
+// set Y receives tile kt + 1.
+__device__ __forceinline__ void fp8_tile(const Ops& o, int kt, int nfull, const uint8_t* lds, uint32_t lds0, int w,
+                                         int lane, int wa, int wb, const uint32_t (&base)[2], Set<0>& X, Set<0>& Y,
+                                         f32x16 (&acc)[4][4]) {
+  issue_stage<0>(o, min(kt + PF, nfull - 1), lds0 + ((kt + PF) % NST) * STAGE_BYTES, w);
+  pin_set<0, 0, 2>(X.af, X.bf, X.sa, X.sb);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_rows<0, 0, 0, 2>(X.af, X.bf, X.sa, X.sb, acc);
+  gemm::pin_acc(acc);
+  __builtin_amdgcn_sched_barrier(0);
+  gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
+  const uint8_t* nst = lds + ((kt + 1) % NST) * STAGE_BYTES;
+  read_frags<0>(nst, 0, wa, wb, base, Y.af, Y.bf);
+  read_scales(nst, wa, wb, lane, Y.sa, Y.sb);
+  pin_set<0, 2, 4>(X.af, X.bf, X.sa, X.sb);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_rows<0, 0, 2, 4>(X.af, X.bf, X.sa, X.sb, acc);
+  gemm::pin_acc(acc);
+  __builtin_amdgcn_sched_barrier(0);
+  shift_scales(Y.sa, Y.sb, 8 * (lane >> 5) + 16 * ((kt + 1) & 1));
 }
 
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int tiles_n) {
   typedef Fmt<FMT> F;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
   gemm::tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const uint8_t* A = (const uint8_t*)a.A;
-  const uint8_t* B = (const uint8_t*)a.B;
-  const int64_t lda_b = a.lda / F::EPB, ldb_b = a.ldb / F::EPB;
   const int64_t nblk = a.K / 32;
   const int wa = 128 * wm, wb = 128 * wn;
 
@@ -195,91 +212,109 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
 
-  uint32_t aoff[8], boff[8], abase[4], bbase[4], sfa_off[4], sfb_off[4];
-  dma_offsets(lda_b, m0, a.M, w, lane, aoff);
-  dma_offsets(ldb_b, n0, a.N, w, lane, boff);
-  frag_bases<FMT>(lane, abase);
-  frag_bases<FMT>(lane, bbase);
-  // scale rows of this lane: wave base + 32t + l%32, clamped to the last row, as byte
-  // offsets from the tile's first row (never negative: the tile's first row exists)
-  const uint8_t* sfa0 = a.SFA + m0 * a.ld_sfa;
-  const uint8_t* sfb0 = a.SFB + n0 * a.ld_sfb;
-#pragma unroll
-  for (int t = 0; t < 4; t++) {
-    sfa_off[t] = (uint32_t)((min(m0 + wa + 32 * t + (lane & 31), a.M - 1) - m0) * a.ld_sfa);
-    sfb_off[t] = (uint32_t)((min(n0 + wb + 32 * t + (lane & 31), a.N - 1) - n0) * a.ld_sfb);
-  }
-  const int bpt = F::KT / 32;  // scale blocks per K tile
+  Ops o;
+  o.lda_b = a.lda / F::EPB;
+  o.ldb_b = a.ldb / F::EPB;
+  o.A = (const uint8_t*)a.A + m0 * o.lda_b;
+  o.B = (const uint8_t*)a.B + n0 * o.ldb_b;
+  o.SFA = a.SFA + m0 * a.ld_sfa;
+  o.SFB = a.SFB + n0 * a.ld_sfb;
+  o.ld_sfa = a.ld_sfa;
+  o.ld_sfb = a.ld_sfb;
+  gemm::kmajor_dma_offsets(o.lda_b, m0, a.M, w, lane, o.aoff);
+  gemm::kmajor_dma_offsets(o.ldb_b, n0, a.N, w, lane, o.boff);
+  // scale row 64w + l of the tile (clamped to the last row), relative to the first row
+  o.sfa_off = (uint32_t)((min(m0 + 64 * w + lane, a.M - 1) - m0) * a.ld_sfa);
+  o.sfb_off = (uint32_t)((min(n0 + 64 * w + lane, a.N - 1) - n0) * a.ld_sfb);
+  uint32_t base[2];
+  frag_bases(lane, base);
 
   const int nfull = (int)(a.K / F::KT);
   const int tail = (int)(a.K % F::KT);
   const uint32_t lds0 = gemm::lds_addr(lds);
-  uint4 af[2][4][2], bf[2][4][2];
-  uint32_t sa[4][2], sb[4][2], na[4][2], nb[4][2];
-  load_scales<FMT>(sfa0, sfa_off, 0, nblk, na);
-  load_scales<FMT>(sfb0, sfb_off, 0, nblk, nb);
-  prep_scales<FMT>(na, 0, nblk, lane, sa);
-  prep_scales<FMT>(nb, 0, nblk, lane, sb);
+  const int h8 = 8 * (lane >> 5);
+  Set<FMT> X, Y;
   if (nfull > 0) {
-    issue_tile(A + m0 * lda_b, aoff, lds0, w);
-    issue_tile(B + n0 * ldb_b, boff, lds0 + TILE_BYTES, w);
-    gemm::wait_dma();
-    __syncthreads();
-    read_step<FMT>(lds, lds + TILE_BYTES, 0, wa, wb, abase, bbase, af[0], bf[0]);
-  }
-  // The loop body is branch-free so that the scheduling fences hold: on the last K tile
-  // the prefetch re-reads the last tile (clamped index) into the stage nobody reads again.
-  for (int kt = 0; kt < nfull; kt++) {
-    const int cur = kt & 1;
-    const uint8_t* ta = lds + cur * STAGE_BYTES;
-    const uint8_t* tb = ta + TILE_BYTES;
-    const uint8_t* nta = lds + (cur ^ 1) * STAGE_BYTES;
-    const int kn = min(kt + 1, nfull - 1);
-    read_step<FMT>(ta, tb, 1, wa, wb, abase, bbase, af[1], bf[1]);
-    {
-      const uint32_t nxt = lds0 + (cur ^ 1) * STAGE_BYTES;
-      const int64_t kb1 = (int64_t)kn * ROWB;
-      issue_tile(A + m0 * lda_b + kb1, aoff, nxt, w);
-      issue_tile(B + n0 * ldb_b + kb1, boff, nxt + TILE_BYTES, w);
-    }
-    // scales of K tile kt+1 (it exists when kt+1 < nfull or a partial tile follows)
-    const int64_t blk1 = (kt + 1 < nfull || tail) ? (int64_t)(kt + 1) * bpt : (int64_t)kt * bpt;
-    load_scales<FMT>(sfa0, sfa_off, blk1, nblk, na);
-    load_scales<FMT>(sfb0, sfb_off, blk1, nblk, nb);
 #pragma unroll
-    for (int s = 0; s < F::STEPS; s++) {
+    for (int p = 0; p < PF; p++) issue_stage<FMT>(o, min(p, nfull - 1), lds0 + p * STAGE_BYTES, w);
+    gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
+    read_frags<FMT>(lds, 0, wa, wb, base, X.af, X.bf);
+    read_scales(lds, wa, wb, lane, X.sa, X.sb);
+    shift_scales(X.sa, X.sb, h8);
+  }
+  if constexpr (FMT == 4) {
+    // Iteration kt: read step 1 of tile kt, start the copy of tile kt + PF into the
+    // stage tile kt - 1 used, MFMAs of step 0, barrier (tile kt + 1 landed), read step 0
+    // and the scales of tile kt + 1, MFMAs of step 1, then shift the new scales.
+    // Branch-free: past the last tile the copies re-read it into unused stages.
+    for (int kt = 0; kt < nfull; kt++) {
+      const uint8_t* st = lds + (kt % NST) * STAGE_BYTES;
+      const uint8_t* nst = lds + ((kt + 1) % NST) * STAGE_BYTES;
+      read_frags<4>(st, 1, wa, wb, base, Y.af, Y.bf);
+      issue_stage<4>(o, min(kt + PF, nfull - 1), lds0 + ((kt + PF) % NST) * STAGE_BYTES, w);
+      pin_set<4, 0, 4>(X.af, X.bf, X.sa, X.sb);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step<FMT>(af[s & 1], bf[s & 1], s, sa, sb, acc);
+      mfma_rows<4, 0, 0, 4>(X.af, X.bf, X.sa, X.sb, acc);
+      gemm::pin_acc(acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 2 < F::STEPS) {
-        read_step<FMT>(ta, tb, s + 2, wa, wb, abase, bbase, af[s & 1], bf[s & 1]);
-      } else if (s + 2 == F::STEPS) {
-        gemm::wait_dma();
-        __syncthreads();
-        read_step<FMT>(nta, nta + TILE_BYTES, 0, wa, wb, abase, bbase, af[s & 1], bf[s & 1]);
+      gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
+      read_frags<4>(nst, 0, wa, wb, base, X.af, X.bf);
+      read_scales(nst, wa, wb, lane, Y.sa, Y.sb);
+      pin_set<4, 0, 4>(Y.af, Y.bf, X.sa, X.sb);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_rows<4, 2, 0, 4>(Y.af, Y.bf, X.sa, X.sb, acc);
+      gemm::pin_acc(acc);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        X.sa[t] = Y.sa[t] >> h8;
+        X.sb[t] = Y.sb[t] >> h8;
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    prep_scales<FMT>(na, blk1, nblk, lane, sa);
-    prep_scales<FMT>(nb, blk1, nblk, lane, sb);
+  } else {
+    // Two register sets alternate between consecutive K tiles.
+    int kt = 0;
+    for (; kt + 2 <= nfull; kt += 2) {
+      fp8_tile(o, kt, nfull, lds, lds0, w, lane, wa, wb, base, X, Y, acc);
+      fp8_tile(o, kt + 1, nfull, lds, lds0, w, lane, wa, wb, base, Y, X, acc);
+    }
+    if (kt < nfull) {
+      fp8_tile(o, kt, nfull, lds, lds0, w, lane, wa, wb, base, X, Y, acc);
+    }
   }
+  // Every copy has landed and every wave is done with LDS before stage 0 is refilled
+  // (and before the workgroup can end with copies in flight).
+  gemm::stage_barrier<0>();
   if (tail) {
-    uint8_t* st = lds + (nfull & 1) * STAGE_BYTES;
     const int64_t kb0 = (int64_t)nfull * ROWB;
     const int64_t kb_end = a.K / F::EPB;
-    fill_tile_masked(A, lda_b, m0, a.M, kb0, kb_end, st, w, lane);
-    fill_tile_masked(B, ldb_b, n0, a.N, kb0, kb_end, st + TILE_BYTES, w, lane);
+    gemm::kmajor_fill_masked((const uint8_t*)a.A, o.lda_b, m0, a.M, kb0, kb_end, lds, w, lane);
+    gemm::kmajor_fill_masked((const uint8_t*)a.B, o.ldb_b, n0, a.N, kb0, kb_end, lds + TILE_BYTES, w, lane);
+    {
+      // scale words of the partial tile; blocks at or past nblk (beyond K) become 127
+      // (2^0): their operand bytes are zero, and a NaN code in the row padding must not
+      // poison them
+      const int64_t word = sf_word<FMT>(nfull);
+      const int64_t valid = nblk - word;  // >= 1: the partial tile's first block exists
+      const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : (1u << (8 * valid)) - 1u;
+      const uint32_t ra = *(const uint32_t*)(o.SFA + o.sfa_off + word);
+      const uint32_t rb = *(const uint32_t*)(o.SFB + o.sfb_off + word);
+      *(BSM_LDS uint32_t*)(lds + 2 * TILE_BYTES + 256 * w + 4 * lane) = (ra & keep) | (0x7F7F7F7Fu & ~keep);
+      *(BSM_LDS uint32_t*)(lds + 2 * TILE_BYTES + SF_BYTES + 256 * w + 4 * lane) = (rb & keep) | (0x7F7F7F7Fu & ~keep);
+    }
     __syncthreads();
+    // 64-K steps of the partial tile (fp4: one or two); the second one takes its scale
+    // bytes from a 16-bit further shift, so every step uses op_sel 0. A counted loop keeps
+    // the accumulators in place across the optional work.
     const int steps = (tail + 63) / 64;
-#pragma unroll
-    for (int s = 0; s < F::STEPS; s++) {
-      if (s < steps) {
-        read_step<FMT>(st, st + TILE_BYTES, s, wa, wb, abase, bbase, af[0], bf[0]);
-        mfma_step<FMT>(af[0], bf[0], s, sa, sb, acc);
-      }
+    for (int s = 0; s < steps; s++) {
+      read_scales(lds, wa, wb, lane, X.sa, X.sb);
+      shift_scales(X.sa, X.sb, FMT == 4 ? h8 + 16 * s : h8 + 16 * (nfull & 1));
+      read_frags<FMT>(lds, s, wa, wb, base, X.af, X.bf);
+      mfma_rows<FMT, 0, 0, 4>(X.af, X.bf, X.sa, X.sb, acc);
     }
   }
-  gemm::store_tile(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
+  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
 }
 
 }  // namespace

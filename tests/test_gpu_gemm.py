@@ -116,7 +116,7 @@ def test_gemm_f16_128_workload(O):
 
 
 SHAPES = [(1, 1, 1), (7, 9, 5), (17, 33, 9), (64, 64, 64), (255, 257, 130), (300, 520, 200), (513, 130, 64),
-          (96, 272, 1000)]
+          (96, 272, 1000), (33, 40, 31), (40, 33, 33), (64, 64, 96), (256, 256, 33), (64, 72, 128)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
@@ -261,7 +261,7 @@ def mx_case(fmt, seed, M, N, K, exp_range=4, ld_pad=0):
 
 
 MX_SHAPES = [(1, 1, 32), (9, 17, 64), (33, 40, 96), (256, 256, 128), (300, 260, 288), (130, 513, 512),
-             (64, 96, 1056)]
+             (64, 96, 1056), (64, 64, 160), (64, 64, 224), (40, 40, 192)]
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])

@@ -55,7 +55,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
 
 // Operand-tile geometry of the dense GEMM (rows x K elements per LDS stage).
 constexpr int kDenseTileRows = 256;
-constexpr int kDenseTileK = 32;
+constexpr int kDenseTileK = 64;
 hipError_t launch_debug_fragments(const uint16_t* src, int kmajor, uint16_t* dump, hipStream_t st);
 
 }  // namespace bsm

@@ -86,31 +86,38 @@ __device__ __forceinline__ void pin_frag(uint4& x) {
 }
 __device__ __forceinline__ void pin_word(uint32_t& x) { asm volatile("" : "+v"(x)::"memory"); }
 
-// ---- K-major operand tiles: 256 rows x 64 bytes of K, 16 KiB per tile -------------
-// The 16-byte chunk c of LDS row r is stored at physical chunk c ^ ((r >> 2) & 3): the
-// 16 rows that one 16-lane group of a 16-byte LDS read touches then cover all 64 banks
-// (4 rows per 256-byte bank window, 4 distinct chunks per row position).
-constexpr int kKRowBytes = 64;
+// Joins the workgroup barrier once this wave's LDS operations are done (its vector-memory
+// copies may still be in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---- K-major operand tiles: 256 rows x 128 bytes of K, 32 KiB per tile -------------
+// Whole 128-byte cache lines per row: the copy path sustains far more bandwidth with
+// full-line requests than with half lines. The 16-byte chunk c of LDS row r is stored
+// at physical chunk c ^ ((r >> 1) & 7): the 16 rows that one 16-lane group of a 16-byte
+// LDS read touches then cover all 64 banks (2 rows per 256-byte bank window, 8 distinct
+// chunks per row parity).
+constexpr int kKRowBytes = 128;
 constexpr int kKTileBytes = 256 * kKRowBytes;
 
 // Per-lane offsets (bytes, relative to the tile's first row at the tile's first K byte)
-// of the 4 direct LDS copies a wave issues per tile. Copy j of wave w fills LDS bytes
-// [1024 (w + 4j), +1024), i.e. rows 16 (w + 4j) .. +15: lane l writes row
-// 16 (w + 4j) + l/4, physical chunk l%4, which holds logical chunk (l%4) ^ (l/16).
-// Rows past the operand's last row re-read the last row (their results are not stored).
+// of the 8 direct LDS copies a wave issues per tile. Copy j of wave w fills LDS bytes
+// [1024 (w + 4j), +1024), i.e. rows 8 (w + 4j) .. +7: lane l writes row 8 (w + 4j) + l/8,
+// physical chunk l%8, which holds logical chunk (l%8) ^ ((row >> 1) & 7). Rows past the
+// operand's last row re-read the last row (their results are not stored).
 __device__ __forceinline__ void kmajor_dma_offsets(int64_t ld_bytes, int64_t row0, int64_t rows, int w, int lane,
-                                                   uint32_t (&off)[4]) {
-  const int c = (lane & 3) ^ (lane >> 4);
+                                                   uint32_t (&off)[8]) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int64_t rg = min(row0 + 16 * (w + 4 * j) + (lane >> 2), rows - 1);
+  for (int j = 0; j < 8; j++) {
+    const int r = 8 * (w + 4 * j) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int64_t rg = min(row0 + r, rows - 1);
     off[j] = (uint32_t)((rg - row0) * ld_bytes + 16 * c);
   }
 }
 
-__device__ __forceinline__ void issue_tile4(const void* base, const uint32_t (&off)[4], uint32_t lds_tile, int w) {
+__device__ __forceinline__ void issue_tile8(const void* base, const uint32_t (&off)[8], uint32_t lds_tile, int w) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) dma16s(base, off[j], lds_tile + 1024 * (w + 4 * j));
+  for (int j = 0; j < 8; j++) dma16s(base, off[j], lds_tile + 1024 * (w + 4 * j));
 }
 
 // Byte offset inside a K-major tile of logical chunk `chunk` of the row that lane l
@@ -118,7 +125,7 @@ __device__ __forceinline__ void issue_tile4(const void* base, const uint32_t (&o
 // so they add to this without changing the swizzle).
 __device__ __forceinline__ uint32_t kmajor_frag_base(int lane, int chunk) {
   const int r = lane & 31;
-  return (uint32_t)(r * kKRowBytes + ((chunk ^ ((r >> 2) & 3)) << 4));
+  return (uint32_t)(r * kKRowBytes + ((chunk ^ ((r >> 1) & 7)) << 4));
 }
 
 // The same tile for a partial last K tile, through registers: bytes at or past kb_end
@@ -126,11 +133,12 @@ __device__ __forceinline__ uint32_t kmajor_frag_base(int lane, int chunk) {
 __device__ __forceinline__ void kmajor_fill_masked(const uint8_t* __restrict__ p, int64_t ld_bytes, int64_t row0,
                                                    int64_t rows, int64_t kb0, int64_t kb_end, uint8_t* tile,
                                                    int w, int lane) {
-  const int c = (lane & 3) ^ (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
+  for (int j = 0; j < 8; j++) {
     const int i = w + 4 * j;
-    const int64_t rg = min(row0 + 16 * i + (lane >> 2), rows - 1);
+    const int r = 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int64_t rg = min(row0 + r, rows - 1);
     const int64_t kb = kb0 + 16 * c;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (kb < kb_end) {

@@ -6,24 +6,24 @@
 // first K step starts from D when accumulating and from zero otherwise.
 //
 // gfx950 design:
-//  - workgroup tile 256 x 256, K tile 32, four wave64s in a 2 x 2 grid, each owning a
+//  - workgroup tile 256 x 256, K tile 64, four wave64s in a 2 x 2 grid, each owning a
 //    128 x 128 sub-tile as 4 x 4 v_mfma_f32_32x32x16 accumulators (256 fp32 per lane,
 //    held in AGPRs). The MFMA is issued with the operands swapped (B fragment first), so
 //    a lane ends up holding four consecutive output columns per register group and the
 //    epilogue moves D in 16-byte pieces;
 //  - operand tiles stream HBM -> LDS with global_load_lds_dwordx4 (no register
-//    staging): an SGPR tile base plus per-lane 32-bit offsets that stay fixed over the
-//    whole K loop; four LDS stages (4 x 32 KiB) with K tile kt+3 in flight while tile kt
-//    is consumed, and one barrier per K tile that waits only for tile kt+1;
-//  - K-major tiles: 64-byte rows, 16-byte chunk c of row r stored at chunk
-//    c ^ ((r >> 2) & 3), so the 16 rows one 16-lane group reads with ds_read_b128
+//    staging) in whole 128-byte lines: an SGPR tile base plus per-lane 32-bit offsets
+//    that stay fixed over the whole K loop; two LDS stages of 64 KiB;
+//  - each wave reads all four K steps of a tile's fragments into registers early, so a
+//    stage is released after the first K step and the copy of tile kt+2 starts while
+//    tile kt is still being multiplied: two K tiles stay in flight;
+//  - K-major tiles: 128-byte rows, 16-byte chunk c of row r stored at chunk
+//    c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group reads with ds_read_b128
 //    cover all 64 LDS banks;
 //  - MN-major tiles (the transposed storage): 512-byte k-rows, chunk c of k-row kr
 //    stored at c ^ (4 * (kr & 3)); fragments come from ds_read_b64_tr_b16, the LDS
 //    transpose read (the analog of ldmatrix .trans in "ldmatrix / stmatrix",
 //    Transpose and stores), whose 32-lane groups again cover all banks;
-//  - software pipeline: the 16 MFMAs of one K step overlap the LDS reads of the other
-//    step; the stage barrier sits between the two steps of a K tile;
 //  - M/N edges clamp the rows that are loaded and mask the stores; a ragged last K
 //    tile is loaded through registers with the elements past K zeroed.
 #include "gemm_common.hpp"
@@ -32,24 +32,22 @@
 namespace bsm {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int TILE_BYTES = 256 * BK * 2;  // one operand tile: 16 KiB
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int TILE_BYTES = 256 * BK * 2;  // one operand tile: 32 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr int NST = 4;                    // LDS stages
-constexpr int PF = NST - 1;               // K tiles in flight ahead of the one consumed
-constexpr int DMA_PER_TILE = 8;           // copies per wave per K tile (4 A + 4 B)
+constexpr int DMA_PER_TILE = 16;          // copies per wave per K tile (8 A + 8 B)
 static_assert(TILE_BYTES == gemm::kKTileBytes, "K-major tile geometry");
 
-// Per-lane byte offsets (relative to the tile's global base) of the 4 direct LDS copies
+// Per-lane byte offsets (relative to the tile's global base) of the 8 direct LDS copies
 // a wave issues for one operand tile; copy j of wave w fills LDS bytes
 // [1024 (w + 4j), +1024).
-//  K-major: the shared 64-byte-row layout (gemm::kmajor_dma_offsets);
+//  K-major: the shared 128-byte-row layout (gemm::kmajor_dma_offsets);
 //  MN-major: LDS k-row kr = 2(w+4j) + l/32 holds global k-row k0 + kr, its physical
 //           chunk l%32 holds logical chunk (l%32) ^ (4 (kr & 3)) (columns clamped to
 //           the last 8-aligned chunk).
 template <bool KMAJ>
 __device__ __forceinline__ void dma_offsets(int64_t ld, int64_t row0, int64_t rows, int w, int lane,
-                                            uint32_t (&off)[4]) {
+                                            uint32_t (&off)[8]) {
   if (KMAJ) {
     gemm::kmajor_dma_offsets(2 * ld, row0, rows, w, lane, off);
   } else {
@@ -57,7 +55,7 @@ __device__ __forceinline__ void dma_offsets(int64_t ld, int64_t row0, int64_t ro
     const int c = (lane & 31) ^ ((kr0 & 3) << 2);
     const int64_t col = min(row0 + 8 * c, (rows - 1) & ~int64_t(7));
 #pragma unroll
-    for (int j = 0; j < 4; j++) off[j] = (uint32_t)(((kr0 + 8 * j) * ld + (col - row0)) * 2);
+    for (int j = 0; j < 8; j++) off[j] = (uint32_t)(((kr0 + 8 * j) * ld + (col - row0)) * 2);
   }
 }
 
@@ -76,7 +74,7 @@ __device__ __forceinline__ void fill_tile_masked(const uint16_t* __restrict__ p,
     return;
   }
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
+  for (int j = 0; j < 8; j++) {
     const int i = w + 4 * j;
     const int kr = 2 * i + (lane >> 5);
     const int c = (lane & 31) ^ ((kr & 3) << 2);
@@ -96,7 +94,7 @@ struct Frag<BSM_F16> { typedef f16x8 T; };
 
 // LDS read addresses of the v_mfma_f32_32x32x16 operand fragments. Lane l must hold
 // operand (row wbase + 32t + l%32, k 16ks + 8(l/32) + e), e = 0..7.
-//  K-major: one ds_read_b128 at 64 wbase + 2048t + base[ks] (logical chunk 2ks + l/32);
+//  K-major: one ds_read_b128 at 128 wbase + 4096t + base[ks] (logical chunk 2ks + l/32);
 //  MN-major: two ds_read_b64_tr_b16 (h = 0, 1) at 2 wbase + base[t] + 8192ks + 2048h,
 //   where within each 16-lane group (i = l%16, G = l/16) lane i provides k-row
 //   16ks + 8(G/2) + 4h + i/4 and columns 16(G%2) + 4(i%4)..+3, and receives the
@@ -106,8 +104,7 @@ template <bool KMAJ>
 __device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[4]) {
   if (KMAJ) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) base[ks] = gemm::kmajor_frag_base(lane, 2 * ks + (lane >> 5));
-    base[2] = base[3] = 0;
+    for (int ks = 0; ks < 4; ks++) base[ks] = gemm::kmajor_frag_base(lane, 2 * ks + (lane >> 5));
   } else {
     const int i = lane & 15, G = lane >> 4;
     const uint32_t L = (uint32_t)((8 * (G >> 1) + (i >> 2)) * 512 + 16 * (2 * (G & 1) + ((i & 3) >> 1)) + 8 * (i & 1) +
@@ -120,7 +117,7 @@ __device__ __forceinline__ void frag_bases(int lane, uint32_t (&base)[4]) {
 template <bool KMAJ>
 __device__ __forceinline__ uint4 read_frag(const uint8_t* tile, int wbase, const uint32_t (&base)[4], int ks, int t) {
   if (KMAJ) {
-    return lds_read_b128(tile + wbase * 64 + 2048 * t + base[ks]);
+    return lds_read_b128(tile + wbase * 128 + 4096 * t + base[ks]);
   } else {
     const uint8_t* p = tile + 2 * wbase + base[t] + 8192 * ks;
     const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
@@ -168,16 +165,16 @@ __device__ __forceinline__ void pin_step(uint4 (&af)[4], uint4 (&bf)[4]) {
 
 template <bool AK, bool BKM>
 __device__ __forceinline__ void issue_stage(const uint16_t* A, int64_t lda, int64_t m0, const uint16_t* B,
-                                            int64_t ldb, int64_t n0, int kt, const uint32_t (&aoff)[4],
-                                            const uint32_t (&boff)[4], uint32_t stage, int w) {
+                                            int64_t ldb, int64_t n0, int kt, const uint32_t (&aoff)[8],
+                                            const uint32_t (&boff)[8], uint32_t stage, int w) {
   const int64_t k0 = (int64_t)kt * BK;
-  gemm::issue_tile4(tile_base<AK>(A, lda, m0, k0), aoff, stage, w);
-  gemm::issue_tile4(tile_base<BKM>(B, ldb, n0, k0), boff, stage + TILE_BYTES, w);
+  gemm::issue_tile8(tile_base<AK>(A, lda, m0, k0), aoff, stage, w);
+  gemm::issue_tile8(tile_base<BKM>(B, ldb, n0, k0), boff, stage + TILE_BYTES, w);
 }
 
 template <int DT, bool AK, bool BKM>
 __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
@@ -194,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
 
-  uint32_t aoff[4], boff[4], abase[4], bbase[4];
+  uint32_t aoff[8], boff[8], abase[4], bbase[4];
   dma_offsets<AK>(a.lda, m0, a.M, w, lane, aoff);
   dma_offsets<BKM>(a.ldb, n0, a.N, w, lane, boff);
   frag_bases<AK>(lane, abase);
@@ -204,37 +201,46 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
   const int nfull = (int)(a.K / BK);
   const int tail = (int)(a.K % BK);
   const uint32_t lds0 = gemm::lds_addr(lds);
-  uint4 a0[4], b0[4], a1[4], b1[4];
+  // fragments of the four K steps of the current tile
+  uint4 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4], a3[4], b3[4];
   if (nfull > 0) {
-#pragma unroll
-    for (int p = 0; p < PF; p++)
-      issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(p, nfull - 1), aoff, boff, lds0 + p * STAGE_BYTES, w);
-    gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
+    issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, 0, aoff, boff, lds0, w);
+    issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(1, nfull - 1), aoff, boff, lds0 + STAGE_BYTES, w);
+    gemm::stage_barrier<DMA_PER_TILE>();
     read_step<AK, BKM>(lds, lds + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
   }
-  // K tile kt lives in stage kt % NST. Iteration kt: read step 1 of tile kt and start
-  // the copy of tile kt + PF into the stage that tile kt - 1 used (every wave finished
-  // reading it before the previous barrier); 16 MFMAs of step 0; barrier once this
-  // wave's copies of tile kt + 1 have landed (and its LDS reads are done); read step 0
-  // of tile kt + 1; 16 MFMAs of step 1. The body is branch-free so that the scheduling
-  // fences hold: past the last tile the copies re-read the last tile (clamped index)
-  // into stages nobody reads again.
+  // K tile kt lives in stage kt & 1. Iteration kt: read K steps 1..3 of tile kt; MFMAs of
+  // step 0; barrier once every wave's reads of the stage are done; start the copy of tile
+  // kt + 2 into it; MFMAs of steps 1 and 2; barrier once this wave's copies of tile kt + 1
+  // have landed; read step 0 of tile kt + 1; MFMAs of step 3. The body is branch-free so
+  // that the scheduling fences hold: past the last tile the copies re-read the last tile
+  // (clamped index) into a stage nobody reads again.
   for (int kt = 0; kt < nfull; kt++) {
-    const uint8_t* ta = lds + (kt % NST) * STAGE_BYTES;
-    const uint8_t* na = lds + ((kt + 1) % NST) * STAGE_BYTES;
+    const uint8_t* ta = lds + (kt & 1) * STAGE_BYTES;
+    const uint8_t* na = lds + ((kt + 1) & 1) * STAGE_BYTES;
     read_step<AK, BKM>(ta, ta + TILE_BYTES, 1, wa, wb, abase, bbase, a1, b1);
-    issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(kt + PF, nfull - 1), aoff, boff,
-                         lds0 + ((kt + PF) % NST) * STAGE_BYTES, w);
+    read_step<AK, BKM>(ta, ta + TILE_BYTES, 2, wa, wb, abase, bbase, a2, b2);
+    read_step<AK, BKM>(ta, ta + TILE_BYTES, 3, wa, wb, abase, bbase, a3, b3);
     pin_step(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step<DT>(a0, b0, acc);
     gemm::pin_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
-    gemm::stage_barrier<(PF - 1) * DMA_PER_TILE>();
-    read_step<AK, BKM>(na, na + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
+    gemm::lds_barrier();
+    issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(kt + 2, nfull - 1), aoff, boff,
+                         lds0 + (kt & 1) * STAGE_BYTES, w);
     pin_step(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step<DT>(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<DT>(a2, b2, acc);
+    gemm::pin_acc(acc);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm::stage_barrier<DMA_PER_TILE>();
+    read_step<AK, BKM>(na, na + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
+    pin_step(a3, b3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<DT>(a3, b3, acc);
     gemm::pin_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -276,9 +282,9 @@ template <bool KMAJ>
 __global__ __launch_bounds__(256) void k_debug_fragments(const uint16_t* __restrict__ src, uint16_t* dump) {
   __shared__ __attribute__((aligned(1024))) uint8_t tile[TILE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t off[4], base[4];
+  uint32_t off[8], base[4];
   dma_offsets<KMAJ>(KMAJ ? BK : BM, 0, BM, w, lane, off);
-  gemm::issue_tile4(src, off, gemm::lds_addr(tile), w);
+  gemm::issue_tile8(src, off, gemm::lds_addr(tile), w);
   gemm::stage_barrier<0>();
   frag_bases<KMAJ>(lane, base);
   for (int mb = 2 * w; mb < 2 * w + 2; mb++) {

@@ -11,6 +11,15 @@ resident in HBM, on one HIP stream:
 Prints one JSON line. `value` is the step's GEMM work (sum of 2*M*N*K of the three
 GEMMs) divided by the measured step time; every kernel's own rate and roofline
 fraction is in `per_kernel`, from HIP events on the launch stream.
+
+`roofline.traffic` is the dominant kernel's measured HBM bytes per launch, read from
+the committed counter summary profiles/hbm_traffic_bench_step.md (rocprofv3 FETCH_SIZE
+and WRITE_SIZE, calibrated against a plain copy of known size, see --copy-calibration);
+it is null when the kernel's sources no longer hash to the ones the counters were
+taken with.
+
+--copy-calibration runs only the calibration copy: the float32 add-scalar kernel over a
+1 GiB buffer (1 GiB read + 1 GiB written per launch), three launches.
 """
 from __future__ import annotations
 
@@ -24,6 +33,58 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"hbm_GBs": 8000.0, "bf16_TFs": 2516.6, "fp8_TFs": 5033.2, "fp4_TFs": 10066.3}
+
+# Source files each kernel is built from (their hash ties a counter summary to the code).
+_CSRC = os.path.join("block_scaled_matrix_amd", "csrc")
+KERNEL_SOURCES = {
+    "box_copy": ["k_tile.hip", "bsm_device.hpp"],
+    "gemm_bf16": ["k_gemm_dense.hip", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_mxfp8": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_mxfp4": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
+    "add_one": ["k_tile.hip", "bsm_device.hpp"],
+}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
+CALIB_BYTES = 1 << 30
+
+
+def source_hash(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, _CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, if it matches the code."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                # machine-readable rows: "traffic: <kernel> <bytes per launch> <source hash>"
+                parts = line.split()
+                if len(parts) == 4 and parts[0] == "traffic:" and parts[1] == kernel:
+                    return int(parts[2]) if parts[3] == source_hash(kernel) else None
+    except OSError:
+        return None
+    return None
+
+
+def copy_calibration():
+    import torch
+
+    import block_scaled_matrix_amd as bsm
+
+    n = CALIB_BYTES // 4
+    src = torch.zeros(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        bsm.bsm_tile_add_scalar_f32(src, dst, n, 1.0)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "add_scalar_f32", "bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
+                      "launches": 3}), flush=True)
 
 
 def log(*a):
@@ -104,7 +165,7 @@ def cpu_baseline():
     flops = 0.0
     t_gemm = 0.0
     g = W.gemm_bf16()
-    rows = 8
+    rows = 16
     t0 = time.perf_counter()
     O.gemm(g["M"], g["N"], g["K"], "bf16", g["A"], g["K"], "k", g["B"], g["N"], "n", g["D0"], g["N"], 0, 0, 1, 0, rows)
     t_gemm += time.perf_counter() - t0
@@ -113,16 +174,16 @@ def cpu_baseline():
     g = W.mxfp8()
     t0 = time.perf_counter()
     O.gemm_block_scale(g["M"], g["N"], g["K"], "e4m3", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e4m3", g["B"], g["K"],
-                       g["SFB"], g["ld_sfb"], None, 0, 0, 0, 0, 0, 2)
+                       g["SFB"], g["ld_sfb"], None, 0, 0, 0, 0, 0, 4)
     t_gemm += time.perf_counter() - t0
-    flops += 2.0 * 2 * g["N"] * g["K"]
+    flops += 2.0 * 4 * g["N"] * g["K"]
     del g
     g = W.mxfp4()
     t0 = time.perf_counter()
     O.gemm_block_scale(g["M"], g["N"], g["K"], "e2m1", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e2m1", g["B"], g["K"],
-                       g["SFB"], g["ld_sfb"], None, 0, 1, 0, 0, 0, 4)
+                       g["SFB"], g["ld_sfb"], None, 0, 1, 0, 0, 0, 8)
     t_gemm += time.perf_counter() - t0
-    flops += 2.0 * 4 * g["N"] * g["K"]
+    flops += 2.0 * 8 * g["N"] * g["K"]
     del g
     # box round trip on a 1024-row band of the copy workload (128 boxes wide)
     b = W.box_copy_bf16(rows=1024)
@@ -132,7 +193,7 @@ def cpu_baseline():
     t_box = time.perf_counter() - t0
     box_gbs = 4 * 1024 * b["cols"] * 2 / t_box / 1e9
     return {"value": flops / t_gemm / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"GEMM rows: bf16 8 of 8192, mxfp8 2 of 8192, mxfp4 4 of 16384 (full N and K), "
+            "sample": f"GEMM rows: bf16 16 of 8192, mxfp8 4 of 8192, mxfp4 8 of 16384 (full N and K), "
                       f"{t_gemm:.1f} s; box copy on a 1024x8190 band: {box_gbs:.3f} GB/s in {t_box:.1f} s",
             "box_copy_GBs": box_gbs}
 
@@ -143,6 +204,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the plain copy of known size used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); every workload here fits one MI355X and "
@@ -154,6 +217,9 @@ def main():
     import block_scaled_matrix_amd as bsm
     bsm.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     inp = make_inputs()
     ks = kernels(inp)
     stream = torch.cuda.current_stream()
@@ -212,7 +278,7 @@ def main():
                    "seeds": {"box_copy": 2, "gemm_bf16": 3, "mxfp8": 4, "mxfp4": 5}},
         "per_kernel": per,
         "roofline": {"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
-                     "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": None},
+                     "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dom)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -19,12 +19,14 @@ namespace bsm {
 // ------------------------------------------------------------------ add scalar
 // "Tile Operands and Execution", A Load, Compute, and Store Example: 64 lanes,
 // each with three 4-word loads, twelve scalar adds and three 4-word stores.
-// One wave64 covers a (2,32,3,4) float32 tile; lane t owns floats 12t..12t+11.
+// One wave64 covers a (2,32,3,4) float32 tile. Lane t owns the float4 groups at 4t,
+// 256 + 4t and 512 + 4t (rather than 12 consecutive floats), so that every 16-byte
+// access of the wave covers 1 KiB contiguous; the element-wise map is unchanged.
 __global__ __launch_bounds__(64) void k_add_scalar_f32(const float* __restrict__ src, float* dst, int64_t n, float s) {
-  const int64_t base = (int64_t)blockIdx.x * 768 + 12 * threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * 768 + 4 * threadIdx.x;
 #pragma unroll
   for (int r = 0; r < 3; r++) {
-    const int64_t i = base + 4 * r;
+    const int64_t i = base + 256 * r;
     if (i + 4 <= n) {
       float4 v = *(const float4*)(src + i);
       v.x += s; v.y += s; v.z += s; v.w += s;

@@ -7,9 +7,12 @@
 // compact row-major before a 16-byte-chunk XOR swizzle.
 //
 // Work mapping: one workgroup (256 lanes) per box; the image is cut into 16-byte
-// chunks (an image row is a whole number of them) and lane i moves chunks
-// i, i+256, ... . A chunk whose 16 global bytes are in range and 16-byte aligned
-// moves with one 128-bit access; any other chunk is assembled element by element.
+// chunks (an image row is a whole number of them). General boxes: lane i moves chunks
+// i, i+256, ...; a chunk whose 16 global bytes are in range and 16-byte aligned moves
+// with one 128-bit access, any other chunk element by element. Rank-2 boxes with unit
+// element strides (the common case, chosen on the host) use a dedicated kernel that
+// issues every HBM read of the workgroup before its first use, uses streaming accesses
+// and handles ragged edges without per-element loads.
 #include "bsm_device.hpp"
 #include "bsm_internal.hpp"
 #include "../../include/bsm.h"
@@ -97,24 +100,38 @@ __device__ __forceinline__ void store_elem(uint8_t* p, int esize, uint32_t v) {
   else *(uint32_t*)p = v;
 }
 
+// Word i of a 16-byte chunk, and its replacement, as register selects (no local arrays,
+// which the compiler would place in scratch memory once indexed at run time).
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ void set_word(uint4& v, int i, uint32_t x) {
+  v.x = i == 0 ? x : v.x;
+  v.y = i == 1 ? x : v.y;
+  v.z = i == 2 ? x : v.z;
+  v.w = i == 3 ? x : v.w;
+}
+__device__ __forceinline__ uint4 select4(bool c, const uint4& a, const uint4& b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 __device__ __forceinline__ uint32_t get_elem(const uint4& v, int esize, int e) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   const int bit = e * esize * 8;
-  const uint32_t word = w[bit >> 5];
+  const uint32_t word = word_of(v, bit >> 5);
   if (esize == 4) return word;
   const uint32_t mask = esize == 2 ? 0xFFFFu : 0xFFu;
   return (word >> (bit & 31)) & mask;
 }
 
 __device__ __forceinline__ void put_elem(uint4& v, int esize, int e, uint32_t x) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
   const int bit = e * esize * 8;
-  if (esize == 4) w[bit >> 5] = x;
-  else {
+  if (esize == 4) {
+    set_word(v, bit >> 5, x);
+  } else {
     const uint32_t mask = (esize == 2 ? 0xFFFFu : 0xFFu) << (bit & 31);
-    w[bit >> 5] = (w[bit >> 5] & ~mask) | ((x << (bit & 31)) & mask);
+    const uint32_t w = word_of(v, bit >> 5);
+    set_word(v, bit >> 5, (w & ~mask) | ((x << (bit & 31)) & mask));
   }
-  v = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Element-wise add of two elements of a float format, rounded once (RNE) to the format.
@@ -227,25 +244,37 @@ hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, 
   return hipGetLastError();
 }
 
+// Non-temporal 16-byte global accesses for data touched exactly once.
+__device__ __forceinline__ uint4 stream_load16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void stream_store16(uint8_t* p, uint4 x) {
+  const u32x4 v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, (u32x4*)p);
+}
+
 // ------------------------------------------------------------------ grid round trip
 struct CopyOut {
   int64_t dst_strides[5];
   int64_t add_strides[5];
+  uint32_t tiles[5];  // boxes per axis, ceil(dims / box)
 };
 
 // One workgroup per tile coordinate t*box: global -> swizzled LDS image -> dst / dst_add.
 __global__ __launch_bounds__(256) void k_box_copy(BoxGeom g, CopyOut o, const uint8_t* __restrict__ src,
                                                   uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_add) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t image[];
+  // Box coordinates: blockIdx unravelled over the per-axis tile counts, innermost fastest
+  // (the host guarantees fewer than 2^31 boxes, so 32-bit arithmetic suffices).
   int32_t c[5];
-  int64_t rem = blockIdx.x;
+  uint32_t rem = blockIdx.x;
 #pragma unroll
   for (int i = 4; i >= 0; i--) {
     c[i] = 0;
     if (i < g.rank) {
-      const int64_t tiles = (g.dims[i] + g.box[i] - 1) / g.box[i];
-      c[i] = (int32_t)((rem % tiles) * g.box[i]);
-      rem /= tiles;
+      c[i] = (int32_t)((rem % o.tiles[i]) * (uint32_t)g.box[i]);
+      rem /= o.tiles[i];
     }
   }
   const int cpr = g.row_bytes >> 4;
@@ -264,11 +293,111 @@ __global__ __launch_bounds__(256) void k_box_copy(BoxGeom g, CopyOut o, const ui
   }
 }
 
+
+// Rank-2 grid round trip with unit element strides, an image of at most 1024 16-byte chunks
+// with a power-of-two number of chunks per row, and rows of at least one whole chunk (the
+// host checks all of this): a small kernel with only the arguments this case needs.
+struct Copy2D {
+  const uint8_t* src; uint8_t* dst; uint8_t* add;
+  int64_t dims0, dims1;                 // rows, columns (elements)
+  int64_t s_src, s_dst, s_add;          // row strides (bytes)
+  uint32_t tiles1;                      // boxes per row of boxes
+  int32_t box0, box1;                   // box extents (rows, elements)
+  int32_t esize, dtype, swizzle, lg_cpr, row_bytes;
+  uint32_t fill_word;                   // the fill element replicated over 32 bits
+};
+
+// Lane l moves chunk column l % cpr of image rows l / cpr + k * (256 / cpr), k < 4. All
+// source and reduce-add chunks are fetched first with 128-bit streaming loads, so every HBM
+// read of the workgroup is in flight at once. A chunk that straddles the last column is
+// read whole as well (its 16 bytes lie inside the tensor's extent on every row but the
+// last) and its elements past the last column are replaced by the fill; on the tensor's
+// last row it is gathered element by element. Rows past the last row and chunks past the
+// last column take the fill. Whole chunks are stored with 128-bit streaming stores, the
+// straddling chunk element-wise (in-range elements only).
+template <bool ADD>
+__global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t image[];
+  const uint32_t t1 = blockIdx.x % a.tiles1, t0 = blockIdx.x / a.tiles1;
+  const int64_t c0 = (int64_t)t0 * a.box0, c1 = (int64_t)t1 * a.box1;
+  const int cpr = 1 << a.lg_cpr;
+  const int cc = threadIdx.x & (cpr - 1), r0 = threadIdx.x >> a.lg_cpr, rstep = 256 >> a.lg_cpr;
+  const int epc = 16 / a.esize;
+  const int64_t k0 = c1 + (int64_t)cc * epc;           // first element of the lane's chunk
+  const bool whole = k0 + epc <= a.dims1;              // chunk wholly in range
+  const bool part = !whole && k0 < a.dims1;            // chunk straddles the last column
+  const int64_t kc = whole || part ? k0 : ((a.dims1 / epc) - 1) * epc;  // a whole chunk stands in
+  const uint4 fill4 = make_uint4(a.fill_word, a.fill_word, a.fill_word, a.fill_word);
+  uint4 v[4], d[4];
+  bool rin[4], last[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int r = r0 + k * rstep;
+    const int64_t row = c0 + r;
+    rin[k] = r < a.box0 && row < a.dims0;
+    const int64_t rowc = min(row, a.dims0 - 1);          // rows past the end re-read the last row
+    last[k] = part && rowc == a.dims0 - 1;               // no 16-byte read past the tensor's end
+    const int64_t col = (last[k] ? ((a.dims1 / epc) - 1) * epc : kc) * a.esize;
+    v[k] = stream_load16(a.src + rowc * a.s_src + col);
+    if (ADD) d[k] = stream_load16(a.add + rowc * a.s_add + col);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    v[k] = select4(rin[k] && (whole || part), v[k], fill4);
+    if (part) {
+      for (int e = 0; e < epc; e++)
+        if (k0 + e >= a.dims1) put_elem(v[k], a.esize, e, a.fill_word);
+    }
+  }
+  if (__builtin_expect(part && a.dims0 - 1 < c0 + a.box0, 0)) {
+    // the straddling chunk of the tensor's last row, element by element
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      if (!rin[k] || !last[k]) continue;
+      const uint8_t* row = a.src + (c0 + r0 + k * rstep) * a.s_src;
+      for (int e = 0; e < epc; e++)
+        if (k0 + e < a.dims1) put_elem(v[k], a.esize, e, load_elem(row + (k0 + e) * a.esize, a.esize));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int r = r0 + k * rstep;
+    if (r < a.box0) lds_write_b128(image + image_swizzle((uint32_t)(r * a.row_bytes + cc * 16), a.swizzle), v[k]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int r = r0 + k * rstep;
+    const int64_t row = c0 + r;
+    if (!rin[k] || !(whole || part)) continue;
+    const uint4 x = lds_read_b128(image + image_swizzle((uint32_t)(r * a.row_bytes + cc * 16), a.swizzle));
+    if (__builtin_expect(whole, 1)) {
+      if (a.dst) stream_store16(a.dst + row * a.s_dst + k0 * a.esize, x);
+      if (ADD) stream_store16(a.add + row * a.s_add + k0 * a.esize, add_chunk(a.dtype, d[k], x));
+    } else {
+      const uint4 y = ADD ? add_chunk(a.dtype, d[k], x) : x;  // d[k] is valid unless on the last row
+      for (int e = 0; e < epc; e++) {
+        if (k0 + e >= a.dims1) continue;
+        if (a.dst) store_elem(a.dst + row * a.s_dst + (k0 + e) * a.esize, a.esize, get_elem(x, a.esize, e));
+        if (ADD) {
+          uint8_t* q = a.add + row * a.s_add + (k0 + e) * a.esize;
+          store_elem(q, a.esize,
+                     last[k] ? add_elem(a.dtype, load_elem(q, a.esize), get_elem(x, a.esize, e)) : get_elem(y, a.esize, e));
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const int64_t* dst_strides, void* dst_add,
                            const int64_t* add_strides, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_box_copy, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k_box_copy2d<true>, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k_box_copy2d<false>, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -278,10 +407,32 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
     o.add_strides[i] = add_strides ? add_strides[i] : 0;
   }
   int64_t tiles = 1;
-  for (int i = 0; i < g.rank; i++) tiles *= (g.dims[i] + g.box[i] - 1) / g.box[i];
+  for (int i = 0; i < g.rank; i++) {
+    const int64_t t = (g.dims[i] + g.box[i] - 1) / g.box[i];
+    o.tiles[i] = (uint32_t)t;
+    tiles *= t;
+  }
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   // LDS holds the whole swizzle period: a swizzled offset of the image can land past
   // image_bytes (up to image_stride).
+  const int cpr = g.row_bytes >> 4;
+  if (g.rank == 2 && g.estr[0] == 1 && g.nrows * cpr <= 1024 && (cpr & (cpr - 1)) == 0 && g.dims[1] * g.esize >= 16) {
+    Copy2D a;
+    a.src = (const uint8_t*)src; a.dst = (uint8_t*)dst; a.add = (uint8_t*)dst_add;
+    a.dims0 = g.dims[0]; a.dims1 = g.dims[1];
+    a.s_src = g.strides[0]; a.s_dst = o.dst_strides[0]; a.s_add = o.add_strides[0];
+    a.tiles1 = o.tiles[1];
+    a.box0 = g.box[0]; a.box1 = g.box[1];
+    a.esize = g.esize; a.dtype = g.dtype; a.swizzle = g.swizzle; a.row_bytes = g.row_bytes;
+    a.lg_cpr = 0;
+    while ((1 << a.lg_cpr) < cpr) a.lg_cpr++;
+    a.fill_word = g.esize == 1 ? g.fill_bits * 0x01010101u : (g.esize == 2 ? g.fill_bits * 0x00010001u : g.fill_bits);
+    if (dst_add)
+      hipLaunchKernelGGL(k_box_copy2d<true>, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, a);
+    else
+      hipLaunchKernelGGL(k_box_copy2d<false>, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_box_copy, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, g, o,
                      (const uint8_t*)src, (uint8_t*)dst, (uint8_t*)dst_add);
   return hipGetLastError();

@@ -146,7 +146,7 @@ def _copy_case(O, rows, cols, pitch, box, swz, seed):
 
 @pytest.mark.parametrize("rows,cols,pitch,box,swz", [
     (45, 70, 72, (16, 32), 2), (128, 64, 64, (128, 64), 3), (300, 190, 192, (128, 64), 3),
-    (257, 8190 // 8, 1024, (128, 64), 3), (33, 17, 24, (8, 8), 0)])
+    (257, 8190 // 8, 1024, (128, 64), 3), (33, 17, 24, (8, 8), 0), (9, 9, 16, (4, 8), 0), (130, 196, 200, (128, 64), 3)])
 def test_box_copy_grid_vs_oracle(O, rows, cols, pitch, box, swz):
     src, dst, add = _copy_case(O, rows, cols, pitch, box, swz, rows)
     say("box_copy", rows, cols, pitch, box, swz)

@@ -156,14 +156,62 @@ __device__ __forceinline__ void kmajor_fill_masked(const uint8_t* __restrict__ p
   }
 }
 
-// D = s * acc (+ D) for a 128 x 128 wave sub-tile held as 4 x 4 blocks of v_mfma 32x32
+// Accumulators start from s * D when accumulating; the epilogue then stores s * acc,
+// i.e. D + s * sum with the negation applied exactly twice. Lane layout as in
+// store_tile_t. Rows past M and columns past N start at zero (their addresses are
+// clamped into the tensor; they are never stored). Branch-free within each path so
+// that the accumulators are written once, in place.
+__device__ __forceinline__ void load_acc(const float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
+                                         int64_t col0, int lane, float sgn, f32x16 (&acc)[4][4]) {
+  const bool cols_whole = col0 + 128 <= N;  // wave-uniform
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    const int64_t row = row0 + 32 * mt + (lane & 31);
+    const float rs = row < M ? sgn : 0.0f;
+    const float* drow = D + min(row, M - 1) * ldd;
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int64_t col = col0 + 32 * nt + 8 * q + 4 * (lane >> 5);
+        float4 v;
+        if (cols_whole) {
+          v = *(const float4*)(drow + col);
+        } else {
+          v.x = col < N ? drow[min(col, N - 1)] : 0.0f;
+          v.y = col + 1 < N ? drow[min(col + 1, N - 1)] : 0.0f;
+          v.z = col + 2 < N ? drow[min(col + 2, N - 1)] : 0.0f;
+          v.w = col + 3 < N ? drow[min(col + 3, N - 1)] : 0.0f;
+        }
+        acc[mt][nt][4 * q] = rs * v.x;
+        acc[mt][nt][4 * q + 1] = rs * v.y;
+        acc[mt][nt][4 * q + 2] = rs * v.z;
+        acc[mt][nt][4 * q + 3] = rs * v.w;
+      }
+    }
+    // one 32-row block at a time: bounds the registers the loads occupy before they move
+    // into the accumulators
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) asm volatile("" : "+a"(acc[mt][nt])::"memory");
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
+}
+
+// D = s * acc for a 128 x 128 wave sub-tile held as 4 x 4 blocks of v_mfma 32x32
 // accumulators computed with the operands swapped (the MFMA row index runs over N):
 // register 4q + e of block (mt, nt) is output row 32mt + l%32, column
 // 32nt + 8q + 4(l/32) + e, so each group of four registers is 16 contiguous bytes of a
-// row of D and moves with one dwordx4 load / store (element-wise only at a ragged N).
+// row of D and moves with one dwordx4 store (element-wise only at a ragged N).
 __device__ __forceinline__ void store_tile_t(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
-                                             int64_t col0, int lane, float sgn, int accum,
-                                             const f32x16 (&acc)[4][4]) {
+                                             int64_t col0, int lane, float sgn, const f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
     const int64_t row = row0 + 32 * mt + (lane & 31);
@@ -174,20 +222,14 @@ __device__ __forceinline__ void store_tile_t(float* __restrict__ D, int64_t ldd,
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int64_t col = col0 + 32 * nt + 8 * q + 4 * (lane >> 5);
-        float4 v = make_float4(sgn * acc[mt][nt][4 * q], sgn * acc[mt][nt][4 * q + 1], sgn * acc[mt][nt][4 * q + 2],
-                               sgn * acc[mt][nt][4 * q + 3]);
+        const float4 v = make_float4(sgn * acc[mt][nt][4 * q], sgn * acc[mt][nt][4 * q + 1],
+                                     sgn * acc[mt][nt][4 * q + 2], sgn * acc[mt][nt][4 * q + 3]);
         if (col + 3 < N) {
-          float4* d = (float4*)(drow + col);
-          if (accum) {
-            const float4 o = *d;
-            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-          }
-          *d = v;
+          *(float4*)(drow + col) = v;
         } else {
-          const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 4; i++)
-            if (col + i < N) drow[col + i] = accum ? drow[col + i] + e[i] : e[i];
+          if (col < N) drow[col] = v.x;
+          if (col + 1 < N) drow[col + 1] = v.y;
+          if (col + 2 < N) drow[col + 2] = v.z;
         }
       }
     }

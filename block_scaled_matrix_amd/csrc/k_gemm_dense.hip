@@ -17,6 +17,8 @@
 //  - each wave reads all four K steps of a tile's fragments into registers early, so a
 //    stage is released after the first K step and the copy of tile kt+2 starts while
 //    tile kt is still being multiplied: two K tiles stay in flight;
+//  - LDS reads and copies are interleaved one by one with the MFMAs, so they issue while
+//    the matrix pipe is busy rather than in bursts that stall it;
 //  - K-major tiles: 128-byte rows, 16-byte chunk c of row r stored at chunk
 //    c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group reads with ds_read_b128
 //    cover all 64 LDS banks;
@@ -163,6 +165,24 @@ __device__ __forceinline__ void pin_step(uint4 (&af)[4], uint4 (&bf)[4]) {
   }
 }
 
+
+// One K step of 16 MFMAs with side work interleaved: side(i) runs after MFMA i, so that
+// LDS reads and copies issue while the matrix pipe is busy instead of in bursts. Empty asm
+// "rewrites" of each accumulator before and after its MFMA fix the order of the MFMAs and
+// the side operations (all volatile) without any hardware wait.
+template <int DT, typename Side>
+__device__ __forceinline__ void mfma_step_il(const uint4 (&af)[4], const uint4 (&bf)[4], f32x16 (&acc)[4][4],
+                                             Side side) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int mt = i >> 2, nt = i & 3;
+    asm volatile("" : "+a"(acc[mt][nt])::"memory");
+    acc[mt][nt] = mfma<DT>(bf[nt], af[mt], acc[mt][nt]);
+    asm volatile("" : "+a"(acc[mt][nt])::"memory");
+    side(i);
+  }
+}
+
 template <bool AK, bool BKM>
 __device__ __forceinline__ void issue_stage(const uint16_t* A, int64_t lda, int64_t m0, const uint16_t* B,
                                             int64_t ldb, int64_t n0, int kt, const uint32_t (&aoff)[8],
@@ -172,7 +192,7 @@ __device__ __forceinline__ void issue_stage(const uint16_t* A, int64_t lda, int6
   gemm::issue_tile8(tile_base<BKM>(B, ldb, n0, k0), boff, stage + TILE_BYTES, w);
 }
 
-template <int DT, bool AK, bool BKM>
+template <int DT, bool AK, bool BKM, bool ACC>
 __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,21 +202,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const uint16_t* A = (const uint16_t*)a.A;
   const uint16_t* B = (const uint16_t*)a.B;
+  const int wa = 128 * wm, wb = 128 * wn;
+  const float sgn = a.negate ? -1.0f : 1.0f;
 
+  // accumulators start from s * D (or zero); D is read here, before the operand copies
   f32x16 acc[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
+  if (ACC) gemm::load_acc(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
+  else gemm::zero_acc(acc);
 
   uint32_t aoff[8], boff[8], abase[4], bbase[4];
   dma_offsets<AK>(a.lda, m0, a.M, w, lane, aoff);
   dma_offsets<BKM>(a.ldb, n0, a.N, w, lane, boff);
   frag_bases<AK>(lane, abase);
   frag_bases<BKM>(lane, bbase);
-  const int wa = 128 * wm, wb = 128 * wn;
 
   const int nfull = (int)(a.K / BK);
   const int tail = (int)(a.K % BK);
@@ -209,40 +227,47 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
     gemm::stage_barrier<DMA_PER_TILE>();
     read_step<AK, BKM>(lds, lds + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
   }
-  // K tile kt lives in stage kt & 1. Iteration kt: read K steps 1..3 of tile kt; MFMAs of
-  // step 0; barrier once every wave's reads of the stage are done; start the copy of tile
-  // kt + 2 into it; MFMAs of steps 1 and 2; barrier once this wave's copies of tile kt + 1
-  // have landed; read step 0 of tile kt + 1; MFMAs of step 3. The body is branch-free so
-  // that the scheduling fences hold: past the last tile the copies re-read the last tile
-  // (clamped index) into a stage nobody reads again.
+  // K tile kt lives in stage kt & 1. Iteration kt: MFMAs of step 0 with the fragment reads
+  // of steps 1..3 spread over its first 12 MFMAs; barrier once every wave's reads of the
+  // stage are done; MFMAs of step 1 with the 16 copies of tile kt + 2 into the stage, one
+  // after each MFMA; MFMAs of step 2; barrier once this wave's copies of tile kt + 1 have
+  // landed; MFMAs of step 3 with the step-0 fragment reads of tile kt + 1. The body is
+  // branch-free: past the last tile the copies re-read the last tile (clamped index) into
+  // a stage nobody reads again.
   for (int kt = 0; kt < nfull; kt++) {
     const uint8_t* ta = lds + (kt & 1) * STAGE_BYTES;
+    const uint8_t* tb = ta + TILE_BYTES;
     const uint8_t* na = lds + ((kt + 1) & 1) * STAGE_BYTES;
-    read_step<AK, BKM>(ta, ta + TILE_BYTES, 1, wa, wb, abase, bbase, a1, b1);
-    read_step<AK, BKM>(ta, ta + TILE_BYTES, 2, wa, wb, abase, bbase, a2, b2);
-    read_step<AK, BKM>(ta, ta + TILE_BYTES, 3, wa, wb, abase, bbase, a3, b3);
+    const uint32_t stage = lds0 + (kt & 1) * STAGE_BYTES;
+    const int64_t k2 = (int64_t)min(kt + 2, nfull - 1) * BK;
+    const uint16_t* ga = tile_base<AK>(A, a.lda, m0, k2);
+    const uint16_t* gb = tile_base<BKM>(B, a.ldb, n0, k2);
     pin_step(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<DT>(a0, b0, acc);
-    gemm::pin_acc(acc);
-    __builtin_amdgcn_sched_barrier(0);
+    mfma_step_il<DT>(a0, b0, acc, [&](int i) {
+      if (i < 12) {
+#pragma unroll
+        for (int rr = 0; rr < 2; rr++) {
+          const int r = 2 * i + rr;  // read r: step 1 + r / 8, operand (r / 4) & 1, block r & 3
+          const int st = 1 + r / 8, op = (r / 4) & 1, t = r & 3;
+          uint4& dst = st == 1 ? (op ? b1[t] : a1[t]) : st == 2 ? (op ? b2[t] : a2[t]) : (op ? b3[t] : a3[t]);
+          dst = op ? read_frag<BKM>(tb, wb, bbase, st, t) : read_frag<AK>(ta, wa, abase, st, t);
+        }
+      }
+    });
     gemm::lds_barrier();
-    issue_stage<AK, BKM>(A, a.lda, m0, B, a.ldb, n0, min(kt + 2, nfull - 1), aoff, boff,
-                         lds0 + (kt & 1) * STAGE_BYTES, w);
     pin_step(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<DT>(a1, b1, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<DT>(a2, b2, acc);
-    gemm::pin_acc(acc);
-    __builtin_amdgcn_sched_barrier(0);
+    mfma_step_il<DT>(a1, b1, acc, [&](int i) {
+      if (i < 8) gemm::dma16s(ga, aoff[i], stage + 1024 * (w + 4 * i));
+      else gemm::dma16s(gb, boff[i - 8], stage + TILE_BYTES + 1024 * (w + 4 * (i - 8)));
+    });
+    pin_step(a2, b2);
+    mfma_step_il<DT>(a2, b2, acc, [&](int) {});
     gemm::stage_barrier<DMA_PER_TILE>();
-    read_step<AK, BKM>(na, na + TILE_BYTES, 0, wa, wb, abase, bbase, a0, b0);
     pin_step(a3, b3);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<DT>(a3, b3, acc);
-    gemm::pin_acc(acc);
-    __builtin_amdgcn_sched_barrier(0);
+    mfma_step_il<DT>(a3, b3, acc, [&](int i) {
+      if (i < 4) a0[i] = read_frag<AK>(na, wa, abase, 0, i);
+      else if (i < 8) b0[i - 4] = read_frag<BKM>(na + TILE_BYTES, wb, bbase, 0, i - 4);
+    });
   }
   // Every copy has landed and every wave is done with LDS before the stage is refilled
   // (and before the workgroup can end with copies in flight).
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
       mfma_step<DT>(a0, b0, acc);
     }
   }
-  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
+  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
 }
 
 template <int DT, bool AK, bool BKM>
@@ -265,7 +290,10 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = (int)tm64, tiles_n = (int)tn64;
-  hipLaunchKernelGGL((k_gemm_dense<DT, AK, BKM>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m, tiles_n);
+  if (a.accum)
+    hipLaunchKernelGGL((k_gemm_dense<DT, AK, BKM, true>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_dense<DT, AK, BKM, false>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -172,7 +172,7 @@ __device__ __forceinline__ void shift_scales(const uint32_t (&ra)[4][2], const u
     }
 }
 
-template <int FMT>
+template <int FMT, bool ACC>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int tiles_n) {
   typedef Fmt<FMT> F;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * F::STAGE];
@@ -183,14 +183,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nblk = a.K / 32;
   const int wa = 128 * wm, wb = 128 * wn;
+  const float sgn = a.negate ? -1.0f : 1.0f;
 
+  // accumulators start from s * D (or zero); D is read here, before the operand copies
   f32x16 acc[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
+  if (ACC) gemm::load_acc(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
+  else gemm::zero_acc(acc);
 
   Ops o;
   o.lda_b = a.lda / F::EPB;
@@ -326,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
       mfma_rows<FMT, 0, 0, 4>(f0, sa, sb, acc);
     }
   }
-  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, a.negate ? -1.0f : 1.0f, a.accum, acc);
+  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
 }
 
 }  // namespace
@@ -339,10 +337,14 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
   const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = (int)tm64, tiles_n = (int)tn64;
-  if (a.dtype == BSM_E2M1)
-    hipLaunchKernelGGL(k_gemm_mx<4>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL(k_gemm_mx<0>, dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m, tiles_n);
+  const dim3 grid(tiles_m * tiles_n);
+  if (a.dtype == BSM_E2M1) {
+    if (a.accum) hipLaunchKernelGGL((k_gemm_mx<4, true>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((k_gemm_mx<4, false>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
+  } else {
+    if (a.accum) hipLaunchKernelGGL((k_gemm_mx<0, true>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((k_gemm_mx<0, false>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
+  }
   return hipGetLastError();
 }
 

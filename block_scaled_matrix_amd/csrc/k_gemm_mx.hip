@@ -17,13 +17,19 @@
 //    holds four consecutive output columns per register group (16-byte epilogue);
 //  - workgroup tile 256 x 256 x (128 bytes of K per row), four wave64s with 128 x 128
 //    sub-tiles (4 x 4 accumulators of 16 fp32 in AGPRs); operand tiles (whole 128-byte
-//    lines per row, the 128-byte-row XOR swizzle shared with the dense kernel) and the
-//    scale words of each row stream HBM -> LDS with global_load_lds_dwordx4 / _dword
-//    into two stages;
+//    lines per row, the 128-byte-row XOR swizzle shared with the dense kernel) stream
+//    HBM -> LDS with global_load_lds_dwordx4 into two stages;
+//  - scale words reach LDS through a ring of two groups of 32 bytes per row (8 K tiles
+//    of fp8, 4 of fp4), copied a slice per K tile with 8 rows per 4-byte-per-lane copy:
+//    measured on the device, a copy whose 64 lanes touch 64 rows occupies the copy path
+//    four times as long as a 1 KiB operand copy, one touching 8 rows 0.6 times as long;
 //  - each wave reads a tile's fragments into registers early, so a stage is released
-//    after the first 64-K step and the copy of tile kt+2 starts while tile kt is still
-//    being multiplied: two K tiles stay in flight. fp8 tiles have two 64-K steps (the
-//    barrier for the next tile sits inside the second), fp4 tiles four.
+//    during the tile's first 64-K step and the copy of tile kt+2 starts while tile kt is
+//    still being multiplied: two K tiles stay in flight;
+//  - fragment reads, copies and barriers are placed one by one between the MFMAs: four
+//    wave bursts of copies would block the issuing waves behind the shared copy path
+//    while the matrix pipe idles, whereas one copy per 64-cycle fp8 MFMA (per two 32-cycle
+//    fp4 MFMAs) keeps it fed in the background.
 #include "gemm_common.hpp"
 #include "../../include/bsm.h"
 
@@ -33,7 +39,13 @@ namespace {
 constexpr int BM = 256, BN = 256;
 constexpr int ROWB = 128;                  // bytes of K per row per K tile
 constexpr int TILE_BYTES = 256 * ROWB;     // 32 KiB per operand tile
+constexpr int STAGE = 2 * TILE_BYTES;      // A tile, B tile
 static_assert(TILE_BYTES == gemm::kKTileBytes, "K-major tile geometry");
+// Scale ring: two group buffers (A, B) of 256 rows x 32 bytes after the two stages.
+constexpr int RING = 2 * STAGE;
+constexpr int RING_OP = 256 * 32;
+constexpr int RING_GROUP = 2 * RING_OP;
+constexpr int LDS_BYTES = RING + 2 * RING_GROUP;  // 160 KiB
 
 template <int FMT>
 struct Fmt {
@@ -41,33 +53,79 @@ struct Fmt {
   static constexpr int STEPS = FMT == 4 ? 4 : 2;   // 64-K MFMA steps per K tile
   static constexpr int EPB = FMT == 4 ? 2 : 1;     // elements per byte
   static constexpr int SFW = FMT == 4 ? 2 : 1;     // scale words per row per K tile
-  static constexpr int SF_BYTES = 256 * 4 * SFW;   // scale words of one operand tile
-  // stage: A tile, B tile, A scales, B scales (scale word q of row r at 1024 q + 4 r)
-  static constexpr int STAGE = 2 * TILE_BYTES + 2 * SF_BYTES;
-  static constexpr int DMA_PER_TILE = 16 + 2 * SFW;  // copies per wave per K tile
+  static constexpr int G = 8 / SFW;                // K tiles per scale group (32 bytes of a row)
+  static constexpr int SLICE_ROWS = 256 / G;       // rows of each operand's group copied per K tile
+  static constexpr int SLICE_COPIES = 2 * SLICE_ROWS / 8 / 4;  // per wave per K tile (8 rows a copy)
+  static constexpr int DMA_PER_TILE = 16 + SLICE_COPIES;
 };
 
 struct Ops {
-  const uint8_t* A; int64_t lda_b; uint32_t aoff[8];
-  const uint8_t* B; int64_t ldb_b; uint32_t boff[8];
-  const uint8_t* SFA; uint32_t sfa_off;
-  const uint8_t* SFB; uint32_t sfb_off;
+  const uint8_t* A; uint32_t aoff[8];
+  const uint8_t* B; uint32_t boff[8];
+  const uint8_t* SFA; uint32_t ld_sfa; int lim_a;  // lim: last valid tile row (<= 255)
+  const uint8_t* SFB; uint32_t ld_sfb; int lim_b;
+  int ldw;                                         // scale words per row that may be read
 };
 
-// Copies of K tile kt: operand rows from the tile's first row; scale word q of rows
-// 64w + l (each wave one 64-row quarter) into LDS word-major order.
+// Copy d of the 16 operand copies of one K tile (8 of A, then 8 of B) into `stage`.
+__device__ __forceinline__ void issue_data(const Ops& o, const uint8_t* ga, const uint8_t* gb, int d, uint32_t stage,
+                                           int w) {
+  if (d < 8) gemm::dma16s(ga, o.aoff[d], stage + 1024 * (w + 4 * d));
+  else gemm::dma16s(gb, o.boff[d - 8], stage + TILE_BYTES + 1024 * (w + 4 * (d - 8)));
+}
+
+// Scale ring. Row R of an operand's group buffer holds the 8 scale words of K tiles
+// G g .. G g + G - 1 (SFW words per tile), logical word q at physical word
+// q ^ ((R >> 3) & 7), so the 32 rows one wave reads per block land in 32 distinct banks.
+// Group g lives in buffer g & 1 and is copied in G slices of SLICE_ROWS rows per
+// operand, one slice per K tile while group g - 1 is in use. Copy c of this wave for
+// slice j of group g: 8 rows, lane l -> row 8 (l / 8) + ..., physical word l % 8.
 template <int FMT>
-__device__ __forceinline__ void issue_stage(const Ops& o, int kt, uint32_t stage, int w) {
+__device__ __forceinline__ void issue_slice(const Ops& o, int g, int j, int c, uint32_t ring, int w, int lane) {
   typedef Fmt<FMT> F;
-  const int64_t kb = (int64_t)kt * ROWB;
-  gemm::issue_tile8(o.A + kb, o.aoff, stage, w);
-  gemm::issue_tile8(o.B + kb, o.boff, stage + TILE_BYTES, w);
+  constexpr int PER_OP = F::SLICE_ROWS / 8;
+  const int k = w * F::SLICE_COPIES + c;
+  const int op = k / PER_OP, ii = k % PER_OP;
+  const int R = j * F::SLICE_ROWS + 8 * ii + (lane >> 3);
+  const int q = (lane & 7) ^ ((R >> 3) & 7);
+  const uint32_t word = (uint32_t)min(8 * g + q, o.ldw - 1);
+  const uint8_t* base = op ? o.SFB : o.SFA;
+  const uint32_t off = (uint32_t)min(R, op ? o.lim_b : o.lim_a) * (op ? o.ld_sfb : o.ld_sfa) + 4 * word;
+  gemm::dma4s(base, off, ring + (g & 1) * RING_GROUP + op * RING_OP + 32 * (j * F::SLICE_ROWS + 8 * ii));
+}
+
+// Raw scale words of K tile kt for this lane's rows (wave base + 32t + l%32).
+template <int FMT>
+__device__ __forceinline__ void read_scales(const uint8_t* lds, int kt, int wa, int wb, int lane, uint32_t (&sa)[4][2],
+                                            uint32_t (&sb)[4][2]) {
+  typedef Fmt<FMT> F;
+  const uint8_t* buf = lds + RING + ((kt / F::G) & 1) * RING_GROUP;
+  const int w0 = F::SFW * (kt % F::G);
+  const int r = lane & 31;
 #pragma unroll
-  for (int q = 0; q < F::SFW; q++) {
-    const int64_t word = 4 * ((int64_t)kt * F::SFW + q);
-    gemm::dma4s(o.SFA + word, o.sfa_off, stage + 2 * TILE_BYTES + 1024 * q + 256 * w);
-    gemm::dma4s(o.SFB + word, o.sfb_off, stage + 2 * TILE_BYTES + F::SF_BYTES + 1024 * q + 256 * w);
-  }
+  for (int q = 0; q < F::SFW; q++)
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const int sw = (4 * t + (r >> 3)) & 7;  // (row >> 3) & 7 for rows wave base + 32t + r
+      const uint32_t o = 32 * (32 * t + r) + 4 * ((w0 + q) ^ sw);
+      sa[t][q] = *(const BSM_LDS uint32_t*)(buf + 32 * wa + o);
+      sb[t][q] = *(const BSM_LDS uint32_t*)(buf + RING_OP + 32 * wb + o);
+    }
+}
+
+// Scale words of a partial last K tile, word-major at `area` (word q of row r at 1024q + 4r,
+// B after SFW KiB).
+template <int FMT>
+__device__ __forceinline__ void read_scales_wm(const uint8_t* area, int wa, int wb, int lane, uint32_t (&sa)[4][2],
+                                               uint32_t (&sb)[4][2]) {
+  typedef Fmt<FMT> F;
+#pragma unroll
+  for (int q = 0; q < F::SFW; q++)
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      sa[t][q] = *(const BSM_LDS uint32_t*)(area + 1024 * q + 4 * (wa + 32 * t + (lane & 31)));
+      sb[t][q] = *(const BSM_LDS uint32_t*)(area + 1024 * F::SFW + 1024 * q + 4 * (wb + 32 * t + (lane & 31)));
+    }
 }
 
 // Fragments of one 64-K step for one wave: af/bf[t][0..1] are the 16-byte chunks of
@@ -76,45 +134,31 @@ struct Frags {
   uint4 af[4][2], bf[4][2];
 };
 
-// Reads the fragments of 64-K step s of the stage at `st` for this wave. The lane's row
-// within a 32-row block is l%32; fp8 step s covers bytes 64s.. of the row: logical chunks
-// 4s + l/32 (k 16(l/32)..) and 4s + 2 + l/32 (k 32 + 16(l/32)..); fp4 step s covers bytes
-// 32s..: logical chunk 2s + l/32.
+// LDS read r of the fragments of 64-K step s of the tile at `st`: fp8 has 16 reads per step
+// (r: operand r / 8, block (r / 2) % 4, chunk r % 2), fp4 8 (operand r / 4, block r % 4).
+// The lane's row within a 32-row block is l%32; fp8 step s covers bytes 64s.. of the row:
+// logical chunks 4s + l/32 (k 16(l/32)..) and 4s + 2 + l/32 (k 32 + 16(l/32)..); fp4 step
+// s covers bytes 32s..: logical chunk 2s + l/32.
 template <int FMT>
-__device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wa, int wb, int lane, Frags& f) {
+__device__ __forceinline__ void read_frag(const uint8_t* st, int s, int r, int wa, int wb, int lane, Frags& f) {
   const int h = lane >> 5;
-#pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const uint8_t* pa = st + wa * ROWB + 4096 * t;
-    const uint8_t* pb = st + TILE_BYTES + wb * ROWB + 4096 * t;
-    if (FMT == 4) {
-      const uint32_t o = gemm::kmajor_frag_base(lane, 2 * s + h);
-      f.af[t][0] = lds_read_b128(pa + o);
-      f.bf[t][0] = lds_read_b128(pb + o);
-    } else {
-      const uint32_t o0 = gemm::kmajor_frag_base(lane, 4 * s + h), o1 = gemm::kmajor_frag_base(lane, 4 * s + 2 + h);
-      f.af[t][0] = lds_read_b128(pa + o0);
-      f.af[t][1] = lds_read_b128(pa + o1);
-      f.bf[t][0] = lds_read_b128(pb + o0);
-      f.bf[t][1] = lds_read_b128(pb + o1);
-    }
+  if (FMT == 4) {
+    const int op = r >> 2, t = r & 3;
+    const uint8_t* p = st + op * TILE_BYTES + (op ? wb : wa) * ROWB + 4096 * t;
+    const uint4 v = lds_read_b128(p + gemm::kmajor_frag_base(lane, 2 * s + h));
+    if (op) f.bf[t][0] = v; else f.af[t][0] = v;
+  } else {
+    const int op = r >> 3, t = (r >> 1) & 3, c = r & 1;
+    const uint8_t* p = st + op * TILE_BYTES + (op ? wb : wa) * ROWB + 4096 * t;
+    const uint4 v = lds_read_b128(p + gemm::kmajor_frag_base(lane, 4 * s + 2 * c + h));
+    if (op) f.bf[t][c] = v; else f.af[t][c] = v;
   }
 }
 
-// Raw scale words q of this lane's rows (wave base + 32t + l%32).
 template <int FMT>
-__device__ __forceinline__ void read_scales(const uint8_t* st, int wa, int wb, int lane, uint32_t (&sa)[4][2],
-                                            uint32_t (&sb)[4][2]) {
-  typedef Fmt<FMT> F;
-  const uint8_t* pa = st + 2 * TILE_BYTES;
-  const uint8_t* pb = pa + F::SF_BYTES;
+__device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wa, int wb, int lane, Frags& f) {
 #pragma unroll
-  for (int q = 0; q < F::SFW; q++)
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      sa[t][q] = *(const BSM_LDS uint32_t*)(pa + 1024 * q + 4 * (wa + 32 * t + (lane & 31)));
-      sb[t][q] = *(const BSM_LDS uint32_t*)(pb + 1024 * q + 4 * (wb + 32 * t + (lane & 31)));
-    }
+  for (int r = 0; r < (FMT == 4 ? 8 : 16); r++) read_frag<FMT>(st, s, r, wa, wb, lane, f);
 }
 
 template <int FMT, int SEL>
@@ -133,29 +177,35 @@ __device__ __forceinline__ f32x16 mfma_sc(const uint4 (&b)[2], const uint4 (&a)[
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, FMT, FMT, SEL, (int)sb, SEL, (int)sa);
 }
 
-template <int FMT, int MT0, int MT1>
+template <int FMT>
 __device__ __forceinline__ void pin_frags(Frags& f) {
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    if (t >= MT0 && t < MT1) {
-      gemm::pin_frag(f.af[t][0]);
-      if (FMT != 4) gemm::pin_frag(f.af[t][1]);
-    }
+    gemm::pin_frag(f.af[t][0]);
     gemm::pin_frag(f.bf[t][0]);
-    if (FMT != 4) gemm::pin_frag(f.bf[t][1]);
+    if (FMT != 4) {
+      gemm::pin_frag(f.af[t][1]);
+      gemm::pin_frag(f.bf[t][1]);
+    }
   }
 }
 
-// MFMAs of accumulator rows mt in [MT0, MT1) for 64-K step s of the tile: scale word
-// s / 2 of each row (after the per-lane shift), byte 2 (s & 1) (op_sel).
-template <int FMT, int S, int MT0, int MT1>
-__device__ __forceinline__ void mfma_rows(const Frags& f, const uint32_t (&sa)[4][2], const uint32_t (&sb)[4][2],
-                                          f32x16 (&acc)[4][4]) {
+// The 16 MFMAs of 64-K step S (accumulator rows mt-major), scale word S / 2 of each row
+// (after the per-lane shift), byte 2 (S & 1) (op_sel); side(i) runs after MFMA i, so that
+// LDS reads, copies and barriers issue while the matrix pipe is busy. Empty asm
+// "rewrites" of each accumulator before and after its MFMA fix the order of the MFMAs and
+// the side operations (all volatile) without any hardware wait.
+template <int FMT, int S, typename Side>
+__device__ __forceinline__ void mfma_step_il(const Frags& f, const uint32_t (&sa)[4][2], const uint32_t (&sb)[4][2],
+                                             f32x16 (&acc)[4][4], Side side) {
 #pragma unroll
-  for (int mt = MT0; mt < MT1; mt++)
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++)
-      acc[mt][nt] = mfma_sc<FMT, 2 * (S & 1)>(f.bf[nt], f.af[mt], acc[mt][nt], sb[nt][S >> 1], sa[mt][S >> 1]);
+  for (int i = 0; i < 16; i++) {
+    const int mt = i >> 2, nt = i & 3;
+    asm volatile("" : "+a"(acc[mt][nt])::"memory");
+    acc[mt][nt] = mfma_sc<FMT, 2 * (S & 1)>(f.bf[nt], f.af[mt], acc[mt][nt], sb[nt][S >> 1], sa[mt][S >> 1]);
+    asm volatile("" : "+a"(acc[mt][nt])::"memory");
+    side(i);
+  }
 }
 
 // Right-shift by 8 (l/32): lanes 32..63 carry the second 32-K block of each 64-K step,
@@ -175,7 +225,7 @@ __device__ __forceinline__ void shift_scales(const uint32_t (&ra)[4][2], const u
 template <int FMT, bool ACC>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int tiles_n) {
   typedef Fmt<FMT> F;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * F::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
@@ -191,95 +241,120 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   else gemm::zero_acc(acc);
 
   Ops o;
-  o.lda_b = a.lda / F::EPB;
-  o.ldb_b = a.ldb / F::EPB;
-  o.A = (const uint8_t*)a.A + m0 * o.lda_b;
-  o.B = (const uint8_t*)a.B + n0 * o.ldb_b;
+  const int64_t lda_b = a.lda / F::EPB, ldb_b = a.ldb / F::EPB;
+  o.A = (const uint8_t*)a.A + m0 * lda_b;
+  o.B = (const uint8_t*)a.B + n0 * ldb_b;
+  gemm::kmajor_dma_offsets(lda_b, m0, a.M, w, lane, o.aoff);
+  gemm::kmajor_dma_offsets(ldb_b, n0, a.N, w, lane, o.boff);
   o.SFA = a.SFA + m0 * a.ld_sfa;
   o.SFB = a.SFB + n0 * a.ld_sfb;
-  gemm::kmajor_dma_offsets(o.lda_b, m0, a.M, w, lane, o.aoff);
-  gemm::kmajor_dma_offsets(o.ldb_b, n0, a.N, w, lane, o.boff);
-  // scale row 64w + l of the tile (clamped to the last row), relative to the first row
-  o.sfa_off = (uint32_t)((min(m0 + 64 * w + lane, a.M - 1) - m0) * a.ld_sfa);
-  o.sfb_off = (uint32_t)((min(n0 + 64 * w + lane, a.N - 1) - n0) * a.ld_sfb);
+  o.ld_sfa = (uint32_t)a.ld_sfa;
+  o.ld_sfb = (uint32_t)a.ld_sfb;
+  o.lim_a = (int)min(a.M - 1 - m0, (int64_t)255);
+  o.lim_b = (int)min(a.N - 1 - n0, (int64_t)255);
+  o.ldw = (int)(min(a.ld_sfa, a.ld_sfb) / 4);
 
   const int nfull = (int)(a.K / F::KT);
   const int tail = (int)(a.K % F::KT);
   const uint32_t lds0 = gemm::lds_addr(lds);
+  const uint32_t ring = lds0 + RING;
   const int h8 = 8 * (lane >> 5);
   Frags f0, f1, f2, f3;
   uint32_t sa[4][2], sb[4][2], ra[4][2], rb[4][2];
   if (nfull > 0) {
-    issue_stage<FMT>(o, 0, lds0, w);
-    issue_stage<FMT>(o, min(1, nfull - 1), lds0 + F::STAGE, w);
-    gemm::stage_barrier<F::DMA_PER_TILE>();
+    // scale group 0 whole and slice 0 of group 1, then K tiles 0 and 1
+#pragma unroll
+    for (int j = 0; j < F::G; j++)
+#pragma unroll
+      for (int c = 0; c < F::SLICE_COPIES; c++) issue_slice<FMT>(o, 0, j, c, ring, w, lane);
+#pragma unroll
+    for (int c = 0; c < F::SLICE_COPIES; c++) issue_slice<FMT>(o, 1, 0, c, ring, w, lane);
+    const int k1 = min(1, nfull - 1);
+#pragma unroll
+    for (int d = 0; d < 16; d++) issue_data(o, o.A, o.B, d, lds0, w);
+#pragma unroll
+    for (int d = 0; d < 16; d++) issue_data(o, o.A + k1 * ROWB, o.B + k1 * ROWB, d, lds0 + STAGE, w);
+    gemm::stage_barrier<16>();
     read_frags<FMT>(lds, 0, wa, wb, lane, f0);
-    read_scales<FMT>(lds, wa, wb, lane, ra, rb);
+    read_scales<FMT>(lds, 0, wa, wb, lane, ra, rb);
     shift_scales<FMT>(ra, rb, h8, sa, sb);
   }
-  // K tile kt lives in stage kt & 1. The loop body is branch-free so that the scheduling
-  // fences hold: past the last tile the copies re-read the last tile (clamped index)
-  // into a stage nobody reads again.
+  // K tile kt lives in stage kt & 1; f0 holds its first 64-K step and sa/sb its scales
+  // when iteration kt starts. Each iteration: the fragment reads of the tile's other steps
+  // go out over the first MFMAs; one barrier once every wave's reads of the stage are done
+  // (then it takes the copies of tile kt + 2 and its share of the next scale group,
+  // spread one per MFMA slot or two); a second barrier once this wave's copies of tile
+  // kt + 1 have landed (then the step-0 fragments and the scales of tile kt + 1 are read).
+  // The body is branch-free: past the last tile the copies re-read the last tile (clamped
+  // index) into a stage nobody reads again, and the scale copies re-read the last words.
   for (int kt = 0; kt < nfull; kt++) {
-    const uint8_t* st = lds + (kt & 1) * F::STAGE;
-    const uint8_t* nst = lds + ((kt + 1) & 1) * F::STAGE;
-    const uint32_t stage = lds0 + (kt & 1) * F::STAGE;
-    const int kn = min(kt + 2, nfull - 1);
+    const uint8_t* st = lds + (kt & 1) * STAGE;
+    const uint8_t* nst = lds + ((kt + 1) & 1) * STAGE;
+    const uint32_t stage = lds0 + (kt & 1) * STAGE;
+    const int64_t k2 = (int64_t)min(kt + 2, nfull - 1) * ROWB;
+    const uint8_t* ga = o.A + k2;
+    const uint8_t* gb = o.B + k2;
+    const int sg = (kt + 1) / F::G + 1, sj = (kt + 1) % F::G;
+    // copy d of this iteration: operand copies 0..15, then the scale slice copies
+    auto copy = [&](int d) {
+      if (d < 16) issue_data(o, ga, gb, d, stage, w);
+      else issue_slice<FMT>(o, sg, sj, d - 16, ring, w, lane);
+    };
     if constexpr (FMT == 4) {
-      // read steps 1..3; MFMAs of step 0; barrier (stage free); copy tile kt + 2;
-      // MFMAs of steps 1, 2; barrier (tile kt + 1 landed); read step 0 and the scales of
-      // tile kt + 1; MFMAs of step 3; shift the new scales into place
-      read_frags<4>(st, 1, wa, wb, lane, f1);
-      read_frags<4>(st, 2, wa, wb, lane, f2);
-      read_frags<4>(st, 3, wa, wb, lane, f3);
-      pin_frags<4, 0, 4>(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<4, 0, 0, 4>(f0, sa, sb, acc);
-      gemm::pin_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
+      // 64 MFMA slots of 32 cycles: step 0 (slots 0..15) reads steps 1..3 (two a slot);
+      // barrier; copies at even slots 16..54; barrier at slot 40 (12 copies issued); the
+      // next tile's step-0 fragments and scales at slots 40..51
+      pin_frags<4>(f0);
+      mfma_step_il<4, 0>(f0, sa, sb, acc, [&](int i) {
+        if (i < 12) {
+#pragma unroll
+          for (int rr = 0; rr < 2; rr++) {
+            const int r = 2 * i + rr;  // step 1 + r / 8, read r % 8
+            Frags& dst = r < 8 ? f1 : (r < 16 ? f2 : f3);
+            read_frag<4>(st, 1 + r / 8, r & 7, wa, wb, lane, dst);
+          }
+        }
+      });
       gemm::lds_barrier();
-      issue_stage<4>(o, kn, stage, w);
-      pin_frags<4, 0, 4>(f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<4, 1, 0, 4>(f1, sa, sb, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<4, 2, 0, 4>(f2, sa, sb, acc);
-      gemm::pin_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm::stage_barrier<F::DMA_PER_TILE>();
-      read_frags<4>(nst, 0, wa, wb, lane, f0);
-      read_scales<4>(nst, wa, wb, lane, ra, rb);
-      pin_frags<4, 0, 4>(f3);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<4, 3, 0, 4>(f3, sa, sb, acc);
-      gemm::pin_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
+      pin_frags<4>(f1);
+      mfma_step_il<4, 1>(f1, sa, sb, acc, [&](int i) {
+        if ((i & 1) == 0) copy(i >> 1);
+      });
+      pin_frags<4>(f2);
+      mfma_step_il<4, 2>(f2, sa, sb, acc, [&](int i) {
+        if ((i & 1) == 0) copy(8 + (i >> 1));
+        if (i == 7) gemm::stage_barrier<12>();
+        if (i >= 8) read_frag<4>(nst, 0, i - 8, wa, wb, lane, f0);
+      });
+      pin_frags<4>(f3);
+      mfma_step_il<4, 3>(f3, sa, sb, acc, [&](int i) {
+        if ((i & 1) == 0 && i < 8) copy(16 + (i >> 1));
+        if (i == 0) read_scales<4>(lds, kt + 1, wa, wb, lane, ra, rb);
+      });
       shift_scales<4>(ra, rb, h8, sa, sb);
     } else {
-      // read step 1; MFMAs of step 0; barrier (stage free); copy tile kt + 2; MFMAs of
-      // rows 0-1 of step 1; barrier (tile kt + 1 landed); read step 0 and the scales of
-      // tile kt + 1; MFMAs of rows 2-3 of step 1; shift the new scales into place
-      read_frags<0>(st, 1, wa, wb, lane, f1);
-      pin_frags<0, 0, 4>(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<0, 0, 0, 4>(f0, sa, sb, acc);
-      gemm::pin_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm::lds_barrier();
-      issue_stage<0>(o, kn, stage, w);
-      pin_frags<0, 0, 2>(f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<0, 1, 0, 2>(f1, sa, sb, acc);
-      gemm::pin_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm::stage_barrier<F::DMA_PER_TILE>();
-      read_frags<0>(nst, 0, wa, wb, lane, f0);
-      read_scales<0>(nst, wa, wb, lane, ra, rb);
-      pin_frags<0, 2, 4>(f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_rows<0, 1, 2, 4>(f1, sa, sb, acc);
-      gemm::pin_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
+      // 32 MFMA slots of 64 cycles: step 0 reads step 1 at slots 0..3 (four a slot);
+      // barrier after slot 9; copies at slots 10..27; barrier before step 1 (6 copies
+      // issued); the next tile's step-0 fragments and scales at slots 16..23
+      pin_frags<0>(f0);
+      mfma_step_il<0, 0>(f0, sa, sb, acc, [&](int i) {
+        if (i < 4) {
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) read_frag<0>(st, 1, 4 * i + rr, wa, wb, lane, f1);
+        }
+        if (i == 9) gemm::lds_barrier();
+        if (i >= 10) copy(i - 10);
+      });
+      gemm::stage_barrier<6>();
+      pin_frags<0>(f1);
+      mfma_step_il<0, 1>(f1, sa, sb, acc, [&](int i) {
+        if (i < 12) copy(6 + i);
+        if (i < 8) {
+          read_frag<0>(nst, 0, 2 * i, wa, wb, lane, f0);
+          read_frag<0>(nst, 0, 2 * i + 1, wa, wb, lane, f0);
+        }
+        if (i == 0) read_scales<0>(lds, kt + 1, wa, wb, lane, ra, rb);
+      });
       shift_scales<0>(ra, rb, h8, sa, sb);
     }
   }
@@ -289,8 +364,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   if (tail) {
     const int64_t kb0 = (int64_t)nfull * ROWB;
     const int64_t kb_end = a.K / F::EPB;
-    gemm::kmajor_fill_masked((const uint8_t*)a.A, o.lda_b, m0, a.M, kb0, kb_end, lds, w, lane);
-    gemm::kmajor_fill_masked((const uint8_t*)a.B, o.ldb_b, n0, a.N, kb0, kb_end, lds + TILE_BYTES, w, lane);
+    gemm::kmajor_fill_masked((const uint8_t*)a.A, lda_b, m0, a.M, kb0, kb_end, lds, w, lane);
+    gemm::kmajor_fill_masked((const uint8_t*)a.B, ldb_b, n0, a.N, kb0, kb_end, lds + TILE_BYTES, w, lane);
+    uint8_t* area = lds + STAGE;
 #pragma unroll
     for (int q = 0; q < F::SFW; q++) {
       // scale word q of the partial tile; blocks at or past nblk (beyond K) become 127
@@ -299,13 +375,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
       const int64_t blk = ((int64_t)nfull * F::SFW + q) * 4;
       const int64_t valid = nblk - blk;
       const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : (1u << (8 * valid)) - 1u);
+      const int ra_row = min(64 * w + lane, o.lim_a), rb_row = min(64 * w + lane, o.lim_b);
       uint32_t wa_ = 0x7F7F7F7Fu, wb_ = 0x7F7F7F7Fu;
       if (valid > 0) {
-        wa_ = (*(const uint32_t*)(o.SFA + o.sfa_off + blk) & keep) | (0x7F7F7F7Fu & ~keep);
-        wb_ = (*(const uint32_t*)(o.SFB + o.sfb_off + blk) & keep) | (0x7F7F7F7Fu & ~keep);
+        wa_ = (*(const uint32_t*)(o.SFA + (int64_t)ra_row * a.ld_sfa + blk) & keep) | (0x7F7F7F7Fu & ~keep);
+        wb_ = (*(const uint32_t*)(o.SFB + (int64_t)rb_row * a.ld_sfb + blk) & keep) | (0x7F7F7F7Fu & ~keep);
       }
-      *(BSM_LDS uint32_t*)(lds + 2 * TILE_BYTES + 1024 * q + 256 * w + 4 * lane) = wa_;
-      *(BSM_LDS uint32_t*)(lds + 2 * TILE_BYTES + F::SF_BYTES + 1024 * q + 256 * w + 4 * lane) = wb_;
+      *(BSM_LDS uint32_t*)(area + 1024 * q + 256 * w + 4 * lane) = wa_;
+      *(BSM_LDS uint32_t*)(area + 1024 * F::SFW + 1024 * q + 256 * w + 4 * lane) = wb_;
     }
     __syncthreads();
     // 64-K steps of the partial tile: steps past K see zero operands (and unit scales)
@@ -314,14 +391,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
     const int steps = (tail + 63) / 64;
     for (int s = 0; s < steps; s++) {
       read_frags<FMT>(lds, s, wa, wb, lane, f0);
-      read_scales<FMT>(lds, wa, wb, lane, ra, rb);
+      read_scales_wm<FMT>(area, wa, wb, lane, ra, rb);
       const int sh = h8 + 16 * (s & 1);
 #pragma unroll
       for (int t = 0; t < 4; t++) {
         sa[t][0] = __builtin_amdgcn_readfirstlane(s >> 1) ? ra[t][1] >> sh : ra[t][0] >> sh;
         sb[t][0] = __builtin_amdgcn_readfirstlane(s >> 1) ? rb[t][1] >> sh : rb[t][0] >> sh;
       }
-      mfma_rows<FMT, 0, 0, 4>(f0, sa, sb, acc);
+      mfma_step_il<FMT, 0>(f0, sa, sb, acc, [](int) {});
     }
   }
   gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);

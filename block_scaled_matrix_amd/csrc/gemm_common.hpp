@@ -236,5 +236,75 @@ __device__ __forceinline__ void store_tile_t(float* __restrict__ D, int64_t ldd,
   }
 }
 
+// The same store through LDS: the accumulators pass through this wave's 32 KiB region
+// `region` in two halves of 64 rows and leave as stores of two 512-byte row pieces per
+// instruction (whole 128-byte lines), instead of 32 rows x 32 bytes per instruction,
+// which the memory path takes about twice as long to accept. Region row r (512 bytes)
+// keeps its 16-byte chunk c at c ^ (r & 15): the 16 rows written by one 16-lane group
+// then cover all 64 banks, and so does a read of 16 consecutive chunks of one row. D is
+// addressed as global memory so that the compiler may keep several LDS reads in flight
+// ahead of the stores. A sub-tile that crosses the edge of D stores the in-range
+// elements only. The caller has synchronised the workgroup so that nobody still reads
+// the region's bytes.
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+typedef __attribute__((address_space(1))) float global_f32;
+__device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
+                                                 int64_t col0, int lane, float sgn, const f32x16 (&acc)[4][4],
+                                                 uint8_t* region) {
+  const bool whole = row0 + 128 <= M && col0 + 128 <= N;  // wave-uniform
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+#pragma unroll
+    for (int m2 = 0; m2 < 2; m2++) {
+      const int r = 32 * m2 + (lane & 31);
+#pragma unroll
+      for (int nt = 0; nt < 4; nt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int c = 8 * nt + 2 * q + (lane >> 5);
+          const f32x16& v = acc[2 * half + m2][nt];
+          const uint4 x = make_uint4(__float_as_uint(sgn * v[4 * q]), __float_as_uint(sgn * v[4 * q + 1]),
+                                     __float_as_uint(sgn * v[4 * q + 2]), __float_as_uint(sgn * v[4 * q + 3]));
+          lds_write_b128(region + 512 * r + 16 * (c ^ (r & 15)), x);
+        }
+    }
+    const int c = lane & 31;
+    const int64_t col = col0 + 4 * c;
+    if (whole) {
+      // eight reads in flight ahead of their stores
+#pragma unroll
+      for (int j0 = 0; j0 < 32; j0 += 8) {
+        uint4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const int r = 2 * (j0 + j) + (lane >> 5);
+          x[j] = lds_read_b128(region + 512 * r + 16 * (c ^ (r & 15)));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const int r = 2 * (j0 + j) + (lane >> 5);
+          *(global_u32x4*)(D + (row0 + 64 * half + r) * ldd + col) = (u32x4){x[j].x, x[j].y, x[j].z, x[j].w};
+        }
+      }
+    } else {
+      for (int j = 0; j < 32; j++) {
+        const int r = 2 * j + (lane >> 5);
+        const uint4 x = lds_read_b128(region + 512 * r + 16 * (c ^ (r & 15)));
+        const int64_t row = row0 + 64 * half + r;
+        if (row < M) {
+          global_f32* p = (global_f32*)(D + row * ldd + col);
+          if (col + 3 < N) {
+            *(global_u32x4*)p = (u32x4){x.x, x.y, x.z, x.w};
+          } else {
+            if (col < N) p[0] = __uint_as_float(x.x);
+            if (col + 1 < N) p[1] = __uint_as_float(x.y);
+            if (col + 2 < N) p[2] = __uint_as_float(x.z);
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace gemm
 }  // namespace bsm

@@ -229,9 +229,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
   }
   // K tile kt lives in stage kt & 1. Iteration kt: MFMAs of step 0 with the fragment reads
   // of steps 1..3 spread over its first 12 MFMAs; barrier once every wave's reads of the
-  // stage are done; MFMAs of step 1 with the 16 copies of tile kt + 2 into the stage, one
-  // after each MFMA; MFMAs of step 2; barrier once this wave's copies of tile kt + 1 have
-  // landed; MFMAs of step 3 with the step-0 fragment reads of tile kt + 1. The body is
+  // stage are done; MFMAs of steps 1 and 2 with the 16 copies of tile kt + 2 into the
+  // stage, one after every second MFMA (the four waves' copies then keep the shared copy
+  // path busy without blocking their issue); barrier once this wave's copies of tile
+  // kt + 1 have landed; MFMAs of step 3 with the step-0 fragment reads of tile kt + 1. The body is
   // branch-free: past the last tile the copies re-read the last tile (clamped index) into
   // a stage nobody reads again.
   for (int kt = 0; kt < nfull; kt++) {
@@ -257,11 +258,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
     gemm::lds_barrier();
     pin_step(a1, b1);
     mfma_step_il<DT>(a1, b1, acc, [&](int i) {
-      if (i < 8) gemm::dma16s(ga, aoff[i], stage + 1024 * (w + 4 * i));
-      else gemm::dma16s(gb, boff[i - 8], stage + TILE_BYTES + 1024 * (w + 4 * (i - 8)));
+      if ((i & 1) == 0) gemm::dma16s(ga, aoff[i >> 1], stage + 1024 * (w + 4 * (i >> 1)));
     });
     pin_step(a2, b2);
-    mfma_step_il<DT>(a2, b2, acc, [&](int) {});
+    mfma_step_il<DT>(a2, b2, acc, [&](int i) {
+      if ((i & 1) == 0) gemm::dma16s(gb, boff[i >> 1], stage + TILE_BYTES + 1024 * (w + 4 * (i >> 1)));
+    });
     gemm::stage_barrier<DMA_PER_TILE>();
     pin_step(a3, b3);
     mfma_step_il<DT>(a3, b3, acc, [&](int i) {
@@ -282,7 +284,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
       mfma_step<DT>(a0, b0, acc);
     }
   }
-  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
+  // every wave is done with LDS before the accumulators pass through it
+  __syncthreads();
+  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w);
 }
 
 template <int DT, bool AK, bool BKM>

@@ -401,7 +401,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
       mfma_step_il<FMT, 0>(f0, sa, sb, acc, [](int) {});
     }
   }
-  gemm::store_tile_t(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
+  // every wave is done with LDS before the accumulators pass through it
+  __syncthreads();
+  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w);
 }
 
 }  // namespace

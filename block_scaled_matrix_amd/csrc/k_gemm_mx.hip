@@ -302,8 +302,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
     };
     if constexpr (FMT == 4) {
       // 64 MFMA slots of 32 cycles: step 0 (slots 0..15) reads steps 1..3 (two a slot);
-      // barrier; copies at even slots 16..54; barrier at slot 40 (12 copies issued); the
-      // next tile's step-0 fragments and scales at slots 40..51
+      // barrier at slot 24, once the LDS has served those reads; copies at even slots
+      // 24..62; barrier at slot 48 (12 copies issued); the next tile's step-0 fragments
+      // and scales at slots 48..55
       pin_frags<4>(f0);
       mfma_step_il<4, 0>(f0, sa, sb, acc, [&](int i) {
         if (i < 12) {
@@ -315,27 +316,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
           }
         }
       });
-      gemm::lds_barrier();
       pin_frags<4>(f1);
       mfma_step_il<4, 1>(f1, sa, sb, acc, [&](int i) {
-        if ((i & 1) == 0) copy(i >> 1);
+        if (i == 7) gemm::lds_barrier();
+        if (i >= 8 && (i & 1) == 0) copy((i - 8) >> 1);
       });
       pin_frags<4>(f2);
       mfma_step_il<4, 2>(f2, sa, sb, acc, [&](int i) {
-        if ((i & 1) == 0) copy(8 + (i >> 1));
-        if (i == 7) gemm::stage_barrier<12>();
-        if (i >= 8) read_frag<4>(nst, 0, i - 8, wa, wb, lane, f0);
+        if ((i & 1) == 0) copy(4 + (i >> 1));
       });
       pin_frags<4>(f3);
       mfma_step_il<4, 3>(f3, sa, sb, acc, [&](int i) {
-        if ((i & 1) == 0 && i < 8) copy(16 + (i >> 1));
+        if (i == 0) gemm::stage_barrier<12>();
+        if ((i & 1) == 0) copy(12 + (i >> 1));
         if (i == 0) read_scales<4>(lds, kt + 1, wa, wb, lane, ra, rb);
+        if (i < 8) read_frag<4>(nst, 0, i, wa, wb, lane, f0);
       });
       shift_scales<4>(ra, rb, h8, sa, sb);
     } else {
       // 32 MFMA slots of 64 cycles: step 0 reads step 1 at slots 0..3 (four a slot);
-      // barrier after slot 9; copies at slots 10..27; barrier before step 1 (6 copies
-      // issued); the next tile's step-0 fragments and scales at slots 16..23
+      // barrier after slot 9; copies at slots 10..27; barrier at slot 20 (10 copies
+      // issued); the next tile's step-0 fragments and scales at slots 20..27
       pin_frags<0>(f0);
       mfma_step_il<0, 0>(f0, sa, sb, acc, [&](int i) {
         if (i < 4) {
@@ -345,15 +346,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
         if (i == 9) gemm::lds_barrier();
         if (i >= 10) copy(i - 10);
       });
-      gemm::stage_barrier<6>();
       pin_frags<0>(f1);
       mfma_step_il<0, 1>(f1, sa, sb, acc, [&](int i) {
+        if (i == 4) gemm::stage_barrier<10>();
         if (i < 12) copy(6 + i);
-        if (i < 8) {
-          read_frag<0>(nst, 0, 2 * i, wa, wb, lane, f0);
-          read_frag<0>(nst, 0, 2 * i + 1, wa, wb, lane, f0);
+        if (i == 4) read_scales<0>(lds, kt + 1, wa, wb, lane, ra, rb);
+        if (i >= 4 && i < 12) {
+          read_frag<0>(nst, 0, 2 * (i - 4), wa, wb, lane, f0);
+          read_frag<0>(nst, 0, 2 * (i - 4) + 1, wa, wb, lane, f0);
         }
-        if (i == 0) read_scales<0>(lds, kt + 1, wa, wb, lane, ra, rb);
       });
       shift_scales<0>(ra, rb, h8, sa, sb);
     }

@@ -254,6 +254,25 @@ __device__ __forceinline__ void stream_store16(uint8_t* p, uint4 x) {
   __builtin_nontemporal_store(v, (u32x4*)p);
 }
 
+// The first nb bytes (0 < nb < 16) of a 16-byte chunk to a 16-byte aligned address, as at
+// most four naturally aligned stores of 8, 4, 2 and 1 bytes: element-wise sub-dword stores
+// of a chunk's tail cost the memory path far more than these.
+__device__ __forceinline__ void store_head16(uint8_t* p, uint4 x, int nb) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  int o = 0;
+  if (nb & 8) {
+    *(uint2*)p = make_uint2(x.x, x.y);
+    o = 8;
+  }
+  if (nb & 4) {
+    *(uint32_t*)(p + o) = o ? x.z : x.x;
+    o += 4;
+  }
+  const uint32_t wo = o == 0 ? w[0] : (o == 4 ? w[1] : (o == 8 ? w[2] : w[3]));
+  if (nb & 2) *(uint16_t*)(p + o) = (uint16_t)wo;
+  if (nb & 1) *(p + o + (nb & 2)) = (uint8_t)(wo >> (8 * (nb & 2)));
+}
+
 // ------------------------------------------------------------------ grid round trip
 struct CopyOut {
   int64_t dst_strides[5];
@@ -302,39 +321,60 @@ struct Copy2D {
   int64_t dims0, dims1;                 // rows, columns (elements)
   int64_t s_src, s_dst, s_add;          // row strides (bytes)
   uint32_t tiles1;                      // boxes per row of boxes
+  uint32_t groups1;                     // workgroups per row of boxes: ceil(tiles1 / 2^lg_nb)
+  uint32_t slices;                      // row slices per box: ceil(box0 / (4 * rows per pass))
   int32_t box0, box1;                   // box extents (rows, elements)
-  int32_t esize, dtype, swizzle, lg_cpr, row_bytes;
+  int32_t esize, dtype, swizzle, lg_cpr, lg_nb, row_bytes;
   uint32_t fill_word;                   // the fill element replicated over 32 bits
 };
 
-// Lane l moves chunk column l % cpr of image rows l / cpr + k * (256 / cpr), k < 4. All
-// source and reduce-add chunks are fetched first with 128-bit streaming loads, so every HBM
-// read of the workgroup is in flight at once. A chunk that straddles the last column is
-// read whole as well (its 16 bytes lie inside the tensor's extent on every row but the
-// last) and its elements past the last column are replaced by the fill; on the tensor's
-// last row it is gathered element by element. Rows past the last row and chunks past the
-// last column take the fill. Whole chunks are stored with 128-bit streaming stores, the
-// straddling chunk element-wise (in-range elements only).
-template <bool ADD>
+// A workgroup moves one row slice of 2^lg_nb horizontally adjacent boxes (the bf16 (128,
+// 64) box: 32 rows x 4 boxes, i.e. rows of 512 contiguous bytes, which HBM serves
+// markedly faster than the 128-byte rows of a single box at a power-of-two row pitch).
+// Lane l takes chunk column l % (nb cpr) (box (l % (nb cpr)) / cpr) of slice rows
+// l / (nb cpr) + k * rstep, k < 4. Each box keeps its own image region in LDS: the slice's
+// rows sit there at the swizzled offsets they have in the full box image (a slice spans a
+// whole number of swizzle periods, so the pattern is the same). All source and
+// reduce-add chunks are fetched first with 128-bit streaming loads, so every HBM read of the
+// workgroup is in flight at once. A chunk that straddles the last column is read whole as
+// well (its 16 bytes lie inside the tensor's extent on every row but the last) and its
+// elements past the last column are replaced by the fill; on the tensor's last row it is
+// gathered element by element. Rows past the last row and chunks past the last column
+// take the fill. Whole chunks are stored with 128-bit streaming stores, the straddling
+// chunk's in-range head with at most four aligned stores. Boxes past the end of a row of boxes (when
+// the workgroup's group is incomplete) do nothing.
+// ADDT: 0 for a plain copy, else the reduce-add element type (BSM_F32, BSM_BF16, BSM_F16),
+// fixed at compile time so that the add is straight-line code: a run-time type switch
+// between the stores makes the compiler wait for every outstanding store before each add.
+template <int ADDT>
 __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
+  constexpr bool ADD = ADDT != 0;
   extern __shared__ __attribute__((aligned(1024))) uint8_t image[];
-  const uint32_t t1 = blockIdx.x % a.tiles1, t0 = blockIdx.x / a.tiles1;
-  const int64_t c0 = (int64_t)t0 * a.box0, c1 = (int64_t)t1 * a.box1;
+  const uint32_t g1 = blockIdx.x % a.groups1, rest = blockIdx.x / a.groups1;
+  const uint32_t sl = rest % a.slices, t0 = rest / a.slices;
+  const int lg_row = a.lg_cpr + a.lg_nb;                  // log2 chunks per slice row
   const int cpr = 1 << a.lg_cpr;
-  const int cc = threadIdx.x & (cpr - 1), r0 = threadIdx.x >> a.lg_cpr, rstep = 256 >> a.lg_cpr;
+  const int call = threadIdx.x & ((1 << lg_row) - 1);
+  const int bx = call >> a.lg_cpr, cc = call & (cpr - 1);
+  const int rr0 = threadIdx.x >> lg_row, rstep = 256 >> lg_row;
+  const int rs = 4 * rstep;                               // rows per slice
+  const uint32_t t1 = (g1 << a.lg_nb) + bx;
+  const bool boxok = t1 < a.tiles1;
+  const int64_t c0 = (int64_t)t0 * a.box0, c1 = (int64_t)t1 * a.box1;
   const int epc = 16 / a.esize;
   const int64_t k0 = c1 + (int64_t)cc * epc;           // first element of the lane's chunk
   const bool whole = k0 + epc <= a.dims1;              // chunk wholly in range
   const bool part = !whole && k0 < a.dims1;            // chunk straddles the last column
   const int64_t kc = whole || part ? k0 : ((a.dims1 / epc) - 1) * epc;  // a whole chunk stands in
   const uint4 fill4 = make_uint4(a.fill_word, a.fill_word, a.fill_word, a.fill_word);
+  uint8_t* region = image + bx * rs * a.row_bytes;      // this box's slice of its image
   uint4 v[4], d[4];
   bool rin[4], last[4];
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    const int r = r0 + k * rstep;
+    const int r = (int)sl * rs + rr0 + k * rstep;        // row within the box
     const int64_t row = c0 + r;
-    rin[k] = r < a.box0 && row < a.dims0;
+    rin[k] = boxok && r < a.box0 && row < a.dims0;
     const int64_t rowc = min(row, a.dims0 - 1);          // rows past the end re-read the last row
     last[k] = part && rowc == a.dims0 - 1;               // no 16-byte read past the tensor's end
     const int64_t col = (last[k] ? ((a.dims1 / epc) - 1) * epc : kc) * a.esize;
@@ -354,35 +394,40 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       if (!rin[k] || !last[k]) continue;
-      const uint8_t* row = a.src + (c0 + r0 + k * rstep) * a.s_src;
+      const uint8_t* row = a.src + (c0 + (int)sl * rs + rr0 + k * rstep) * a.s_src;
       for (int e = 0; e < epc; e++)
         if (k0 + e < a.dims1) put_elem(v[k], a.esize, e, load_elem(row + (k0 + e) * a.esize, a.esize));
     }
   }
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    const int r = r0 + k * rstep;
-    if (r < a.box0) lds_write_b128(image + image_swizzle((uint32_t)(r * a.row_bytes + cc * 16), a.swizzle), v[k]);
+    const int rr = rr0 + k * rstep;
+    if ((int)sl * rs + rr < a.box0)
+      lds_write_b128(region + image_swizzle((uint32_t)(rr * a.row_bytes + cc * 16), a.swizzle), v[k]);
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    const int r = r0 + k * rstep;
-    const int64_t row = c0 + r;
+    const int rr = rr0 + k * rstep;
+    const int64_t row = c0 + (int)sl * rs + rr;
     if (!rin[k] || !(whole || part)) continue;
-    const uint4 x = lds_read_b128(image + image_swizzle((uint32_t)(r * a.row_bytes + cc * 16), a.swizzle));
+    const uint4 x = lds_read_b128(region + image_swizzle((uint32_t)(rr * a.row_bytes + cc * 16), a.swizzle));
     if (__builtin_expect(whole, 1)) {
       if (a.dst) stream_store16(a.dst + row * a.s_dst + k0 * a.esize, x);
-      if (ADD) stream_store16(a.add + row * a.s_add + k0 * a.esize, add_chunk(a.dtype, d[k], x));
+      if (ADD) stream_store16(a.add + row * a.s_add + k0 * a.esize, add_chunk(ADDT, d[k], x));
     } else {
-      const uint4 y = ADD ? add_chunk(a.dtype, d[k], x) : x;  // d[k] is valid unless on the last row
-      for (int e = 0; e < epc; e++) {
-        if (k0 + e >= a.dims1) continue;
-        if (a.dst) store_elem(a.dst + row * a.s_dst + (k0 + e) * a.esize, a.esize, get_elem(x, a.esize, e));
-        if (ADD) {
-          uint8_t* q = a.add + row * a.s_add + (k0 + e) * a.esize;
-          store_elem(q, a.esize,
-                     last[k] ? add_elem(a.dtype, load_elem(q, a.esize), get_elem(x, a.esize, e)) : get_elem(y, a.esize, e));
+      // the straddling chunk: its in-range head only
+      const int nb = (int)(a.dims1 - k0) * a.esize;
+      if (a.dst) store_head16(a.dst + row * a.s_dst + k0 * a.esize, x, nb);
+      if (ADD) {
+        uint8_t* q = a.add + row * a.s_add + k0 * a.esize;
+        if (!last[k]) {
+          store_head16(q, add_chunk(ADDT, d[k], x), nb);  // d[k] holds this chunk
+        } else {
+          // the tensor's last row: d[k] holds another chunk, the addends come element-wise
+          for (int e = 0; e < epc; e++)
+            if (k0 + e < a.dims1)
+              store_elem(q + e * a.esize, a.esize, add_elem(ADDT, load_elem(q + e * a.esize, a.esize), get_elem(x, a.esize, e)));
         }
       }
     }
@@ -394,10 +439,7 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_box_copy, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k_box_copy2d<true>, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k_box_copy2d<false>, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -426,11 +468,29 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
     a.esize = g.esize; a.dtype = g.dtype; a.swizzle = g.swizzle; a.row_bytes = g.row_bytes;
     a.lg_cpr = 0;
     while ((1 << a.lg_cpr) < cpr) a.lg_cpr++;
+    // up to 4 boxes side by side per workgroup while a slice row stays within 64 chunks
+    // (at least 4 rows per pass) and the row of boxes has that many boxes
+    a.lg_nb = 0;
+    while (a.lg_nb < 2 && (2 * cpr << a.lg_nb) <= 64 && (int64_t(2) << a.lg_nb) <= (int64_t)o.tiles[1]) a.lg_nb++;
+    const int rs = 4 * (256 >> (a.lg_cpr + a.lg_nb));      // rows per slice
+    a.groups1 = (uint32_t)((o.tiles[1] + (1u << a.lg_nb) - 1) >> a.lg_nb);
+    a.slices = (uint32_t)((g.box[0] + rs - 1) / rs);
     a.fill_word = g.esize == 1 ? g.fill_bits * 0x01010101u : (g.esize == 2 ? g.fill_bits * 0x00010001u : g.fill_bits);
-    if (dst_add)
-      hipLaunchKernelGGL(k_box_copy2d<true>, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, a);
+    const int64_t wgs = (int64_t)o.tiles[0] * a.slices * a.groups1;
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // every box's slice region is rs * row_bytes = 16 KiB / 2^lg_nb, a whole number of
+    // swizzle periods (the swizzle stays inside aligned 2^(7 + mode)-byte windows)
+    const size_t lds_bytes = (size_t)4 * 256 * 16;
+    if (!dst_add)
+      hipLaunchKernelGGL(k_box_copy2d<0>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
+    else if (g.dtype == BSM_F32)
+      hipLaunchKernelGGL(k_box_copy2d<BSM_F32>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
+    else if (g.dtype == BSM_BF16)
+      hipLaunchKernelGGL(k_box_copy2d<BSM_BF16>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
+    else if (g.dtype == BSM_F16)
+      hipLaunchKernelGGL(k_box_copy2d<BSM_F16>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
     else
-      hipLaunchKernelGGL(k_box_copy2d<false>, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, a);
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_box_copy, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, g, o,

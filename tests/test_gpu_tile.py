@@ -159,6 +159,51 @@ def test_box_copy_grid_vs_oracle(O, rows, cols, pitch, box, swz):
     assert np.array_equal(host(da, np.uint16, add.shape), add)
 
 
+_NP = {"u8": np.uint8, "f16": np.uint16, "bf16": np.uint16, "f32": np.uint32}
+
+
+@pytest.mark.parametrize("dtype,rows,cols,pitch,box,swz,mode", [
+    ("u8", 70, 77, 96, (32, 64), 0, "copy"),      # straddling tail of 13 bytes: 8 + 4 + 1
+    ("u8", 40, 35, 48, (16, 32), 1, "copy"),      # 3 bytes: 2 + 1
+    ("f16", 50, 91, 104, (32, 64), 3, "both"),    # 6 bytes: 4 + 2
+    ("f32", 33, 45, 48, (16, 32), 3, "add"),      # 4 bytes, reduce-add only
+    ("f32", 66, 43, 48, (64, 16), 2, "both"),     # 12 bytes: 8 + 4
+    ("bf16", 20, 63, 64, (16, 64), 3, "copy")])   # 14 bytes: 8 + 4 + 2
+def test_box_copy_grid_dtypes_vs_oracle(O, dtype, rows, cols, pitch, box, swz, mode):
+    """Rank-2 grid round trips over element types and ragged rows whose last 16-byte chunk is
+    cut at every width the head stores handle; the row padding holds a sentinel that must stay."""
+    rng = np.random.default_rng(rows * 1000 + cols)
+    t = _NP[dtype]
+    es = np.dtype(t).itemsize
+
+    def tensor(fill):
+        a = np.full((rows, pitch), fill, t)
+        if dtype == "u8":
+            a[:, :cols] = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+        elif dtype == "f32":
+            a[:, :cols] = rng.standard_normal((rows, cols)).astype(np.float32).view(np.uint32)
+        else:
+            a[:, :cols] = W.to_half_bits(rng.standard_normal((rows, cols)).astype(np.float32), dtype)
+        return a
+
+    sentinel = {"u8": 0xA5, "f16": 0x7E01, "bf16": W.SENTINEL_BF16, "f32": 0x7FC00123}[dtype]
+    src = tensor(sentinel)
+    dst = np.full((rows, pitch), sentinel, t) if mode in ("copy", "both") else None
+    add = tensor(sentinel) if mode in ("add", "both") else None
+    say("box_copy dtypes", dtype, rows, cols, pitch, box, swz, mode)
+    st = (pitch * es, es)
+    ds = dev(src)
+    dd = dev(dst) if dst is not None else None
+    da = dev(add) if add is not None else None
+    desc = lambda x: bsm.tensor_desc(x, dtype, (rows, cols), st) if x is not None else None
+    bsm.bsm_tile_box_copy(desc(ds), desc(dd), desc(da), bsm.box_desc(box, (1, 1), swz, 0))
+    O.box_copy_grid(src, dst, add, dtype, (rows, cols), st, box, (1, 1), swz, 0)
+    if dst is not None:
+        assert np.array_equal(host(dd, t, dst.shape), dst)
+    if add is not None:
+        assert np.array_equal(host(da, t, add.shape), add)
+
+
 def test_box_copy_full_size_vs_oracle(O):
     """The 16381 x 8190 bf16 workload (8192-element pitch, (128,64) boxes, 128-byte swizzle)."""
     w = W.box_copy_bf16()

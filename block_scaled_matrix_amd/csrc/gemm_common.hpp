@@ -156,46 +156,6 @@ __device__ __forceinline__ void kmajor_fill_masked(const uint8_t* __restrict__ p
   }
 }
 
-// Accumulators start from s * D when accumulating; the epilogue then stores s * acc,
-// i.e. D + s * sum with the negation applied exactly twice. Lane layout as in
-// store_tile_t. Rows past M and columns past N start at zero (their addresses are
-// clamped into the tensor; they are never stored). Branch-free within each path so
-// that the accumulators are written once, in place.
-__device__ __forceinline__ void load_acc(const float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
-                                         int64_t col0, int lane, float sgn, f32x16 (&acc)[4][4]) {
-  const bool cols_whole = col0 + 128 <= N;  // wave-uniform
-#pragma unroll
-  for (int mt = 0; mt < 4; mt++) {
-    const int64_t row = row0 + 32 * mt + (lane & 31);
-    const float rs = row < M ? sgn : 0.0f;
-    const float* drow = D + min(row, M - 1) * ldd;
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int64_t col = col0 + 32 * nt + 8 * q + 4 * (lane >> 5);
-        float4 v;
-        if (cols_whole) {
-          v = *(const float4*)(drow + col);
-        } else {
-          v.x = col < N ? drow[min(col, N - 1)] : 0.0f;
-          v.y = col + 1 < N ? drow[min(col + 1, N - 1)] : 0.0f;
-          v.z = col + 2 < N ? drow[min(col + 2, N - 1)] : 0.0f;
-          v.w = col + 3 < N ? drow[min(col + 3, N - 1)] : 0.0f;
-        }
-        acc[mt][nt][4 * q] = rs * v.x;
-        acc[mt][nt][4 * q + 1] = rs * v.y;
-        acc[mt][nt][4 * q + 2] = rs * v.z;
-        acc[mt][nt][4 * q + 3] = rs * v.w;
-      }
-    }
-    // one 32-row block at a time: bounds the registers the loads occupy before they move
-    // into the accumulators
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) asm volatile("" : "+a"(acc[mt][nt])::"memory");
-  }
-}
-
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
@@ -205,52 +165,26 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
       for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
 }
 
-// D = s * acc for a 128 x 128 wave sub-tile held as 4 x 4 blocks of v_mfma 32x32
-// accumulators computed with the operands swapped (the MFMA row index runs over N):
-// register 4q + e of block (mt, nt) is output row 32mt + l%32, column
-// 32nt + 8q + 4(l/32) + e, so each group of four registers is 16 contiguous bytes of a
-// row of D and moves with one dwordx4 store (element-wise only at a ragged N).
-__device__ __forceinline__ void store_tile_t(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
-                                             int64_t col0, int lane, float sgn, const f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int mt = 0; mt < 4; mt++) {
-    const int64_t row = row0 + 32 * mt + (lane & 31);
-    if (row >= M) continue;
-    float* drow = D + row * ldd;
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int64_t col = col0 + 32 * nt + 8 * q + 4 * (lane >> 5);
-        const float4 v = make_float4(sgn * acc[mt][nt][4 * q], sgn * acc[mt][nt][4 * q + 1],
-                                     sgn * acc[mt][nt][4 * q + 2], sgn * acc[mt][nt][4 * q + 3]);
-        if (col + 3 < N) {
-          *(float4*)(drow + col) = v;
-        } else {
-          if (col < N) drow[col] = v.x;
-          if (col + 1 < N) drow[col + 1] = v.y;
-          if (col + 2 < N) drow[col + 2] = v.z;
-        }
-      }
-    }
-  }
-}
-
-// The same store through LDS: the accumulators pass through this wave's 32 KiB region
-// `region` in two halves of 64 rows and leave as stores of two 512-byte row pieces per
-// instruction (whole 128-byte lines), instead of 32 rows x 32 bytes per instruction,
-// which the memory path takes about twice as long to accept. Region row r (512 bytes)
-// keeps its 16-byte chunk c at c ^ (r & 15): the 16 rows written by one 16-lane group
-// then cover all 64 banks, and so does a read of 16 consecutive chunks of one row. D is
-// addressed as global memory so that the compiler may keep several LDS reads in flight
-// ahead of the stores. A sub-tile that crosses the edge of D stores the in-range
-// elements only. The caller has synchronised the workgroup so that nobody still reads
-// the region's bytes.
+// D = s * acc (+ D when `add`) for a 128 x 128 wave sub-tile held as 4 x 4 blocks of
+// v_mfma 32x32 accumulators computed with the operands swapped (the MFMA row index runs over
+// N): register 4q + e of block (mt, nt) is output row 32mt + l%32, column
+// 32nt + 8q + 4(l/32) + e. The accumulators pass through this wave's
+// 32 KiB region `region` in two halves of 64 rows and leave as stores of two 512-byte row
+// pieces per instruction (whole 128-byte lines), instead of 32 rows x 32 bytes per
+// instruction, which the memory path takes about twice as long to accept; with `add`, D
+// arrives in the same whole-line pieces, eight loads in flight. Region row r (512 bytes)
+// keeps its 16-byte chunk c at c ^ (r & 15): the 16 rows written by one 16-lane group then
+// cover all 64 banks, and so does a read of 16 consecutive chunks of one row. D is
+// addressed as global memory so that the compiler may keep several LDS reads and D loads
+// in flight ahead of the stores. A sub-tile that crosses the edge of D touches the
+// in-range elements only. The caller has synchronised the workgroup so that nobody still
+// reads the region's bytes. (s * acc + D rounds once, as an accumulating MFMA chain started
+// from D would round the same terms in another order.)
 typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 typedef __attribute__((address_space(1))) float global_f32;
 __device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
                                                  int64_t col0, int lane, float sgn, const f32x16 (&acc)[4][4],
-                                                 uint8_t* region) {
+                                                 uint8_t* region, bool add) {
   const bool whole = row0 + 128 <= M && col0 + 128 <= N;  // wave-uniform
 #pragma unroll
   for (int half = 0; half < 2; half++) {
@@ -271,19 +205,26 @@ __device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t 
     const int c = lane & 31;
     const int64_t col = col0 + 4 * c;
     if (whole) {
-      // eight reads in flight ahead of their stores
+      // eight reads (and D loads) in flight ahead of their stores
 #pragma unroll
       for (int j0 = 0; j0 < 32; j0 += 8) {
         uint4 x[8];
+        u32x4 y[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
           const int r = 2 * (j0 + j) + (lane >> 5);
           x[j] = lds_read_b128(region + 512 * r + 16 * (c ^ (r & 15)));
+          if (add) y[j] = *(global_u32x4*)(D + (row0 + 64 * half + r) * ldd + col);
         }
 #pragma unroll
         for (int j = 0; j < 8; j++) {
           const int r = 2 * (j0 + j) + (lane >> 5);
-          *(global_u32x4*)(D + (row0 + 64 * half + r) * ldd + col) = (u32x4){x[j].x, x[j].y, x[j].z, x[j].w};
+          u32x4 o = {x[j].x, x[j].y, x[j].z, x[j].w};
+          if (add) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = __float_as_uint(__uint_as_float(o[e]) + __uint_as_float(y[j][e]));
+          }
+          *(global_u32x4*)(D + (row0 + 64 * half + r) * ldd + col) = o;
         }
       }
     } else {
@@ -293,13 +234,10 @@ __device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t 
         const int64_t row = row0 + 64 * half + r;
         if (row < M) {
           global_f32* p = (global_f32*)(D + row * ldd + col);
-          if (col + 3 < N) {
-            *(global_u32x4*)p = (u32x4){x.x, x.y, x.z, x.w};
-          } else {
-            if (col < N) p[0] = __uint_as_float(x.x);
-            if (col + 1 < N) p[1] = __uint_as_float(x.y);
-            if (col + 2 < N) p[2] = __uint_as_float(x.z);
-          }
+          const float xv[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (col + e < N) p[e] = add ? xv[e] + p[e] : xv[e];
         }
       }
     }

@@ -235,10 +235,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   const int wa = 128 * wm, wb = 128 * wn;
   const float sgn = a.negate ? -1.0f : 1.0f;
 
-  // accumulators start from s * D (or zero); D is read here, before the operand copies
+  // accumulators start from zero; the epilogue adds D when accumulating
   f32x16 acc[4][4];
-  if (ACC) gemm::load_acc(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc);
-  else gemm::zero_acc(acc);
+  gemm::zero_acc(acc);
 
   Ops o;
   const int64_t lda_b = a.lda / F::EPB, ldb_b = a.ldb / F::EPB;
@@ -404,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   }
   // every wave is done with LDS before the accumulators pass through it
   __syncthreads();
-  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w);
+  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, ACC);
 }
 
 }  // namespace

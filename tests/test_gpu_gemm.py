@@ -283,6 +283,31 @@ def test_block_scale_vs_oracle(O, fmt):
         assert np.isnan(D[:, N:]).all()
 
 
+# A larger grid (33 x 9 = 297 output tiles, more than one wave of workgroups) with a ragged
+# K tail after the full K tiles, checked element by element on one tile row (rows 256..511).
+LARGE_SHAPE = (8448, 2304, 2112)
+
+
+@pytest.mark.parametrize("fmt,neg_a,accum", [("e4m3", 0, 1), ("e2m1", 1, 0), ("e2m1", 0, 1)])
+def test_block_scale_large_grid_vs_oracle(O, fmt, neg_a, accum):
+    M, N, K = LARGE_SHAPE
+    g = mx_case(fmt, 77, M, N, K)
+    d0 = np.random.default_rng(5).standard_normal((M, N)).astype(np.float32)
+    say("mx large", fmt, M, N, K, neg_a, accum)
+    D = run_mx(M, N, K, fmt, g, d0 if accum else None, neg_a, 0, accum)
+    ref, bound = O.gemm_block_scale(M, N, K, fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], fmt, g["B"], g["ldb"],
+                                    g["SFB"], g["ld_sfb"], d0, N, neg_a, 0, accum, 256, 512)
+    g["K"] = K
+    if fmt == "e2m1":
+        assert O.check_gemm(D[256:512, :N], ref, bound, TOL_MX)[0] == 0
+    else:   # the fp8 window slack is costly to evaluate: 8192 points of those rows
+        rng = np.random.default_rng(6)
+        pm, pn = 256 + rng.integers(0, 256, 8192), rng.integers(0, N, 8192)
+        nb, worst = check_mx(O, fmt, g, D, ref[pm - 256, pn], bound[pm - 256, pn], pm, pn)
+        assert nb == 0, worst
+    assert np.isfinite(D[:, :N]).all()
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 def test_block_scale_exact_sums_bit_exact(O, fmt):
     # narrow scales and small codes: every partial sum is exact in float32

@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "add_one": ["k_tile.hip", "bsm_device.hpp"],
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_busy_bench_step.md")
 CALIB_BYTES = 1 << 30
 
 
@@ -66,6 +67,20 @@ def measured_traffic(kernel):
                 parts = line.split()
                 if len(parts) == 4 and parts[0] == "traffic:" and parts[1] == kernel:
                     return int(parts[2]) if parts[3] == source_hash(kernel) else None
+    except OSError:
+        return None
+    return None
+
+
+def measured_mfma(kernel):
+    """(MFMA busy fraction, clock GHz) from the committed counter summary, if it matches the code."""
+    try:
+        with open(MFMA_SUMMARY) as fh:
+            for line in fh:
+                # machine-readable rows: "mfma: <kernel> <busy fraction> <clock GHz> <source hash>"
+                parts = line.split()
+                if len(parts) == 5 and parts[0] == "mfma:" and parts[1] == kernel:
+                    return (float(parts[2]), float(parts[3])) if parts[4] == source_hash(kernel) else None
     except OSError:
         return None
     return None
@@ -256,6 +271,9 @@ def main():
         rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         per[name] = {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
                      "frac": round(rate / peak, 4), "work_per_launch": work}
+        mf = measured_mfma(name)
+        if mf is not None:   # counter figures of the same kernel sources (profiles/mfma_busy_bench_step.md)
+            per[name]["mfma_busy"], per[name]["clock_ghz"] = mf
         log(f"{name}: {ms:.4f} ms  {rate:.1f} {unit}  ({100 * rate / peak:.1f}% of {peak})")
     dom = max((n for n in per if n != "add_one"), key=lambda n: per[n]["ms"])
     d = per[dom]

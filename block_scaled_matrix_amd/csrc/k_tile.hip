@@ -329,7 +329,7 @@ struct Copy2D {
 };
 
 // A workgroup moves one row slice of 2^lg_nb horizontally adjacent boxes (the bf16 (128,
-// 64) box: 32 rows x 4 boxes, i.e. rows of 512 contiguous bytes, which HBM serves
+// 64) box: 16 rows x 8 boxes, i.e. rows of 1 KiB contiguous bytes, which HBM serves
 // markedly faster than the 128-byte rows of a single box at a power-of-two row pitch).
 // Lane l takes chunk column l % (nb cpr) (box (l % (nb cpr)) / cpr) of slice rows
 // l / (nb cpr) + k * rstep, k < 4. Each box keeps its own image region in LDS: the slice's
@@ -468,18 +468,18 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
     a.esize = g.esize; a.dtype = g.dtype; a.swizzle = g.swizzle; a.row_bytes = g.row_bytes;
     a.lg_cpr = 0;
     while ((1 << a.lg_cpr) < cpr) a.lg_cpr++;
-    // up to 4 boxes side by side per workgroup while a slice row stays within 64 chunks
-    // (at least 4 rows per pass) and the row of boxes has that many boxes
+    // up to 8 boxes side by side per workgroup while a slice row stays within 128 chunks
+    // (at least 2 rows per pass) and the row of boxes has that many boxes
     a.lg_nb = 0;
-    while (a.lg_nb < 2 && (2 * cpr << a.lg_nb) <= 64 && (int64_t(2) << a.lg_nb) <= (int64_t)o.tiles[1]) a.lg_nb++;
+    while (a.lg_nb < 3 && (2 * cpr << a.lg_nb) <= 128 && (int64_t(2) << a.lg_nb) <= (int64_t)o.tiles[1]) a.lg_nb++;
     const int rs = 4 * (256 >> (a.lg_cpr + a.lg_nb));      // rows per slice
     a.groups1 = (uint32_t)((o.tiles[1] + (1u << a.lg_nb) - 1) >> a.lg_nb);
     a.slices = (uint32_t)((g.box[0] + rs - 1) / rs);
     a.fill_word = g.esize == 1 ? g.fill_bits * 0x01010101u : (g.esize == 2 ? g.fill_bits * 0x00010001u : g.fill_bits);
     const int64_t wgs = (int64_t)o.tiles[0] * a.slices * a.groups1;
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-    // every box's slice region is rs * row_bytes = 16 KiB / 2^lg_nb, a whole number of
-    // swizzle periods (the swizzle stays inside aligned 2^(7 + mode)-byte windows)
+    // every box's slice region is rs * row_bytes = 16 KiB / 2^lg_nb >= 2 KiB, a whole number
+    // of swizzle periods (the swizzle stays inside aligned 2^(7 + mode)-byte windows)
     const size_t lds_bytes = (size_t)4 * 256 * 16;
     if (!dst_add)
       hipLaunchKernelGGL(k_box_copy2d<0>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);

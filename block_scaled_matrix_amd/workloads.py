@@ -27,6 +27,7 @@ SENTINEL_BF16 = 0x7FC1  # a NaN payload no kernel produces: marks bytes that mus
 
 # All E4M3 codes except the two NaN encodings 0x7F and 0xFF (OCP E4M3 "fn").
 FINITE_E4M3 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+FINITE_E5M2 = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], dtype=np.uint8)  # exponent field < 31
 
 
 def to_half_bits(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -72,14 +73,17 @@ def gemm_bf16(seed: int = 3, M: int = 8192, N: int = 8192, K: int = 8192):
             "a_major": "k", "b_major": "n", "accum": 1, "neg_a": 0, "neg_b": 0, "dtype": "bf16"}
 
 
-def mxfp8(seed: int = 4, M: int = 8192, N: int = 8192, K: int = 16384, exp_range: int = 4):
+def mxfp8(seed: int = 4, M: int = 8192, N: int = 8192, K: int = 16384, exp_range: int = 4, a_fmt: str = "e4m3",
+          b_fmt: str = "e4m3"):
+    """Uniform random finite codes of the operand formats (E4M3 or E5M2) and scales 127 +- exp_range."""
     rng = np.random.default_rng(seed)
-    a = FINITE_E4M3[rng.integers(0, FINITE_E4M3.size, (M, K), dtype=np.int16)]
-    b = FINITE_E4M3[rng.integers(0, FINITE_E4M3.size, (N, K), dtype=np.int16)]
+    codes = {"e4m3": FINITE_E4M3, "e5m2": FINITE_E5M2}
+    a = codes[a_fmt][rng.integers(0, codes[a_fmt].size, (M, K), dtype=np.int16)]
+    b = codes[b_fmt][rng.integers(0, codes[b_fmt].size, (N, K), dtype=np.int16)]
     sfa = (127 + rng.integers(-exp_range, exp_range + 1, (M, K // 32), dtype=np.int16)).astype(np.uint8)
     sfb = (127 + rng.integers(-exp_range, exp_range + 1, (N, K // 32), dtype=np.int16)).astype(np.uint8)
     return {"M": M, "N": N, "K": K, "A": a, "B": b, "SFA": sfa, "SFB": sfb, "lda": K, "ldb": K,
-            "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": "e4m3", "accum": 0, "neg_a": 0, "neg_b": 0}
+            "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": a_fmt, "b_fmt": b_fmt, "accum": 0, "neg_a": 0, "neg_b": 0}
 
 
 def mxfp4(seed: int = 5, M: int = 16384, N: int = 8192, K: int = 8192, exp_range: int = 6):

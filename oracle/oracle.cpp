@@ -13,7 +13,7 @@
 //   [LDM] "ldmatrix / stmatrix"
 //   [TOE] "Tile Operands and Execution"
 //   [MMA] "tcgen05.mma"
-// Storage formats the pages only name (e4m3, e2m1, the 8-bit scale) follow the
+// Storage formats the pages only name (e4m3, e5m2, e2m1, the 8-bit scale) follow the
 // public OCP Microscaling Formats (MX) v1.0 specification, section 5.
 //
 // Every function returns 0 on success and a negative value on an argument it
@@ -37,7 +37,7 @@ extern "C" {
 // Storage-format codes of this oracle (its own numbering; the Python wrapper maps names).
 enum OracleDtype {
   OD_U8 = 0, OD_U16 = 1, OD_U32 = 2, OD_F16 = 3, OD_BF16 = 4, OD_F32 = 5,
-  OD_E4M3 = 6, OD_E2M1 = 7, OD_E8M0 = 8
+  OD_E4M3 = 6, OD_E2M1 = 7, OD_E8M0 = 8, OD_E5M2 = 9
 };
 
 int oracle_num_threads(void) {
@@ -91,6 +91,17 @@ double oracle_dec_e4m3(uint8_t c) {
   if (e == 15 && m == 7) v = NAN;
   else if (e == 0) v = std::ldexp((double)m, -9);
   else v = std::ldexp(8.0 + m, e - 10);
+  return s ? -v : v;
+}
+
+// OCP E5M2: s.eeeee.mm, bias 15, IEEE-like: exponent 31 is infinity (m == 0) or NaN,
+// subnormals m * 2^-16, largest finite 57344 (OCP MX v1.0, section 5.3).
+double oracle_dec_e5m2(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 2) & 31, m = c & 3;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = std::ldexp((double)m, -16);
+  else v = std::ldexp(4.0 + m, e - 17);
   return s ? -v : v;
 }
 
@@ -154,6 +165,7 @@ int oracle_decode_array(int dtype, const void* src, int64_t n, double* out) {
       case OD_BF16: { uint16_t v; std::memcpy(&v, b + 2 * i, 2); out[i] = oracle_dec_bf16(v); break; }
       case OD_F32: { uint32_t v; std::memcpy(&v, b + 4 * i, 4); out[i] = oracle_dec_f32(v); break; }
       case OD_E4M3: out[i] = oracle_dec_e4m3(b[i]); break;
+      case OD_E5M2: out[i] = oracle_dec_e5m2(b[i]); break;
       case OD_E2M1: out[i] = oracle_dec_e2m1((b[i / 2] >> (4 * (i & 1))) & 15); break;
       case OD_E8M0: out[i] = oracle_dec_e8m0(b[i]); break;
       default: return -1;
@@ -178,7 +190,7 @@ int64_t oracle_swizzle(int64_t off, int mode) {
 
 static int elem_size(int dtype) {
   switch (dtype) {
-    case OD_U8: case OD_E4M3: case OD_E8M0: return 1;
+    case OD_U8: case OD_E4M3: case OD_E5M2: case OD_E8M0: return 1;
     case OD_U16: case OD_F16: case OD_BF16: return 2;
     case OD_U32: case OD_F32: return 4;
     default: return 0;  // E2M1 is sub-byte: box copies treat packed fp4 as U8
@@ -193,6 +205,7 @@ static int nan_bits(int dtype, uint8_t* out) {
     case OD_F16: { uint16_t v = 0x7E00; std::memcpy(out, &v, 2); return 0; }
     case OD_BF16: { uint16_t v = 0x7FC0; std::memcpy(out, &v, 2); return 0; }
     case OD_E4M3: out[0] = 0x7F; return 0;
+    case OD_E5M2: out[0] = 0x7E; return 0;  // exponent 31, quiet-NaN mantissa (the f16 0x7E00 top byte)
     default: return -1;
   }
 }
@@ -468,11 +481,14 @@ int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int dtype,
 // elements starting at k = 0; the operand value is decode(element) * 2^(s-127).
 // K-major storage only: element (r,k) at index r*ld + k; for packed E2M1 that
 // index selects byte idx/2 and the low nibble for even idx.
+static bool mx_fmt(int f) { return f == OD_E4M3 || f == OD_E5M2 || f == OD_E2M1; }
+
 static double load_op_scaled(int fmt, const uint8_t* p, int64_t ld, const uint8_t* sf,
                              int64_t ld_sf, int64_t r, int64_t k) {
   int64_t idx = r * ld + k;
   double v;
   if (fmt == OD_E4M3) v = oracle_dec_e4m3(p[idx]);
+  else if (fmt == OD_E5M2) v = oracle_dec_e5m2(p[idx]);
   else v = oracle_dec_e2m1((p[idx >> 1] >> (4 * (idx & 1))) & 15);
   return v * oracle_dec_e8m0(sf[r * ld_sf + k / 32]);
 }
@@ -482,7 +498,7 @@ int oracle_gemm_block_scale(int64_t M, int64_t N, int64_t K,
                             int b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
                             const float* D0, int64_t ldd, int neg_a, int neg_b, int accum,
                             int64_t m_begin, int64_t m_end, double* ref, double* bound) {
-  if ((a_fmt != OD_E4M3 && a_fmt != OD_E2M1) || (b_fmt != OD_E4M3 && b_fmt != OD_E2M1)) return -1;
+  if (!mx_fmt(a_fmt) || !mx_fmt(b_fmt)) return -1;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || m_begin < 0 || m_end > M || m_begin > m_end) return -2;
   if (accum && !D0) return -4;
   const uint8_t* pa = (const uint8_t*)A;
@@ -512,7 +528,7 @@ int oracle_gemm_block_scale_points(int64_t M, int64_t N, int64_t K,
                                    const float* D0, int64_t ldd, int neg_a, int neg_b, int accum,
                                    const int64_t* pm, const int64_t* pn, int64_t npts,
                                    double* ref, double* bound) {
-  if ((a_fmt != OD_E4M3 && a_fmt != OD_E2M1) || (b_fmt != OD_E4M3 && b_fmt != OD_E2M1)) return -1;
+  if (!mx_fmt(a_fmt) || !mx_fmt(b_fmt)) return -1;
   if (K % 32 != 0) return -2;
   if (accum && !D0) return -4;
   for (int64_t i = 0; i < npts; i++) if (pm[i] < 0 || pm[i] >= M || pn[i] < 0 || pn[i] >= N) return -2;

@@ -17,8 +17,8 @@ _SRC = os.path.join(_HERE, "oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # The oracle's own storage-format codes (see OracleDtype in oracle.cpp).
-DT = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "e4m3": 6, "e2m1": 7, "e8m0": 8}
-ESIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e8m0": 1}
+DT = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "e4m3": 6, "e2m1": 7, "e8m0": 8, "e5m2": 9}
+ESIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e8m0": 1, "e5m2": 1}
 
 
 def build(force: bool = True) -> str:

@@ -103,6 +103,21 @@ def test_box_nan_fill_and_fill_count(O):
         O.box_load(np.zeros(16, np.uint32), "u32", (16,), (4,), (4,), (1,), (0,), 0, 1)  # no NaN in u32
 
 
+def test_box_nan_fill_e5m2_and_e4m3(O):
+    """One-byte float formats: the fill byte decodes to NaN (torch's OCP decoders) and, for E5M2,
+    is the top byte of binary16's canonical quiet NaN."""
+    import torch
+    x = np.arange(24, dtype=np.uint8).reshape(3, 8)
+    for dt, tdt in (("e5m2", torch.float8_e5m2), ("e4m3", torch.float8_e4m3fn)):
+        img = O.box_load(x, dt, (3, 8), (8, 1), (4, 16), (1, 1), (1, 0), 0, 1)[:64].reshape(4, 16)
+        assert np.array_equal(img[:2, :8], x[1:3])                     # in range: the bytes themselves
+        fill = np.concatenate([img[:2, 8:].ravel(), img[2:].ravel()])
+        assert len(set(fill.tolist())) == 1
+        assert torch.isnan(torch.from_numpy(fill[:1].copy()).view(tdt).to(torch.float32)).all()
+    assert O.box_load(x, "e5m2", (3, 8), (8, 1), (1, 16), (1, 1), (0, 0), 0, 1)[8] == \
+        (np.array([np.nan], np.float16).view(np.uint16)[0] >> 8)
+
+
 # ----------------------------------------------------------------------------- store / reduce
 def test_load_store_identity_and_oob_untouched(O):
     rng = np.random.default_rng(21)

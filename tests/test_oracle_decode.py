@@ -1,7 +1,8 @@
 """Pins of the oracle's decoders and encoders against independent libraries and closed forms.
 
 Decoders are checked code by code against torch's / numpy's own conversions (for
-e4m3 and e8m0: torch.float8_e4m3fn / float8_e8m0fnu, the OCP formats), and the
+e4m3, e5m2 and e8m0: torch.float8_e4m3fn / float8_e5m2 / float8_e8m0fnu, the OCP formats;
+e5m2 also against numpy's binary16, whose top byte it is), and the
 e2m1 table against the value list of the OCP MX v1.0 specification (section 5.3.3).
 Encoders (round to nearest even) are checked against numpy / torch float64 casts on
 values chosen to hit ties, subnormals, carries and overflow.
@@ -25,6 +26,18 @@ def test_e4m3_all_codes_vs_torch(O):
     assert _same(got, ref)
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
     assert np.isfinite(got).sum() == 254
+
+
+def test_e5m2_all_codes_vs_torch_and_f16_top_byte(O):
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.decode("e5m2", codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert _same(got, ref)
+    # E5M2 is binary16 with the low 8 fraction bits dropped: code c is the half float c << 8
+    half = (codes.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    assert _same(got, half)
+    assert got[0x7B] == 57344.0 and got[0x01] == 2.0 ** -16 and got[0x7C] == np.inf and got[0xFC] == -np.inf
+    assert np.isnan(got[0x7E]) and np.isfinite(got).sum() == 248
 
 
 def test_e8m0_all_codes_vs_torch_and_closed_form(O):

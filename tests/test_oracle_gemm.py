@@ -112,9 +112,10 @@ E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -
 
 
 def mx_vals(raw, fmt, rows, K):
-    """Decoded element values via torch (e4m3) or the OCP table (e2m1), low nibble first."""
-    if fmt == "e4m3":
-        return torch.from_numpy(raw.reshape(rows, K)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    """Decoded element values via torch (e4m3, e5m2) or the OCP table (e2m1), low nibble first."""
+    if fmt in ("e4m3", "e5m2"):
+        t = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+        return torch.from_numpy(raw.reshape(rows, K)).view(t).to(torch.float64).numpy()
     r = raw.reshape(rows, K // 2)
     out = np.empty((rows, K))
     out[:, 0::2] = E2M1[r & 15]
@@ -139,6 +140,25 @@ def test_block_scale_vs_numpy_brute_force(O, fmt):
                                         K // 32, d0, N, neg_a, neg_b, accum)
         av = scaled(mx_vals(g["A"], fmt, M, K), g["SFA"])
         bv = scaled(mx_vals(g["B"], fmt, N, K), g["SFB"])
+        exp = (d0.astype(np.float64) if accum else 0.0) + (-1.0) ** (neg_a + neg_b) * (av @ bv.T)
+        np.testing.assert_allclose(ref, exp, rtol=0, atol=1e-12 * (1 + (np.abs(av) @ np.abs(bv).T).max()))
+        np.testing.assert_allclose(bound, np.abs(av) @ np.abs(bv).T, rtol=1e-12)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")])
+def test_block_scale_e5m2_vs_numpy_brute_force(O, a_fmt, b_fmt):
+    """E5M2 operands, alone and mixed with E4M3 (8-bit operands of either kind pair up)."""
+    rng = np.random.default_rng(17)
+    for trial in range(6):
+        M, N = int(rng.choice(SIZES)), int(rng.choice(SIZES))
+        K = int(rng.choice([32, 64, 96, 160]))
+        neg_a, neg_b, accum = (int(v) for v in rng.integers(0, 2, 3))
+        g = W.mxfp8(seed=40 + trial, M=M, N=N, K=K, a_fmt=a_fmt, b_fmt=b_fmt)
+        d0 = rng.standard_normal((M, N)).astype(np.float32)
+        ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], K, g["SFA"], K // 32, b_fmt, g["B"], K, g["SFB"],
+                                        K // 32, d0, N, neg_a, neg_b, accum)
+        av = scaled(mx_vals(g["A"], a_fmt, M, K), g["SFA"])
+        bv = scaled(mx_vals(g["B"], b_fmt, N, K), g["SFB"])
         exp = (d0.astype(np.float64) if accum else 0.0) + (-1.0) ** (neg_a + neg_b) * (av @ bv.T)
         np.testing.assert_allclose(ref, exp, rtol=0, atol=1e-12 * (1 + (np.abs(av) @ np.abs(bv).T).max()))
         np.testing.assert_allclose(bound, np.abs(av) @ np.abs(bv).T, rtol=1e-12)

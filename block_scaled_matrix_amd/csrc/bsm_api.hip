@@ -32,20 +32,23 @@ int hip_fail(hipError_t e, const char* what) {
 
 int elem_size(int32_t dt) {
   switch (dt) {
-    case BSM_U8: case BSM_E4M3: case BSM_E8M0: return 1;
+    case BSM_U8: case BSM_E4M3: case BSM_E5M2: case BSM_E8M0: return 1;
     case BSM_U16: case BSM_F16: case BSM_BF16: return 2;
     case BSM_U32: case BSM_F32: return 4;
     default: return 0;
   }
 }
 
-bool has_nan(int32_t dt) { return dt == BSM_F32 || dt == BSM_F16 || dt == BSM_BF16 || dt == BSM_E4M3; }
+bool has_nan(int32_t dt) {
+  return dt == BSM_F32 || dt == BSM_F16 || dt == BSM_BF16 || dt == BSM_E4M3 || dt == BSM_E5M2;
+}
 
 uint32_t nan_bits(int32_t dt) {
   switch (dt) {
     case BSM_F32: return 0x7FC00000u;
     case BSM_F16: return 0x7E00u;
     case BSM_BF16: return 0x7FC0u;
+    case BSM_E5M2: return 0x7Eu;
     default: return 0x7Fu;  // E4M3
   }
 }
@@ -277,9 +280,11 @@ int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const v
   int rc;
   if ((rc = check_flag(neg_a, "neg_a")) || (rc = check_flag(neg_b, "neg_b")) || (rc = check_flag(accum, "accum")))
     return rc;
-  if ((a_fmt != BSM_E4M3 && a_fmt != BSM_E2M1) || (b_fmt != BSM_E4M3 && b_fmt != BSM_E2M1))
-    return fail(BSM_E_DTYPE, "a_fmt %d / b_fmt %d: block-scaled GEMM takes E4M3 or E2M1", a_fmt, b_fmt);
-  if (a_fmt != b_fmt) return fail(BSM_E_DTYPE, "mixed operand formats (%d, %d) are not supported", a_fmt, b_fmt);
+  auto mx = [](int32_t f) { return f == BSM_E4M3 || f == BSM_E5M2 || f == BSM_E2M1; };
+  if (!mx(a_fmt) || !mx(b_fmt))
+    return fail(BSM_E_DTYPE, "a_fmt %d / b_fmt %d: block-scaled GEMM takes E4M3, E5M2 or E2M1", a_fmt, b_fmt);
+  if ((a_fmt == BSM_E2M1) != (b_fmt == BSM_E2M1))
+    return fail(BSM_E_DTYPE, "fp4 operand mixed with an fp8 one (%d, %d) is not supported", a_fmt, b_fmt);
   if (M < 0 || N < 0 || K < 0 || M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
     return fail(BSM_E_SHAPE, "M, N, K = %lld, %lld, %lld out of range", (long long)M, (long long)N, (long long)K);
   if (K % 32) return fail(BSM_E_SHAPE, "K = %lld is not a multiple of the 32-element scale block", (long long)K);
@@ -307,7 +312,7 @@ int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const v
       return fail(BSM_E_ALIAS, "an operand or scale tensor overlaps D");
   }
   bsm::GemmArgs g{};
-  g.M = M; g.N = N; g.K = K; g.dtype = a_fmt;
+  g.M = M; g.N = N; g.K = K; g.dtype = a_fmt; g.dtype_b = b_fmt;
   g.A = A; g.lda = lda; g.a_kmajor = 1;
   g.B = B; g.ldb = ldb; g.b_kmajor = 1;
   g.SFA = SFA; g.ld_sfa = ld_sfa; g.SFB = SFB; g.ld_sfb = ld_sfb;

@@ -40,7 +40,8 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
 
 struct GemmArgs {
   int64_t M, N, K;
-  int32_t dtype;        // BSM_F16 / BSM_BF16 (dense) or BSM_E4M3 / BSM_E2M1 (block scaled)
+  int32_t dtype;        // BSM_F16 / BSM_BF16 (dense) or A's BSM_E4M3 / BSM_E5M2 / BSM_E2M1 (block scaled)
+  int32_t dtype_b;      // block scaled: B's format (0 for dense)
   const void* A; int64_t lda; int32_t a_kmajor;
   const void* B; int64_t ldb; int32_t b_kmajor;
   const uint8_t* SFA; int64_t ld_sfa;

@@ -1,4 +1,4 @@
-// k_gemm_mx.hip - block-scaled GEMM (MXFP8 E4M3 / MXFP4 E2M1 with E8M0 scales per 32
+// k_gemm_mx.hip - block-scaled GEMM (MXFP8 E4M3 or E5M2 / MXFP4 E2M1 with E8M0 scales per 32
 // K elements) D = s * A * B^T (+ D) on gfx950 v_mfma_scale_f32_32x32x64_f8f6f4.
 //
 // Semantics ("tcgen05.mma": Weight-stationary and block scaling, Call parameters;
@@ -161,7 +161,9 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wa, int
   for (int r = 0; r < (FMT == 4 ? 8 : 16); r++) read_frag<FMT>(st, s, r, wa, wb, lane, f);
 }
 
-template <int FMT, int SEL>
+// FMT: the operand layout (0: one byte per element, 4: fp4); CA, CB: the MFMA format codes
+// of A and B (0 E4M3, 1 E5M2, 4 E2M1). The MFMA takes B first (cbsz = B's code).
+template <int FMT, int CA, int CB, int SEL>
 __device__ __forceinline__ f32x16 mfma_sc(const uint4 (&b)[2], const uint4 (&a)[2], f32x16 c, uint32_t sb,
                                           uint32_t sa) {
   i32x8 av, bv;
@@ -174,7 +176,7 @@ __device__ __forceinline__ f32x16 mfma_sc(const uint4 (&b)[2], const uint4 (&a)[
     bv[4] = b[1].x; bv[5] = b[1].y; bv[6] = b[1].z; bv[7] = b[1].w;
     av[4] = a[1].x; av[5] = a[1].y; av[6] = a[1].z; av[7] = a[1].w;
   }
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, FMT, FMT, SEL, (int)sb, SEL, (int)sa);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, c, CB, CA, SEL, (int)sb, SEL, (int)sa);
 }
 
 template <int FMT>
@@ -195,14 +197,14 @@ __device__ __forceinline__ void pin_frags(Frags& f) {
 // LDS reads, copies and barriers issue while the matrix pipe is busy. Empty asm
 // "rewrites" of each accumulator before and after its MFMA fix the order of the MFMAs and
 // the side operations (all volatile) without any hardware wait.
-template <int FMT, int S, typename Side>
+template <int FMT, int CA, int CB, int S, typename Side>
 __device__ __forceinline__ void mfma_step_il(const Frags& f, const uint32_t (&sa)[4][2], const uint32_t (&sb)[4][2],
                                              f32x16 (&acc)[4][4], Side side) {
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const int mt = i >> 2, nt = i & 3;
     asm volatile("" : "+a"(acc[mt][nt])::"memory");
-    acc[mt][nt] = mfma_sc<FMT, 2 * (S & 1)>(f.bf[nt], f.af[mt], acc[mt][nt], sb[nt][S >> 1], sa[mt][S >> 1]);
+    acc[mt][nt] = mfma_sc<FMT, CA, CB, 2 * (S & 1)>(f.bf[nt], f.af[mt], acc[mt][nt], sb[nt][S >> 1], sa[mt][S >> 1]);
     asm volatile("" : "+a"(acc[mt][nt])::"memory");
     side(i);
   }
@@ -222,7 +224,7 @@ __device__ __forceinline__ void shift_scales(const uint32_t (&ra)[4][2], const u
     }
 }
 
-template <int FMT, bool ACC>
+template <int FMT, int CA, int CB, bool ACC>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int tiles_n) {
   typedef Fmt<FMT> F;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
       // 24..62; barrier at slot 48 (12 copies issued); the next tile's step-0 fragments
       // and scales at slots 48..55
       pin_frags<4>(f0);
-      mfma_step_il<4, 0>(f0, sa, sb, acc, [&](int i) {
+      mfma_step_il<4, CA, CB, 0>(f0, sa, sb, acc, [&](int i) {
         if (i < 12) {
 #pragma unroll
           for (int rr = 0; rr < 2; rr++) {
@@ -316,16 +318,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
         }
       });
       pin_frags<4>(f1);
-      mfma_step_il<4, 1>(f1, sa, sb, acc, [&](int i) {
+      mfma_step_il<4, CA, CB, 1>(f1, sa, sb, acc, [&](int i) {
         if (i == 7) gemm::lds_barrier();
         if (i >= 8 && (i & 1) == 0) copy((i - 8) >> 1);
       });
       pin_frags<4>(f2);
-      mfma_step_il<4, 2>(f2, sa, sb, acc, [&](int i) {
+      mfma_step_il<4, CA, CB, 2>(f2, sa, sb, acc, [&](int i) {
         if ((i & 1) == 0) copy(4 + (i >> 1));
       });
       pin_frags<4>(f3);
-      mfma_step_il<4, 3>(f3, sa, sb, acc, [&](int i) {
+      mfma_step_il<4, CA, CB, 3>(f3, sa, sb, acc, [&](int i) {
         if (i == 0) gemm::stage_barrier<12>();
         if ((i & 1) == 0) copy(12 + (i >> 1));
         if (i == 0) read_scales<4>(lds, kt + 1, wa, wb, lane, ra, rb);
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
       // barrier after slot 9; copies at slots 10..27; barrier at slot 20 (10 copies
       // issued); the next tile's step-0 fragments and scales at slots 20..27
       pin_frags<0>(f0);
-      mfma_step_il<0, 0>(f0, sa, sb, acc, [&](int i) {
+      mfma_step_il<0, CA, CB, 0>(f0, sa, sb, acc, [&](int i) {
         if (i < 4) {
 #pragma unroll
           for (int rr = 0; rr < 4; rr++) read_frag<0>(st, 1, 4 * i + rr, wa, wb, lane, f1);
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
         if (i >= 10) copy(i - 10);
       });
       pin_frags<0>(f1);
-      mfma_step_il<0, 1>(f1, sa, sb, acc, [&](int i) {
+      mfma_step_il<0, CA, CB, 1>(f1, sa, sb, acc, [&](int i) {
         if (i == 4) gemm::stage_barrier<10>();
         if (i < 12) copy(6 + i);
         if (i == 4) read_scales<0>(lds, kt + 1, wa, wb, lane, ra, rb);
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
         sa[t][0] = __builtin_amdgcn_readfirstlane(s >> 1) ? ra[t][1] >> sh : ra[t][0] >> sh;
         sb[t][0] = __builtin_amdgcn_readfirstlane(s >> 1) ? rb[t][1] >> sh : rb[t][0] >> sh;
       }
-      mfma_step_il<FMT, 0>(f0, sa, sb, acc, [](int) {});
+      mfma_step_il<FMT, CA, CB, 0>(f0, sa, sb, acc, [](int) {});
     }
   }
   // every wave is done with LDS before the accumulators pass through it
@@ -417,13 +419,19 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = (int)tm64, tiles_n = (int)tn64;
   const dim3 grid(tiles_m * tiles_n);
-  if (a.dtype == BSM_E2M1) {
-    if (a.accum) hipLaunchKernelGGL((k_gemm_mx<4, true>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((k_gemm_mx<4, false>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
-  } else {
-    if (a.accum) hipLaunchKernelGGL((k_gemm_mx<0, true>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((k_gemm_mx<0, false>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);
-  }
+  // MFMA format codes: E4M3 0, E5M2 1, E2M1 4 (fp4 pairs only with fp4)
+#define BSM_MX_LAUNCH(FMT, CA, CB)                                                                              \
+  do {                                                                                                            \
+    if (a.accum) hipLaunchKernelGGL((k_gemm_mx<FMT, CA, CB, true>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);  \
+    else hipLaunchKernelGGL((k_gemm_mx<FMT, CA, CB, false>), grid, dim3(256), 0, st, a, tiles_m, tiles_n);         \
+  } while (0)
+  const bool a5 = a.dtype == BSM_E5M2, b5 = a.dtype_b == BSM_E5M2;
+  if (a.dtype == BSM_E2M1) BSM_MX_LAUNCH(4, 4, 4);
+  else if (!a5 && !b5) BSM_MX_LAUNCH(0, 0, 0);
+  else if (a5 && b5) BSM_MX_LAUNCH(0, 1, 1);
+  else if (a5) BSM_MX_LAUNCH(0, 1, 0);
+  else BSM_MX_LAUNCH(0, 0, 1);
+#undef BSM_MX_LAUNCH
   return hipGetLastError();
 }
 

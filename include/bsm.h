@@ -36,7 +36,8 @@ typedef enum bsm_dtype {
   BSM_F32 = 5,   /* IEEE binary32 */
   BSM_E4M3 = 6,  /* OCP fp8 E4M3 ("fn": no infinities, 0x7F/0xFF NaN, max 448) */
   BSM_E2M1 = 7,  /* OCP fp4 E2M1, two per byte, even element in the low nibble */
-  BSM_E8M0 = 8   /* OCP 8-bit power-of-two scale: 2^(code-127), 0xFF NaN */
+  BSM_E8M0 = 8,  /* OCP 8-bit power-of-two scale: 2^(code-127), 0xFF NaN */
+  BSM_E5M2 = 9   /* OCP fp8 E5M2 (IEEE-like: infinities, NaNs; max 57344) */
 } bsm_dtype;
 
 /* Status codes: one per violated rule. */
@@ -79,7 +80,8 @@ typedef struct bsm_tensor {
  *   box:             extents outer to inner, each 1..256;
  *   element_strides: sampling steps outer to inner, each 1..8, the inner one 1;
  *   swizzle:         0/1/2/3 = none / 32 B / 64 B / 128 B;
- *   oob_fill:        0 = zero, 1 = canonical NaN (F32, F16, BF16, E4M3 only).
+ *   oob_fill:        0 = zero, 1 = canonical NaN (F32, F16, BF16, E4M3, E5M2 only; the
+ *                    E5M2 NaN is 0x7E, the top byte of binary16's 0x7E00).
  * The image has extents n_i = ceil(box_i / element_strides_i), is compact row-major
  * (outer to inner) before swizzling, and image element j holds global coordinate
  * coords + j * element_strides (the fill value if any coordinate is outside
@@ -161,7 +163,8 @@ int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab,
  *   D[m,n] = (accum ? D[m,n] : 0) + s * sum_k A(m,k) * B(n,k), float32 accumulation.
  * One E8M0 scale per 32 consecutive K elements (OCP MX block size 32); a scale code
  * of 0xFF (NaN) makes every product of its block NaN.
- *   a_fmt, b_fmt: BSM_E4M3 or BSM_E2M1, equal (mixed formats are rejected);
+ *   a_fmt, b_fmt: both BSM_E2M1, or both 8-bit (BSM_E4M3 and BSM_E5M2 in any pairing);
+ *            fp4 mixed with fp8 is rejected;
  *   lda, ldb in elements; E2M1 element index i is the (i & 1) nibble of byte i/2
  *   (low nibble first); rows 16-byte aligned (lda bytes a multiple of 16);
  *   K a multiple of 32; ld_sfa >= K/32, ld_sfb >= K/32, both multiples of 4, SFA and

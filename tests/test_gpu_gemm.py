@@ -19,15 +19,17 @@ TOL_DENSE, TOL_MX = 2e-3, 1e-5
 WINDOW_BITS = 13
 
 
-def e4m3_window_slack(O, g, pm, pn):
-    """Extra error allowance for E4M3 operands: gfx950's fp8 MFMA sums the 32 products of
+def fp8_window_slack(O, g, pm, pn):
+    """Extra error allowance for 8-bit operands (E4M3, E5M2; measured with E4M3, applied to every
+    8-bit pairing since they go through the same instruction): gfx950's fp8 MFMA sums the 32 products of
     each scale block on a grid of 2^(E-13), E the exponent of the block's largest
     |product| (measured on the device: a product 2^-13 below the block maximum is kept,
     2^-14 below is dropped; sums across blocks and with the accumulator are float32).
     Each product can lose at most min(|p|, grid). Returns that bound per point."""
     K = g["K"]
-    A = O.decode("e4m3", g["A"]).reshape(-1, g["lda"])[:, :K] * np.repeat(np.exp2(g["SFA"][:, :K // 32] - 127.0), 32, 1)
-    B = O.decode("e4m3", g["B"]).reshape(-1, g["ldb"])[:, :K] * np.repeat(np.exp2(g["SFB"][:, :K // 32] - 127.0), 32, 1)
+    af, bf = g.get("fmt", "e4m3"), g.get("b_fmt", g.get("fmt", "e4m3"))
+    A = O.decode(af, g["A"]).reshape(-1, g["lda"])[:, :K] * np.repeat(np.exp2(g["SFA"][:, :K // 32] - 127.0), 32, 1)
+    B = O.decode(bf, g["B"]).reshape(-1, g["ldb"])[:, :K] * np.repeat(np.exp2(g["SFB"][:, :K // 32] - 127.0), 32, 1)
     out = np.empty(len(pm))
     for c in range(0, len(pm), 256):
         p = np.abs(A[pm[c:c + 256]] * B[pn[c:c + 256]]).reshape(-1, K // 32, 32)
@@ -46,8 +48,8 @@ def check_mx(O, fmt, g, D, ref, bound, pm=None, pn=None):
     else:
         d, r, b = D[pm, pn], ref, bound
     tol = TOL_MX * b + np.ldexp(np.abs(r), -24)
-    if fmt == "e4m3":
-        tol = tol + e4m3_window_slack(O, g, pm, pn)
+    if fmt in ("e4m3", "e5m2"):
+        tol = tol + fp8_window_slack(O, g, pm, pn)
     err = np.abs(d.astype(np.float64) - r)
     bad = ~(err <= tol) & ~(np.isnan(d) & np.isnan(r))
     return int(bad.sum()), float(np.max(err / np.maximum(b, 1e-300)))
@@ -228,13 +230,13 @@ def test_fragment_loads_vs_oracle_ldmatrix_image(O, major):
 
 
 # ----------------------------------------------------------------------------- block scaled
-def run_mx(M, N, K, fmt, g, D0=None, neg_a=0, neg_b=0, accum=0):
+def run_mx(M, N, K, fmt, g, D0=None, neg_a=0, neg_b=0, accum=0, b_fmt=None):
     ldd = (N + 3) // 4 * 4
     d = np.full((M, ldd), np.nan, np.float32)
     if D0 is not None:
         d[:, :N] = D0
     dD = dev_f32(d)
-    bsm.bsm_gemm_block_scale(M, N, K, fmt, dev(g["A"]), g["lda"], dev(g["SFA"]), g["ld_sfa"], fmt, dev(g["B"]),
+    bsm.bsm_gemm_block_scale(M, N, K, fmt, dev(g["A"]), g["lda"], dev(g["SFA"]), g["ld_sfa"], b_fmt or fmt, dev(g["B"]),
                              g["ldb"], dev(g["SFB"]), g["ld_sfb"], dD, ldd, neg_a, neg_b, accum)
     return dD.cpu().numpy()
 
@@ -246,8 +248,11 @@ def pad_scales(sf, ld):
     return out
 
 
-def mx_case(fmt, seed, M, N, K, exp_range=4, ld_pad=0):
-    g = (W.mxfp8 if fmt == "e4m3" else W.mxfp4)(seed=seed, M=M, N=N, K=K, exp_range=exp_range)
+def mx_case(fmt, seed, M, N, K, exp_range=4, ld_pad=0, b_fmt=None):
+    if fmt == "e2m1":
+        g = W.mxfp4(seed=seed, M=M, N=N, K=K, exp_range=exp_range)
+    else:
+        g = W.mxfp8(seed=seed, M=M, N=N, K=K, exp_range=exp_range, a_fmt=fmt, b_fmt=b_fmt or fmt)
     if ld_pad:
         epb = 2 if fmt == "e2m1" else 1
         lda = K + ld_pad
@@ -306,6 +311,40 @@ def test_block_scale_large_grid_vs_oracle(O, fmt, neg_a, accum):
         nb, worst = check_mx(O, fmt, g, D, ref[pm - 256, pn], bound[pm - 256, pn], pm, pn)
         assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")])
+def test_block_scale_e5m2_vs_oracle(O, a_fmt, b_fmt):
+    """E5M2 operands, alone and paired with E4M3 (the MFMA takes a format code per operand)."""
+    for i, (M, N, K) in enumerate([(9, 17, 64), (300, 260, 288), (130, 513, 512), (64, 96, 1056), (256, 256, 128)]):
+        neg_a, neg_b, accum = i & 1, (i >> 1) & 1, (i >> 2) & 1
+        g = mx_case(a_fmt, 50 + i, M, N, K, ld_pad=64 if i % 3 == 2 else 0, b_fmt=b_fmt)
+        d0 = np.random.default_rng(i).standard_normal((M, N)).astype(np.float32)
+        say("mx e5m2", a_fmt, b_fmt, M, N, K, neg_a, neg_b, accum)
+        D = run_mx(M, N, K, a_fmt, g, d0 if accum else None, neg_a, neg_b, accum, b_fmt=b_fmt)
+        ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
+                                        g["ldb"], g["SFB"], g["ld_sfb"], d0, N, neg_a, neg_b, accum)
+        g["K"] = K
+        nb, worst = check_mx(O, a_fmt, g, D, ref, bound)
+        assert nb == 0, (M, N, K, worst)
+        assert np.isnan(D[:, N:]).all()
+
+
+def test_block_scale_e5m2_infinities(O):
+    """An E5M2 infinity in row 3 of A makes row 3 of D infinite with the sign of each product
+    (every B element of that K column is a nonzero finite value), as in the oracle."""
+    M, N, K = 8, 24, 64
+    g = mx_case("e5m2", 61, M, N, K)
+    A = g["A"].reshape(M, -1)
+    A[3, 5] = 0x7C                                           # +inf
+    B = g["B"].reshape(N, -1)
+    B[:, 5] = np.where((B[:, 5] & 0x7F) == 0, 0x3C, B[:, 5])  # no zero (or -0) in column 5
+    D = run_mx(M, N, K, "e5m2", g)
+    ref, _ = O.gemm_block_scale(M, N, K, "e5m2", g["A"], g["lda"], g["SFA"], g["ld_sfa"], "e5m2", g["B"], g["ldb"],
+                                g["SFB"], g["ld_sfb"])
+    assert np.isinf(ref[3]).all()
+    assert np.array_equal(D[3, :N], ref[3].astype(np.float32))
+    assert np.isfinite(np.delete(D[:, :N], 3, 0)).all()
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])

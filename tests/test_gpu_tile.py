@@ -14,7 +14,7 @@ from gpu_util import dev, dev_like, host, say
 pytestmark = pytest.mark.gpu
 
 NPDT = {"u8": np.uint8, "u16": np.uint16, "u32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f32": np.uint32,
-        "e4m3": np.uint8}
+        "e4m3": np.uint8, "e5m2": np.uint8}
 
 
 def test_add_one_pages_example(O):
@@ -59,7 +59,7 @@ def _rand_case(rng, rank, dtype):
     return dims, box, estr, swz, mem, strides
 
 
-@pytest.mark.parametrize("dtype", ["u8", "bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["u8", "bf16", "f32", "e5m2", "e4m3"])
 @pytest.mark.parametrize("rank", [1, 2, 3, 5])
 def test_box_load_store_vs_oracle(O, dtype, rank):
     rng = np.random.default_rng(1000 * rank + bsm.DTYPE[dtype])
@@ -89,7 +89,7 @@ def test_box_load_store_vs_oracle(O, dtype, rank):
             assert (got[t][~written] == 0xA5).all()
         # store the images back into a sentinel-filled tensor; reduce-add into a second one
         say("box_store", dtype, rank)
-        sent = np.full_like(mem, 0x3C if dtype == "u8" else 0x3C00)
+        sent = np.full_like(mem, 0x3C if bsm.ESIZE[dtype] == 1 else 0x3C00)
         dst = dev(sent)
         bsm.bsm_tile_box_store(bsm.tensor_desc(dst, dtype, dims, strides), bd, dco, nb, dimg, 0)
         exp = sent.copy()

@@ -21,7 +21,8 @@
 //
 // Parity status of each function (what pins it is in tests/test_oracle_*.py):
 //   decoders, encoders, swizzle, box load/store/reduce, grid copy, add_scalar,
-//   ldmatrix image, dense GEMM, block-scaled GEMM: all pinned (none unpinned).
+//   ldmatrix image, dense GEMM, block-scaled GEMM, silu_affine epilogue: all pinned
+//   (none unpinned).
 
 #include <cmath>
 #include <cstdint>
@@ -549,6 +550,17 @@ int oracle_gemm_block_scale_points(int64_t M, int64_t N, int64_t K,
     ref[i] = d0 + sigma * s;
     bound[i] = b;
   }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Scalar epilogue ([TOE] "Scalar compositions": a typed scalar function applied to every
+// element; the pages' example is silu_affine with scalar scale and bias). In fp64:
+//   out = x / (1 + exp(-x)) * scale + bias
+// ---------------------------------------------------------------------------
+int oracle_ewise_silu_affine(const double* x, int64_t n, double scale, double bias, double* out) {
+  if (n < 0) return -2;
+  for (int64_t i = 0; i < n; i++) out[i] = x[i] / (1.0 + std::exp(-x[i])) * scale + bias;
   return 0;
 }
 

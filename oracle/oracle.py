@@ -43,7 +43,7 @@ def lib():
         L = C.CDLL(_LIB)
         P, I64, I32, D = C.c_void_p, C.c_int64, C.c_int, C.c_double
         L.oracle_num_threads.restype = I32
-        for n in ("f16", "bf16", "e4m3", "e2m1", "e8m0"):
+        for n in ("f16", "bf16", "e4m3", "e5m2", "e2m1", "e8m0"):
             f = getattr(L, "oracle_dec_" + n)
             f.restype = D
             f.argtypes = [C.c_uint16 if n in ("f16", "bf16") else C.c_uint8]
@@ -74,6 +74,7 @@ def lib():
                                                      P, I64, P, I64, I32, I32, I32, P, P, I64, P, P]
         L.oracle_check_gemm.restype = I64
         L.oracle_check_gemm.argtypes = [P, I64, I64, I64, P, P, D, P, P]
+        L.oracle_ewise_silu_affine.argtypes = [P, I64, D, D, P]
         _lib = L
     return _lib
 
@@ -234,6 +235,16 @@ def gemm_block_scale_points(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, 
     if rc:
         raise ValueError(f"oracle_gemm_block_scale_points rc={rc}")
     return ref, bound
+
+
+def ewise_silu_affine(x, scale: float, bias: float) -> np.ndarray:
+    """x / (1 + exp(-x)) * scale + bias in float64, elementwise (same shape as x)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    rc = lib().oracle_ewise_silu_affine(_p(x), x.size, float(scale), float(bias), _p(out))
+    if rc:
+        raise ValueError(f"oracle_ewise_silu_affine rc={rc}")
+    return out
 
 
 def check_gemm(D: np.ndarray, ref: np.ndarray, bound: np.ndarray, tol: float):

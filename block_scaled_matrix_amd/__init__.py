@@ -19,8 +19,9 @@ ESIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, 
 STATUS = {0: "BSM_OK", -1: "BSM_E_NULL", -2: "BSM_E_RANK", -3: "BSM_E_BOX", -4: "BSM_E_ESTRIDE",
           -5: "BSM_E_ALIGN", -6: "BSM_E_SWIZZLE", -7: "BSM_E_FILL", -8: "BSM_E_DTYPE", -9: "BSM_E_SHAPE",
           -10: "BSM_E_MAJOR", -11: "BSM_E_ALIAS", -12: "BSM_E_HIP", -13: "BSM_E_ARG"}
+EWISE = {"none": 0, "silu_affine": 1}
 EXPORTS = ("bsm_image_stride", "bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_gemm",
-           "bsm_gemm_block_scale", "bsm_tile_add_scalar_f32", "bsm_debug_fragments",
+           "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise", "bsm_tile_add_scalar_f32", "bsm_debug_fragments",
            "bsm_debug_fragment_shape", "bsm_last_error")
 
 
@@ -39,6 +40,10 @@ class bsm_tensor(C.Structure):
 class bsm_box(C.Structure):
     _fields_ = [("rank", C.c_int32), ("box", C.c_int32 * 5), ("element_strides", C.c_int32 * 5),
                 ("swizzle", C.c_int32), ("oob_fill", C.c_int32)]
+
+
+class bsm_ewise(C.Structure):
+    _fields_ = [("op", C.c_int32), ("scale", C.c_float), ("bias", C.c_float)]
 
 
 _lib = None
@@ -64,12 +69,15 @@ def lib():
                                C.c_int, P]
         L.bsm_gemm_block_scale.argtypes = [I64, I64, I64, I32, P, I64, P, I64, I32, P, I64, P, I64, P, I64,
                                            C.c_int, C.c_int, C.c_int, P]
+        L.bsm_gemm_ewise.argtypes = L.bsm_gemm.argtypes[:-1] + [C.POINTER(bsm_ewise), P]
+        L.bsm_gemm_block_scale_ewise.argtypes = L.bsm_gemm_block_scale.argtypes[:-1] + [C.POINTER(bsm_ewise), P]
         L.bsm_tile_add_scalar_f32.argtypes = [P, P, I64, C.c_float, P]
         L.bsm_debug_fragments.argtypes = [P, I64, I64, C.c_char, P, P]
         L.bsm_debug_fragment_shape.restype = None
         L.bsm_debug_fragment_shape.argtypes = [C.POINTER(I64), C.POINTER(I64)]
         for rc_fn in ("bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_gemm",
-                      "bsm_gemm_block_scale", "bsm_tile_add_scalar_f32", "bsm_debug_fragments"):
+                      "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise",
+                      "bsm_tile_add_scalar_f32", "bsm_debug_fragments"):
             getattr(L, rc_fn).restype = C.c_int
         _lib = L
     return _lib
@@ -160,6 +168,25 @@ def bsm_gemm_block_scale(M, N, K, a_fmt: str, A, lda, SFA, ld_sfa, b_fmt: str, B
     _check(lib().bsm_gemm_block_scale(M, N, K, DTYPE[a_fmt], _ptr(A), lda, _ptr(SFA), ld_sfa, DTYPE[b_fmt],
                                       _ptr(B), ldb, _ptr(SFB), ld_sfb, _ptr(D), ldd, neg_a, neg_b, accum,
                                       _stream(stream)))
+
+
+def ewise_desc(op: str = "silu_affine", scale: float = 1.0, bias: float = 0.0) -> bsm_ewise:
+    """A bsm_ewise epilogue: op "none" or "silu_affine" (y = x / (1 + exp(-x)); y * scale + bias)."""
+    return bsm_ewise(EWISE[op] if isinstance(op, str) else int(op), scale, bias)
+
+
+def bsm_gemm_ewise(M, N, K, ab: str, A, lda, a_major: str, B, ldb, b_major: str, D, ldd, neg_a=0, neg_b=0,
+                   accum=0, ew: bsm_ewise | None = None, stream=None):
+    _check(lib().bsm_gemm_ewise(M, N, K, DTYPE[ab], _ptr(A), lda, a_major.encode(), _ptr(B), ldb,
+                                b_major.encode(), _ptr(D), ldd, neg_a, neg_b, accum,
+                                C.byref(ew) if ew is not None else None, _stream(stream)))
+
+
+def bsm_gemm_block_scale_ewise(M, N, K, a_fmt: str, A, lda, SFA, ld_sfa, b_fmt: str, B, ldb, SFB, ld_sfb, D, ldd,
+                               neg_a=0, neg_b=0, accum=0, ew: bsm_ewise | None = None, stream=None):
+    _check(lib().bsm_gemm_block_scale_ewise(M, N, K, DTYPE[a_fmt], _ptr(A), lda, _ptr(SFA), ld_sfa, DTYPE[b_fmt],
+                                            _ptr(B), ldb, _ptr(SFB), ld_sfb, _ptr(D), ldd, neg_a, neg_b, accum,
+                                            C.byref(ew) if ew is not None else None, _stream(stream)))
 
 
 def bsm_tile_add_scalar_f32(src, dst, n: int, s: float, stream=None):

@@ -237,8 +237,9 @@ static int check_d(float* D, int64_t M, int64_t N, int64_t ldd) {
   return BSM_OK;
 }
 
-int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, int64_t lda, char a_major, const void* B,
-             int64_t ldb, char b_major, float* D, int64_t ldd, int neg_a, int neg_b, int accum, void* stream) {
+static int gemm_dense(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, int64_t lda, char a_major,
+                      const void* B, int64_t ldb, char b_major, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                      const bsm_ewise& ew, void* stream, const char* name) {
   int rc;
   if ((rc = check_flag(neg_a, "neg_a")) || (rc = check_flag(neg_b, "neg_b")) || (rc = check_flag(accum, "accum")))
     return rc;
@@ -268,15 +269,37 @@ int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, int64_t
   g.A = A; g.lda = lda; g.a_kmajor = a_major == 'k';
   g.B = B; g.ldb = ldb; g.b_kmajor = b_major == 'k';
   g.D = D; g.ldd = ldd; g.negate = neg_a ^ neg_b; g.accum = accum;
+  g.ew_op = ew.op; g.ew_scale = ew.scale; g.ew_bias = ew.bias;
   hipError_t e = bsm::launch_gemm_dense(g, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "bsm_gemm");
+  if (e != hipSuccess) return hip_fail(e, name);
   return ok();
 }
 
-int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
-                         const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
-                         const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
-                         void* stream) {
+static int check_ewise(const bsm_ewise* ew) {
+  if (!ew) return fail(BSM_E_NULL, "ew is NULL");
+  if (ew->op != BSM_EW_NONE && ew->op != BSM_EW_SILU_AFFINE) return fail(BSM_E_ARG, "ew->op = %d is not a bsm_ewise_op", ew->op);
+  return BSM_OK;
+}
+
+int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, int64_t lda, char a_major, const void* B,
+             int64_t ldb, char b_major, float* D, int64_t ldd, int neg_a, int neg_b, int accum, void* stream) {
+  return gemm_dense(M, N, K, ab, A, lda, a_major, B, ldb, b_major, D, ldd, neg_a, neg_b, accum,
+                    bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream, "bsm_gemm");
+}
+
+int bsm_gemm_ewise(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, int64_t lda, char a_major,
+                   const void* B, int64_t ldb, char b_major, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                   const bsm_ewise* ew, void* stream) {
+  int rc;
+  if ((rc = check_ewise(ew))) return rc;
+  return gemm_dense(M, N, K, ab, A, lda, a_major, B, ldb, b_major, D, ldd, neg_a, neg_b, accum, *ew, stream,
+                    "bsm_gemm_ewise");
+}
+
+static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
+                            const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
+                            const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                            const bsm_ewise& ew, void* stream, const char* name) {
   int rc;
   if ((rc = check_flag(neg_a, "neg_a")) || (rc = check_flag(neg_b, "neg_b")) || (rc = check_flag(accum, "accum")))
     return rc;
@@ -317,9 +340,28 @@ int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const v
   g.B = B; g.ldb = ldb; g.b_kmajor = 1;
   g.SFA = SFA; g.ld_sfa = ld_sfa; g.SFB = SFB; g.ld_sfb = ld_sfb;
   g.D = D; g.ldd = ldd; g.negate = neg_a ^ neg_b; g.accum = accum;
+  g.ew_op = ew.op; g.ew_scale = ew.scale; g.ew_bias = ew.bias;
   hipError_t e = bsm::launch_gemm_mx(g, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "bsm_gemm_block_scale");
+  if (e != hipSuccess) return hip_fail(e, name);
   return ok();
+}
+
+int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
+                         const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
+                         const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                         void* stream) {
+  return gemm_block_scale(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld_sfb, D, ldd, neg_a, neg_b,
+                          accum, bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream, "bsm_gemm_block_scale");
+}
+
+int bsm_gemm_block_scale_ewise(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
+                               const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
+                               const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b,
+                               int accum, const bsm_ewise* ew, void* stream) {
+  int rc;
+  if ((rc = check_ewise(ew))) return rc;
+  return gemm_block_scale(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld_sfb, D, ldd, neg_a, neg_b,
+                          accum, *ew, stream, "bsm_gemm_block_scale_ewise");
 }
 
 int bsm_tile_add_scalar_f32(const float* src, float* dst, int64_t n, float s, void* stream) {

@@ -31,6 +31,30 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (BSM_LDS void*)lds_base, 16, 0, 0);
 }
 
+// The silu_affine scalar epilogue in float32 ("Explicit CUDA tile patterns", Scalar
+// compositions): y = x / (1 + exp(-x)), then y * scale + bias.
+// exp(z) is taken as 2^(z log2 e) on the hardware base-2 exponential (v_exp_f32). The
+// product p = z log2 e is rounded; its remainder r = z log2 e - p (exact fma against the
+// float part of log2 e, plus z times the rest of it) enters as the first-order factor
+// 2^r = 1 + r ln 2, so exp keeps a few-ulp relative error at every |z| instead of the
+// |z| 2^-24 that the rounded product alone would leave. Outside |x| < 88 (exp(-x) beyond
+// float range or below half an ulp of 1, and for infinities and NaN, where r is not finite)
+// the factor is skipped. The quotient is x times the hardware reciprocal (1 ulp) of 1 + e.
+// So a large negative x gives y = -0 once e overflows, x = -inf gives NaN (-inf * 0), and
+// NaN stays NaN.
+__device__ __forceinline__ float silu_affine(float x, float scale, float bias) {
+  constexpr float kLog2e = 0x1.715476p+0f;      // log2(e) rounded to float
+  constexpr float kLog2eRest = 0x1.4ae0cp-26f;  // log2(e) - kLog2e, to float
+  constexpr float kLn2 = 0x1.62e43p-1f;
+  const float z = -x;
+  const float p = z * kLog2e;
+  const float r = __builtin_fmaf(z, kLog2eRest, __builtin_fmaf(z, kLog2e, -p));
+  const float e0 = __builtin_amdgcn_exp2f(p);
+  const float e = __builtin_fabsf(x) < 88.0f ? __builtin_fmaf(e0, r * kLn2, e0) : e0;
+  const float y = x * __builtin_amdgcn_rcpf(1.0f + e);
+  return __builtin_fmaf(y, scale, bias);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

@@ -27,6 +27,10 @@ struct BoxGeom {
 
 // D[m*ldd + n] = 0 for m < M, n < N (a kernel, so the call can be graph-captured).
 hipError_t launch_zero_f32_2d(float* D, int64_t ldd, int64_t M, int64_t N, hipStream_t st);
+// The K == 0 GEMM output: D[m*ldd + n] = f(accum ? D[m*ldd + n] : 0) for m < M, n < N,
+// f the epilogue (ew_op, ew_scale, ew_bias) of GemmArgs.
+hipError_t launch_empty_gemm(float* D, int64_t ldd, int64_t M, int64_t N, int accum, int ew_op, float ew_scale,
+                             float ew_bias, hipStream_t st);
 
 hipError_t launch_add_scalar_f32(const float* src, float* dst, int64_t n, float s, hipStream_t st);
 
@@ -49,6 +53,8 @@ struct GemmArgs {
   float* D; int64_t ldd;
   int32_t negate;       // neg_a xor neg_b
   int32_t accum;
+  int32_t ew_op;        // bsm_ewise_op applied to each output before its store (0: none)
+  float ew_scale, ew_bias;
 };
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t st);

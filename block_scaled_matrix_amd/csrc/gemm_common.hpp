@@ -165,10 +165,47 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
       for (int r = 0; r < 16; r++) acc[mt][nt][r] = 0.0f;
 }
 
-// D = s * acc (+ D when `add`) for a 128 x 128 wave sub-tile held as 4 x 4 blocks of
+// Whole 512-byte row pieces of one 64-row half (rows rowh + r, r < 64, of region), lane
+// l moving the 16 bytes at column col of rows 2j + l/32: D = f(x (+ D)), f = silu_affine
+// when EW. Eight LDS reads and D loads are in flight ahead of their stores.
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+typedef __attribute__((address_space(1))) float global_f32;
+template <bool EW>
+__device__ __forceinline__ void store_half_whole(float* __restrict__ D, int64_t ldd, int64_t rowh, int64_t col,
+                                                 int lane, int c, const uint8_t* region, bool add, float es,
+                                                 float eb) {
+#pragma unroll
+  for (int j0 = 0; j0 < 32; j0 += 8) {
+    uint4 x[8];
+    u32x4 y[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int r = 2 * (j0 + j) + (lane >> 5);
+      x[j] = lds_read_b128(region + 512 * r + 16 * (c ^ (r & 15)));
+      if (add) y[j] = *(global_u32x4*)(D + (rowh + r) * ldd + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int r = 2 * (j0 + j) + (lane >> 5);
+      u32x4 o = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        float v = __uint_as_float(o[e]);
+        if (add) v += __uint_as_float(y[j][e]);
+        if (EW) v = silu_affine(v, es, eb);
+        o[e] = __float_as_uint(v);
+      }
+      *(global_u32x4*)(D + (rowh + r) * ldd + col) = o;
+    }
+  }
+}
+
+// D = f(s * acc (+ D when `add`)) for a 128 x 128 wave sub-tile held as 4 x 4 blocks of
 // v_mfma 32x32 accumulators computed with the operands swapped (the MFMA row index runs over
 // N): register 4q + e of block (mt, nt) is output row 32mt + l%32, column
-// 32nt + 8q + 4(l/32) + e. The accumulators pass through this wave's
+// 32nt + 8q + 4(l/32) + e. f is the scalar epilogue (ew_op 0: identity, 1: silu_affine
+// with es, eb), applied in registers to each float32 value just before its store. The
+// accumulators pass through this wave's
 // 32 KiB region `region` in two halves of 64 rows and leave as stores of two 512-byte row
 // pieces per instruction (whole 128-byte lines), instead of 32 rows x 32 bytes per
 // instruction, which the memory path takes about twice as long to accept; with `add`, D
@@ -180,11 +217,9 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 // in-range elements only. The caller has synchronised the workgroup so that nobody still
 // reads the region's bytes. (s * acc + D rounds once, as an accumulating MFMA chain started
 // from D would round the same terms in another order.)
-typedef __attribute__((address_space(1))) u32x4 global_u32x4;
-typedef __attribute__((address_space(1))) float global_f32;
 __device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t ldd, int64_t M, int64_t N, int64_t row0,
                                                  int64_t col0, int lane, float sgn, const f32x16 (&acc)[4][4],
-                                                 uint8_t* region, bool add) {
+                                                 uint8_t* region, bool add, int ew_op, float es, float eb) {
   const bool whole = row0 + 128 <= M && col0 + 128 <= N;  // wave-uniform
 #pragma unroll
   for (int half = 0; half < 2; half++) {
@@ -205,28 +240,8 @@ __device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t 
     const int c = lane & 31;
     const int64_t col = col0 + 4 * c;
     if (whole) {
-      // eight reads (and D loads) in flight ahead of their stores
-#pragma unroll
-      for (int j0 = 0; j0 < 32; j0 += 8) {
-        uint4 x[8];
-        u32x4 y[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const int r = 2 * (j0 + j) + (lane >> 5);
-          x[j] = lds_read_b128(region + 512 * r + 16 * (c ^ (r & 15)));
-          if (add) y[j] = *(global_u32x4*)(D + (row0 + 64 * half + r) * ldd + col);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const int r = 2 * (j0 + j) + (lane >> 5);
-          u32x4 o = {x[j].x, x[j].y, x[j].z, x[j].w};
-          if (add) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) o[e] = __float_as_uint(__uint_as_float(o[e]) + __uint_as_float(y[j][e]));
-          }
-          *(global_u32x4*)(D + (row0 + 64 * half + r) * ldd + col) = o;
-        }
-      }
+      if (ew_op) store_half_whole<true>(D, ldd, row0 + 64 * half, col, lane, c, region, add, es, eb);
+      else store_half_whole<false>(D, ldd, row0 + 64 * half, col, lane, c, region, add, es, eb);
     } else {
       for (int j = 0; j < 32; j++) {
         const int r = 2 * j + (lane >> 5);
@@ -237,7 +252,11 @@ __device__ __forceinline__ void store_tile_lines(float* __restrict__ D, int64_t 
           const float xv[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
 #pragma unroll
           for (int e = 0; e < 4; e++)
-            if (col + e < N) p[e] = add ? xv[e] + p[e] : xv[e];
+            if (col + e < N) {
+              float v = add ? xv[e] + p[e] : xv[e];
+              if (ew_op) v = silu_affine(v, es, eb);
+              p[e] = v;
+            }
         }
       }
     }

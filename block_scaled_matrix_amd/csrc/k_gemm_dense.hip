@@ -285,7 +285,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
   }
   // every wave is done with LDS before the accumulators pass through it
   __syncthreads();
-  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, ACC);
+  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, ACC, a.ew_op,
+                         a.ew_scale, a.ew_bias);
 }
 
 template <int DT, bool AK, bool BKM>
@@ -330,11 +331,8 @@ __global__ __launch_bounds__(256) void k_debug_fragments(const uint16_t* __restr
 }  // namespace
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t st) {
-  if (a.K == 0) {
-    // Empty sum: D = accum ? D : 0 (the sign of an empty sum is irrelevant).
-    if (a.accum) return hipSuccess;
-    return launch_zero_f32_2d(a.D, a.ldd, a.M, a.N, st);
-  }
+  // Empty sum: D = f(accum ? D : 0) (the sign of an empty sum is irrelevant).
+  if (a.K == 0) return launch_empty_gemm(a.D, a.ldd, a.M, a.N, a.accum, a.ew_op, a.ew_scale, a.ew_bias, st);
   return a.dtype == BSM_BF16 ? launch_dt<BSM_BF16>(a, st) : launch_dt<BSM_F16>(a, st);
 }
 

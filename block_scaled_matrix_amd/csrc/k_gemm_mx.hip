@@ -405,16 +405,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   }
   // every wave is done with LDS before the accumulators pass through it
   __syncthreads();
-  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, ACC);
+  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, ACC, a.ew_op,
+                         a.ew_scale, a.ew_bias);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
-  if (a.K == 0) {
-    if (a.accum) return hipSuccess;
-    return launch_zero_f32_2d(a.D, a.ldd, a.M, a.N, st);
-  }
+  if (a.K == 0) return launch_empty_gemm(a.D, a.ldd, a.M, a.N, a.accum, a.ew_op, a.ew_scale, a.ew_bias, st);
   const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = (int)tm64, tiles_n = (int)tn64;

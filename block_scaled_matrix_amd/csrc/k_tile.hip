@@ -63,6 +63,30 @@ hipError_t launch_zero_f32_2d(float* D, int64_t ldd, int64_t M, int64_t N, hipSt
   return hipGetLastError();
 }
 
+// The empty-sum GEMM output with its epilogue, in place: D = f(accum ? D : 0), grid-stride
+// over (row, 256-column block) pairs like k_zero_f32_2d.
+__global__ __launch_bounds__(256) void k_empty_gemm_f32_2d(float* D, int64_t ldd, int64_t M, int64_t N, int accum,
+                                                           float es, float eb) {
+  const int64_t cb = (N + 255) / 256;
+  for (int64_t b = blockIdx.x; b < M * cb; b += gridDim.x) {
+    const int64_t row = b / cb, col = (b - row * cb) * 256 + threadIdx.x;
+    if (col < N) {
+      float* p = D + row * ldd + col;
+      *p = silu_affine(accum ? *p : 0.0f, es, eb);
+    }
+  }
+}
+
+hipError_t launch_empty_gemm(float* D, int64_t ldd, int64_t M, int64_t N, int accum, int ew_op, float es, float eb,
+                             hipStream_t st) {
+  if (ew_op == 0) return accum ? hipSuccess : launch_zero_f32_2d(D, ldd, M, N, st);
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int64_t blocks = M * ((N + 255) / 256);
+  const unsigned g = (unsigned)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(k_empty_gemm_f32_2d, dim3(g), dim3(256), 0, st, D, ldd, M, N, accum, es, eb);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ box helpers
 struct RowPos {
   bool ok;       // every outer coordinate in range

@@ -180,6 +180,41 @@ int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K,
                          int32_t b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
                          float* D, int64_t ldd, int neg_a, int neg_b, int accum, void* stream);
 
+/* Scalar epilogue f applied to every GEMM output element in registers, just before its
+ * store ([TP] "Scalar compositions": a typed float32 scalar function inlined at each
+ * register store, with scalar constants broadcast; the pages' example is silu followed
+ * by an affine map, called with scale 2 and bias 1):
+ *   BSM_EW_NONE:        f(x) = x;
+ *   BSM_EW_SILU_AFFINE: f(x) = y * scale + bias,  y = x / (1 + exp(-x)),
+ * evaluated in float32: exp(-x) within a few ulp (the hardware base-2 exponential with
+ * the rounding of -x log2(e) carried as a correction), then x times the hardware
+ * reciprocal of 1 + exp(-x), so y is within about 4 ulp of silu(x) for every float x
+ * (results below 2^-112 may flush to zero). */
+typedef enum bsm_ewise_op { BSM_EW_NONE = 0, BSM_EW_SILU_AFFINE = 1 } bsm_ewise_op;
+typedef struct bsm_ewise {
+  int32_t op;   /* bsm_ewise_op */
+  float scale;  /* silu_affine: multiplier of silu(x) */
+  float bias;   /* silu_affine: added last */
+} bsm_ewise;
+
+/* bsm_gemm and bsm_gemm_block_scale with the epilogue fused into the output store:
+ *   D[m,n] = f(x),  x = (accum ? D[m,n] : 0) + s * sum_k A(m,k) * B(n,k),
+ * where x is the float32 value the plain call would have stored (same kernels, same
+ * rounding) and f is given by *ew (a host struct, read during the call only). K == 0
+ * gives D = f(accum ? D : 0). Every other argument and rule is that of the plain call;
+ * ew == NULL -> BSM_E_NULL, ew->op not a bsm_ewise_op -> BSM_E_ARG. With BSM_EW_NONE
+ * the result is bit-identical to the plain call's. */
+int bsm_gemm_ewise(int64_t M, int64_t N, int64_t K, int32_t ab,
+                   const void* A, int64_t lda, char a_major,
+                   const void* B, int64_t ldb, char b_major,
+                   float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                   const bsm_ewise* ew, void* stream);
+int bsm_gemm_block_scale_ewise(int64_t M, int64_t N, int64_t K,
+                               int32_t a_fmt, const void* A, int64_t lda, const uint8_t* SFA, int64_t ld_sfa,
+                               int32_t b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
+                               float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                               const bsm_ewise* ew, void* stream);
+
 /* Element-wise scalar add on float32 ([TOE] "A Load, Compute, and Store Example"
  * adds one to a (2,32,3,4) tile; [TP] "Scalar compositions"): dst[i] = src[i] + s,
  * i < n, each lane moving 16-byte vectors. src, dst 16-byte aligned; they may be

@@ -127,6 +127,21 @@ def test_gemm_contract_violations(L):
     expect("BSM_E_NULL", s, 64, 64, 64, "e4m3", A, 64, 0, 4, "e4m3", B, 64, SB, 4, D, 64)
     expect("BSM_E_ALIAS", s, 64, 64, 64, "e4m3", A, 64, D + 64, 4, "e4m3", B, 64, SB, 4, D, 64)
     expect("BSM_E_SHAPE", s, 64, 64, 64, "e4m3", A, 1 << 24, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
+    ew = bsm.ewise_desc("silu_affine", 2.0, 1.0)
+    ge = lambda *a, ew=ew: bsm.bsm_gemm_ewise(*a[:15], ew=a[15] if len(a) > 15 else ew, stream=0)
+    expect("BSM_E_NULL", lambda: bsm.bsm_gemm_ewise(64, 64, 64, "bf16", A, 64, "k", B, 64, "k", D, 64, stream=0))
+    expect("BSM_E_ARG", ge, 64, 64, 64, "bf16", A, 64, "k", B, 64, "k", D, 64, 0, 0, 0, bsm.ewise_desc(2))
+    expect("BSM_E_ARG", ge, 64, 64, 64, "bf16", A, 64, "k", B, 64, "k", D, 64, 0, 0, 0, bsm.ewise_desc(-1))
+    expect("BSM_E_DTYPE", ge, 64, 64, 64, "f32", A, 64, "k", B, 64, "k", D, 64)     # plain-call rules hold
+    expect("BSM_E_ALIAS", ge, 64, 64, 64, "bf16", D + 1024, 64, "k", B, 64, "k", D, 64)
+    bsm.bsm_gemm_ewise(64, 0, 64, "bf16", 0, 0, "k", 0, 0, "k", 0, 0, ew=ew, stream=0)   # N == 0: no-op
+    se = lambda *a: bsm.bsm_gemm_block_scale_ewise(*a[:18], ew=a[18] if len(a) > 18 else ew, stream=0)
+    expect("BSM_E_NULL", lambda: bsm.bsm_gemm_block_scale_ewise(64, 64, 64, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB,
+                                                                4, D, 64, stream=0))
+    expect("BSM_E_ARG", se, 64, 64, 64, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64, 0, 0, 0,
+           bsm.ewise_desc(7))
+    expect("BSM_E_SHAPE", se, 64, 64, 48, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_DTYPE", se, 64, 64, 64, "e4m3", A, 64, SA, 4, "e2m1", B, 64, SB, 4, D, 64)
     a = lambda *x: bsm.bsm_tile_add_scalar_f32(*x, stream=0)
     expect("BSM_E_SHAPE", a, A, B, -1, 1.0)
     expect("BSM_E_ALIGN", a, A + 4, B, 8, 1.0)

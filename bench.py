@@ -18,6 +18,10 @@ and WRITE_SIZE, calibrated against a plain copy of known size, see --copy-calibr
 it is null when the kernel's sources no longer hash to the ones the counters were
 taken with.
 
+--epilogue silu_affine fuses the scalar epilogue f(x) = x / (1 + exp(-x)) * 2 + 1 (the example call
+of "Explicit CUDA tile patterns", Scalar compositions) into the three GEMMs' stores (bsm_gemm_ewise, bsm_gemm_block_scale_ewise); the
+rest of the step is unchanged, and config.epilogue names it.
+
 --copy-calibration runs only the calibration copy: the float32 add-scalar kernel over a
 1 GiB buffer (1 GiB read + 1 GiB written per launch), three launches.
 """
@@ -46,6 +50,7 @@ KERNEL_SOURCES = {
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_busy_bench_step.md")
 CALIB_BYTES = 1 << 30
+EPILOGUE_ARGS = (2.0, 1.0)   # silu_affine scale, bias
 
 
 def source_hash(kernel):
@@ -136,9 +141,16 @@ def make_inputs():
     return inp
 
 
-def kernels(inp):
+def kernels(inp, epilogue="none"):
     """(name, launch callable, work, unit, peak) for each row of the step."""
     import block_scaled_matrix_amd as bsm
+
+    if epilogue == "none":
+        gemm, gemm_bs = bsm.bsm_gemm, bsm.bsm_gemm_block_scale
+    else:
+        ew = bsm.ewise_desc(epilogue, *EPILOGUE_ARGS)
+        gemm = lambda *a: bsm.bsm_gemm_ewise(*a, ew=ew)
+        gemm_bs = lambda *a: bsm.bsm_gemm_block_scale_ewise(*a, ew=ew)
 
     b = inp["box"]
     rows, cols, pitch = b["rows"], b["cols"], b["pitch"]
@@ -153,13 +165,13 @@ def kernels(inp):
     f8, f4 = inp["fp8"], inp["fp4"]
     ks = [
         ("box_copy", lambda: bsm.bsm_tile_box_copy(src, dst, add, box), box_bytes, "GB/s", PEAK["hbm_GBs"]),
-        ("gemm_bf16", lambda: bsm.bsm_gemm(M, N, K, "bf16", g["A"], K, "k", g["B"], N, "n", g["D0"], N, 0, 0, 1),
+        ("gemm_bf16", lambda: gemm(M, N, K, "bf16", g["A"], K, "k", g["B"], N, "n", g["D0"], N, 0, 0, 1),
          2.0 * M * N * K, "TFLOP/s", PEAK["bf16_TFs"]),
-        ("gemm_mxfp8", lambda: bsm.bsm_gemm_block_scale(
+        ("gemm_mxfp8", lambda: gemm_bs(
             f8["M"], f8["N"], f8["K"], "e4m3", f8["A"], f8["lda"], f8["SFA"], f8["ld_sfa"], "e4m3", f8["B"], f8["ldb"],
             f8["SFB"], f8["ld_sfb"], f8["D"], f8["N"], 0, 0, 0), 2.0 * f8["M"] * f8["N"] * f8["K"], "TFLOP/s",
          PEAK["fp8_TFs"]),
-        ("gemm_mxfp4", lambda: bsm.bsm_gemm_block_scale(
+        ("gemm_mxfp4", lambda: gemm_bs(
             f4["M"], f4["N"], f4["K"], "e2m1", f4["A"], f4["lda"], f4["SFA"], f4["ld_sfa"], "e2m1", f4["B"], f4["ldb"],
             f4["SFB"], f4["ld_sfb"], f4["D"], f4["N"], 1, 0, 0), 2.0 * f4["M"] * f4["N"] * f4["K"], "TFLOP/s",
          PEAK["fp4_TFs"]),
@@ -219,6 +231,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--epilogue", choices=["none", "silu_affine"], default="none",
+                    help="scalar epilogue fused into the GEMMs' stores")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the plain copy of known size used to calibrate the HBM byte counters")
     args = ap.parse_args()
@@ -236,7 +250,7 @@ def main():
         copy_calibration()
         return
     inp = make_inputs()
-    ks = kernels(inp)
+    ks = kernels(inp, args.epilogue)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -293,7 +307,9 @@ def main():
         "dtype": "bf16 / e4m3 / e2m1 operands, f32 accumulate; bf16 box copy", "data": "synthetic",
         "config": {"workload": "box_copy bf16 16381x8190 (128,64) swz128 + gemm bf16 8192^3 (B MN-major, accum) + "
                                "mxfp8 8192x8192x16384 + mxfp4 16384x8192x8192 (neg_a) + add_one (2,32,3,4)",
-                   "seeds": {"box_copy": 2, "gemm_bf16": 3, "mxfp8": 4, "mxfp4": 5}},
+                   "seeds": {"box_copy": 2, "gemm_bf16": 3, "mxfp8": 4, "mxfp4": 5},
+                   "epilogue": args.epilogue if args.epilogue == "none" else
+                   f"{args.epilogue}(scale {EPILOGUE_ARGS[0]:g}, bias {EPILOGUE_ARGS[1]:g})"},
         "per_kernel": per,
         "roofline": {"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
                      "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dom)},

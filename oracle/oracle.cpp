@@ -20,9 +20,9 @@
 // cannot interpret; it never guesses.
 //
 // Parity status of each function (what pins it is in tests/test_oracle_*.py):
-//   decoders, encoders, swizzle, box load/store/reduce, grid copy, add_scalar,
-//   ldmatrix image, dense GEMM, block-scaled GEMM, silu_affine epilogue: all pinned
-//   (none unpinned).
+//   decoders, encoders, swizzle, box load/store/reduce, gather4/scatter4, grid copy,
+//   add_scalar, ldmatrix image, dense GEMM, block-scaled GEMM, silu_affine epilogue:
+//   all pinned (none unpinned).
 
 #include <cmath>
 #include <cstdint>
@@ -309,6 +309,55 @@ int oracle_box_store(void* base, int dtype, int rank, const int64_t* dims,
     for (int b = 0; b < es; b++) v[b] = img[oracle_swizzle(lin * es + b, swizzle)];
     if (reduce_add) reduce_add_elem(dtype, dst + off, v);
     else std::memcpy(dst + off, v, es);
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// C3b. Row gather and scatter of four rows ([TMA] "Gather4 and scatter4": a 2-D
+// global operand, a box of one row by `width` elements, a shared image of four such
+// rows, and four explicit row coordinates that need not be consecutive). Reading:
+// the column start `col` is the inner coordinate of the box; image row i holds
+// tensor row rows[i], elements col .. col + width - 1. The image is the compact
+// row-major (4, width) array, permuted by the swizzle as one image. Gather: an
+// element whose row or column is out of range reads the fill. Scatter: such elements
+// are not written; rows are written in the order i = 0..3, so a repeated row keeps
+// the last one.
+// ---------------------------------------------------------------------------
+int oracle_gather4(const void* base, int dtype, const int64_t* dims, const int64_t* strides, int32_t width,
+                   int64_t col, const int64_t* rows, int swizzle, int fill, void* image) {
+  const int es = elem_size(dtype);
+  if (es == 0 || width < 1 || swizzle < 0 || swizzle > 3) return -1;
+  if (fill != 0 && fill != 1) return -2;
+  uint8_t fillv[4] = {0, 0, 0, 0};
+  if (fill == 1 && nan_bits(dtype, fillv) != 0) return -2;
+  const uint8_t* src = (const uint8_t*)base;
+  uint8_t* img = (uint8_t*)image;
+  for (int i = 0; i < 4; i++) {
+    for (int64_t j = 0; j < width; j++) {
+      const int64_t r = rows[i], c = col + j;
+      const bool inb = r >= 0 && r < dims[0] && c >= 0 && c < dims[1];
+      const int64_t lin = (int64_t)i * width + j;
+      for (int b = 0; b < es; b++)
+        img[oracle_swizzle(lin * es + b, swizzle)] = inb ? src[r * strides[0] + c * strides[1] + b] : fillv[b];
+    }
+  }
+  return 0;
+}
+
+int oracle_scatter4(void* base, int dtype, const int64_t* dims, const int64_t* strides, int32_t width,
+                    int64_t col, const int64_t* rows, int swizzle, const void* image) {
+  const int es = elem_size(dtype);
+  if (es == 0 || width < 1 || swizzle < 0 || swizzle > 3) return -1;
+  uint8_t* dst = (uint8_t*)base;
+  const uint8_t* img = (const uint8_t*)image;
+  for (int i = 0; i < 4; i++) {
+    for (int64_t j = 0; j < width; j++) {
+      const int64_t r = rows[i], c = col + j;
+      if (r < 0 || r >= dims[0] || c < 0 || c >= dims[1]) continue;
+      const int64_t lin = (int64_t)i * width + j;
+      for (int b = 0; b < es; b++) dst[r * strides[0] + c * strides[1] + b] = img[oracle_swizzle(lin * es + b, swizzle)];
+    }
   }
   return 0;
 }

@@ -38,8 +38,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)   # missing, or older than its source
         L = C.CDLL(_LIB)
         P, I64, I32, D = C.c_void_p, C.c_int64, C.c_int, C.c_double
         L.oracle_num_threads.restype = I32
@@ -61,6 +61,8 @@ def lib():
         L.oracle_box_store.argtypes = [P, I32, I32, P, P, P, P, P, I32, P, I32]
         L.oracle_image_stride.restype = I64
         L.oracle_image_stride.argtypes = [I32, I32, P, P, I32]
+        L.oracle_gather4.argtypes = [P, I32, P, P, I32, I64, P, I32, I32, P]
+        L.oracle_scatter4.argtypes = [P, I32, P, P, I32, I64, P, I32, P]
         L.oracle_box_copy_grid.argtypes = [P, P, P, I32, I32, P, P, P, P, I32, I32]
         L.oracle_add_scalar_f32.argtypes = [P, P, I64, C.c_float]
         L.oracle_ldmatrix.argtypes = [P, P, I32, I32, P]
@@ -146,6 +148,30 @@ def box_store(mem: np.ndarray, dtype: str, dims, strides, box, estr, coords, ima
                                 _p(image), int(reduce_add))
     if rc:
         raise ValueError(f"oracle_box_store rc={rc}")
+
+
+def gather4(mem: np.ndarray, dtype: str, dims, strides, width: int, col: int, rows, swz=0, fill=0) -> np.ndarray:
+    """Image bytes of one four-row gather: a (4, width) image, length = the image stride of
+    a (4, width) box."""
+    mem = np.ascontiguousarray(mem)
+    img = np.zeros(image_stride(dtype, (4, width), (1, 1), swz), dtype=np.uint8)
+    d, s, r = _i64(dims), _i64(strides), _i64(rows)
+    assert len(r) == 4
+    rc = lib().oracle_gather4(_p(mem), DT[dtype], _p(d), _p(s), int(width), int(col), _p(r), swz, fill, _p(img))
+    if rc:
+        raise ValueError(f"oracle_gather4 rc={rc}")
+    return img
+
+
+def scatter4(mem: np.ndarray, dtype: str, dims, strides, width: int, col: int, rows, image, swz=0):
+    """In place on ``mem`` (a contiguous numpy array of the tensor's backing bytes)."""
+    assert mem.flags.c_contiguous
+    image = np.ascontiguousarray(image)
+    d, s, r = _i64(dims), _i64(strides), _i64(rows)
+    assert len(r) == 4
+    rc = lib().oracle_scatter4(_p(mem), DT[dtype], _p(d), _p(s), int(width), int(col), _p(r), swz, _p(image))
+    if rc:
+        raise ValueError(f"oracle_scatter4 rc={rc}")
 
 
 def box_copy_grid(src, dst, dst_add, dtype, dims, strides, box, estr, swz=0, fill=0):

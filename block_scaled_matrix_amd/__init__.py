@@ -20,7 +20,8 @@ STATUS = {0: "BSM_OK", -1: "BSM_E_NULL", -2: "BSM_E_RANK", -3: "BSM_E_BOX", -4: 
           -5: "BSM_E_ALIGN", -6: "BSM_E_SWIZZLE", -7: "BSM_E_FILL", -8: "BSM_E_DTYPE", -9: "BSM_E_SHAPE",
           -10: "BSM_E_MAJOR", -11: "BSM_E_ALIAS", -12: "BSM_E_HIP", -13: "BSM_E_ARG"}
 EWISE = {"none": 0, "silu_affine": 1}
-EXPORTS = ("bsm_image_stride", "bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_gemm",
+EXPORTS = ("bsm_image_stride", "bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy",
+           "bsm_tile_gather4", "bsm_tile_scatter4", "bsm_gemm",
            "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise", "bsm_tile_add_scalar_f32", "bsm_debug_fragments",
            "bsm_debug_fragment_shape", "bsm_last_error")
 
@@ -65,6 +66,8 @@ def lib():
         L.bsm_tile_box_store.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I64, P, C.c_int, P]
         L.bsm_tile_box_copy.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_tensor), C.POINTER(bsm_tensor),
                                         C.POINTER(bsm_box), P]
+        L.bsm_tile_gather4.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I64, P, P]
+        L.bsm_tile_scatter4.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I64, P, P]
         L.bsm_gemm.argtypes = [I64, I64, I64, I32, P, I64, C.c_char, P, I64, C.c_char, P, I64, C.c_int, C.c_int,
                                C.c_int, P]
         L.bsm_gemm_block_scale.argtypes = [I64, I64, I64, I32, P, I64, P, I64, I32, P, I64, P, I64, P, I64,
@@ -75,7 +78,8 @@ def lib():
         L.bsm_debug_fragments.argtypes = [P, I64, I64, C.c_char, P, P]
         L.bsm_debug_fragment_shape.restype = None
         L.bsm_debug_fragment_shape.argtypes = [C.POINTER(I64), C.POINTER(I64)]
-        for rc_fn in ("bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_gemm",
+        for rc_fn in ("bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_tile_gather4",
+                      "bsm_tile_scatter4", "bsm_gemm",
                       "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise",
                       "bsm_tile_add_scalar_f32", "bsm_debug_fragments"):
             getattr(L, rc_fn).restype = C.c_int
@@ -154,6 +158,15 @@ def bsm_tile_box_copy(src: bsm_tensor, dst: bsm_tensor | None, dst_add: bsm_tens
                       stream=None):
     _check(lib().bsm_tile_box_copy(C.byref(src), C.byref(dst) if dst is not None else None,
                                    C.byref(dst_add) if dst_add is not None else None, C.byref(box),
+                                   _stream(stream)))
+
+
+def bsm_tile_gather4(src: bsm_tensor, box: bsm_box, coords, n_issues: int, images, stream=None):
+    _check(lib().bsm_tile_gather4(C.byref(src), C.byref(box), _ptr(coords), n_issues, _ptr(images), _stream(stream)))
+
+
+def bsm_tile_scatter4(dst: bsm_tensor, box: bsm_box, coords, n_issues: int, images, stream=None):
+    _check(lib().bsm_tile_scatter4(C.byref(dst), C.byref(box), _ptr(coords), n_issues, _ptr(images),
                                    _stream(stream)))
 
 

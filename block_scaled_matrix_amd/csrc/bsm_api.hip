@@ -132,6 +132,25 @@ void fill_tensor_geom(const bsm_tensor* t, bsm::BoxGeom* g) {
   for (int i = 0; i < t->rank; i++) { g->dims[i] = t->dims[i]; g->strides[i] = t->strides[i]; }
 }
 
+// A four-row gather / scatter: a rank-2 tensor and a (1, width) box with unit element
+// strides; g then describes the tensor and the (4, width) image.
+int row4_geom(const bsm_tensor* t, const char* name, const bsm_box* box, bsm::BoxGeom* g) {
+  int rc = check_tensor(t, name);
+  if (rc) return rc;
+  if (!box) return fail(BSM_E_NULL, "box descriptor is NULL");
+  if (t->rank != 2) return fail(BSM_E_RANK, "%s: gather4 / scatter4 take a rank-2 tensor (rank %d)", name, t->rank);
+  if (box->rank != 2) return fail(BSM_E_RANK, "box rank %d: gather4 / scatter4 take a rank-2 box", box->rank);
+  if (box->box[0] != 1)
+    return fail(BSM_E_BOX, "box (%d, %d): gather4 / scatter4 take a box of one row", box->box[0], box->box[1]);
+  if (box->element_strides[0] != 1 || box->element_strides[1] != 1)
+    return fail(BSM_E_ESTRIDE, "gather4 / scatter4 take unit element strides");
+  bsm_box b4 = *box;
+  b4.box[0] = 4;
+  if ((rc = make_geom(&b4, t->dtype, g))) return rc;
+  fill_tensor_geom(t, g);
+  return BSM_OK;
+}
+
 int check_flag(int v, const char* name) {
   if (v != 0 && v != 1) return fail(BSM_E_ARG, "%s = %d is not 0 or 1", name, v);
   return BSM_OK;
@@ -227,6 +246,37 @@ int bsm_tile_box_copy(const bsm_tensor* src, const bsm_tensor* dst, const bsm_te
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "bsm_tile_box_copy");
   return ok();
+}
+
+static int row4_call(const bsm_tensor* t, const bsm_box* box, const int32_t* coords_dev, int64_t n_issues,
+                     const void* images, int scatter, void* stream) {
+  const char* name = scatter ? "dst" : "src";
+  bsm::BoxGeom g;
+  int rc = row4_geom(t, name, box, &g);
+  if (rc) return rc;
+  if (n_issues < 0 || n_issues > (int64_t(1) << 33))
+    return fail(BSM_E_SHAPE, "n_issues %lld out of range", (long long)n_issues);
+  if (n_issues == 0) return ok();
+  if (!coords_dev) return fail(BSM_E_NULL, "coords is NULL");
+  if (!images) return fail(BSM_E_NULL, "images is NULL");
+  if ((uintptr_t)coords_dev % 4) return fail(BSM_E_ALIGN, "coords not 4-byte aligned");
+  const uintptr_t ia = box->swizzle ? (uintptr_t(1) << (7 + box->swizzle)) : 128;
+  if ((uintptr_t)images % ia) return fail(BSM_E_ALIGN, "images not %u-byte aligned", (unsigned)ia);
+  Range ir{(uintptr_t)images, (uintptr_t)images + (uintptr_t)(n_issues * g.image_stride)};
+  if (overlap(ir, tensor_range(t))) return fail(BSM_E_ALIAS, "images overlap %s", name);
+  hipError_t e = bsm::launch_row4(g, t->base, coords_dev, n_issues, (void*)images, scatter, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, scatter ? "bsm_tile_scatter4" : "bsm_tile_gather4");
+  return ok();
+}
+
+int bsm_tile_gather4(const bsm_tensor* src, const bsm_box* box, const int32_t* coords_dev, int64_t n_issues,
+                     void* images, void* stream) {
+  return row4_call(src, box, coords_dev, n_issues, images, 0, stream);
+}
+
+int bsm_tile_scatter4(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev, int64_t n_issues,
+                      const void* images, void* stream) {
+  return row4_call(dst, box, coords_dev, n_issues, images, 1, stream);
 }
 
 static int check_d(float* D, int64_t M, int64_t N, int64_t ldd) {

@@ -38,6 +38,11 @@ hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coo
                            void* images, hipStream_t st);
 hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, int64_t n_boxes,
                             const void* images, int reduce_add, hipStream_t st);
+// Four-row gather (scatter = 0: tensor -> images) or scatter (1: images -> tensor) of
+// n_issues issues; g describes the rank-2 tensor and the (4, width) image; coords holds
+// 5 int32 per issue (column start, four rows).
+hipError_t launch_row4(const BoxGeom& g, void* tensor, const int32_t* coords, int64_t n_issues, void* images,
+                       int scatter, hipStream_t st);
 // Grid round trip; dst_strides / add_strides describe dst and dst_add (NULL allowed).
 hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const int64_t* dst_strides,
                            void* dst_add, const int64_t* add_strides, hipStream_t st);

@@ -522,4 +522,94 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ four-row gather / scatter
+// "cp.async.bulk.tensor / cp.reduce.async.bulk.tensor", Gather4 and scatter4: issue t names
+// a column start and four rows (coords[5t .. 5t+4]) of a rank-2 tensor; its (4, width)
+// image holds those rows' `width` elements from the column start, swizzled as one image.
+// Each lane moves one 16-byte image chunk per issue; a workgroup pass covers
+// ipw = 256 / (4 * chunks per row) issues and a workgroup makes kRow4Passes passes over
+// consecutive issues, all loads before all stores (kRow4Passes 16-byte accesses in flight
+// per lane).
+constexpr int kRow4Passes = 4;
+
+// Chunk cc of tensor row `row` from column `col` (the fill outside the tensor).
+__device__ __forceinline__ uint4 row_chunk_load(const BoxGeom& g, const uint8_t* src, int64_t row, int64_t col,
+                                                int cc) {
+  const int epc = 16 / g.esize;
+  const int64_t g0 = col + (int64_t)cc * epc;
+  const bool rok = row >= 0 && row < g.dims[0];
+  if (rok && g0 >= 0 && g0 + epc <= g.dims[1]) {
+    const uint8_t* p = src + row * g.strides[0] + g0 * g.esize;
+    if ((((uintptr_t)p) & 15) == 0) return *(const uint4*)p;
+  }
+  uint4 v = make_uint4(0, 0, 0, 0);
+  for (int e = 0; e < epc; e++) {
+    const int64_t gi = g0 + e;
+    const bool ok = rok && gi >= 0 && gi < g.dims[1];
+    put_elem(v, g.esize, e, ok ? load_elem(src + row * g.strides[0] + gi * g.esize, g.esize) : g.fill_bits);
+  }
+  return v;
+}
+
+// Chunk cc of tensor row `row` from column `col`, in-range elements only.
+__device__ __forceinline__ void row_chunk_store(const BoxGeom& g, uint8_t* dst, int64_t row, int64_t col, int cc,
+                                                uint4 v) {
+  if (row < 0 || row >= g.dims[0]) return;
+  const int epc = 16 / g.esize;
+  const int64_t g0 = col + (int64_t)cc * epc;
+  uint8_t* p = dst + row * g.strides[0] + g0 * g.esize;
+  if (g0 >= 0 && g0 + epc <= g.dims[1] && (((uintptr_t)p) & 15) == 0) {
+    *(uint4*)p = v;
+    return;
+  }
+  for (int e = 0; e < epc; e++) {
+    const int64_t gi = g0 + e;
+    if (gi >= 0 && gi < g.dims[1]) store_elem(dst + row * g.strides[0] + gi * g.esize, g.esize, get_elem(v, g.esize, e));
+  }
+}
+
+template <bool SCATTER>
+__global__ __launch_bounds__(256) void k_row4(BoxGeom g, uint8_t* tensor, const int32_t* __restrict__ coords,
+                                              uint8_t* images, int64_t n, int ipw) {
+  const int cpr = g.row_bytes >> 4, cpi = 4 * cpr;
+  const int slot = threadIdx.x / cpi, w = threadIdx.x - slot * cpi;
+  if (slot >= ipw) return;  // lanes past the last whole issue of a pass (no barrier follows)
+  const int r = w / cpr, cc = w - r * cpr;
+  const uint32_t ioff = image_swizzle((uint32_t)(r * g.row_bytes + cc * 16), g.swizzle);
+  int64_t t[kRow4Passes];
+  uint4 v[kRow4Passes];
+#pragma unroll
+  for (int p = 0; p < kRow4Passes; p++) t[p] = ((int64_t)blockIdx.x * kRow4Passes + p) * ipw + slot;
+#pragma unroll
+  for (int p = 0; p < kRow4Passes; p++) {
+    if (t[p] < n) {
+      if (SCATTER) v[p] = *(const uint4*)(images + t[p] * g.image_stride + ioff);
+      else v[p] = row_chunk_load(g, tensor, coords[5 * t[p] + 1 + r], coords[5 * t[p]], cc);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kRow4Passes; p++) {
+    if (t[p] < n) {
+      if (SCATTER) row_chunk_store(g, tensor, coords[5 * t[p] + 1 + r], coords[5 * t[p]], cc, v[p]);
+      else *(uint4*)(images + t[p] * g.image_stride + ioff) = v[p];
+    }
+  }
+}
+
+hipError_t launch_row4(const BoxGeom& g, void* tensor, const int32_t* coords, int64_t n_issues, void* images,
+                       int scatter, hipStream_t st) {
+  const int cpi = 4 * (g.row_bytes >> 4);  // 4..256 chunks per issue
+  const int ipw = cpi >= 256 ? 1 : 256 / cpi;
+  const int64_t per_block = (int64_t)ipw * kRow4Passes;
+  const int64_t blocks = (n_issues + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (scatter)
+    hipLaunchKernelGGL(k_row4<true>, dim3((unsigned)blocks), dim3(256), 0, st, g, (uint8_t*)tensor, coords,
+                       (uint8_t*)images, n_issues, ipw);
+  else
+    hipLaunchKernelGGL(k_row4<false>, dim3((unsigned)blocks), dim3(256), 0, st, g, (uint8_t*)tensor, coords,
+                       (uint8_t*)images, n_issues, ipw);
+  return hipGetLastError();
+}
+
 }  // namespace bsm

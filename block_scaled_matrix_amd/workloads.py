@@ -18,6 +18,10 @@ Workloads (sizes are the ones the benchmark runs):
                     E8M0 scales 127+U{-4..4}, both K-major, fresh D, seed 4.
   mxfp4_16384_8192  M=16384, N=8192, K=8192, E2M1 bytes uniform (two uniform nibbles),
                     E8M0 scales 127+U{-6..6}, neg_a, fresh D, seed 5.
+  gather4_bf16      a bf16 65536x4096 table N(0,1), seed 6; four-row gathers with a (1,64)
+                    box and 128-byte swizzle (512-byte images), rows taken four at a time
+                    from a seeded permutation, every 64-column block of each row group;
+                    the scatter sends image k's rows to the rows of a second permutation.
 """
 from __future__ import annotations
 
@@ -94,6 +98,27 @@ def mxfp4(seed: int = 5, M: int = 16384, N: int = 8192, K: int = 8192, exp_range
     sfb = (127 + rng.integers(-exp_range, exp_range + 1, (N, K // 32), dtype=np.int16)).astype(np.uint8)
     return {"M": M, "N": N, "K": K, "A": a, "B": b, "SFA": sfa, "SFB": sfb, "lda": K, "ldb": K,
             "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": "e2m1", "accum": 0, "neg_a": 1, "neg_b": 0}
+
+
+def gather4_bf16(seed: int = 6, rows: int = 65536, cols: int = 4096, width: int = 64):
+    """Table (rows, cols) uint16 bf16 bits; gather and scatter coordinates (n, 5) int32, issue
+    t = group * (cols / width) + block: column start block * width, then four rows."""
+    rng = np.random.default_rng(seed)
+    table = to_half_bits(rng.standard_normal((rows, cols), dtype=np.float32), "bf16")
+    perm_g = rng.permutation(rows).astype(np.int32)
+    perm_s = rng.permutation(rows).astype(np.int32)
+    nb = cols // width
+    col = np.tile(np.arange(nb, dtype=np.int32) * width, rows // 4)
+
+    def coords(perm):
+        c = np.empty((rows // 4 * nb, 5), np.int32)
+        c[:, 0] = col
+        c[:, 1:] = np.repeat(perm.reshape(-1, 4), nb, axis=0)
+        return c
+
+    return {"rows": rows, "cols": cols, "width": width, "table": table, "gather": coords(perm_g),
+            "scatter": coords(perm_s), "perm_gather": perm_g, "perm_scatter": perm_s, "swizzle": 3, "fill": 0,
+            "dtype": "bf16"}
 
 
 def sample_points(M: int, N: int, n: int, seed: int = 99):

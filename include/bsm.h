@@ -128,6 +128,32 @@ int bsm_tile_box_load(const bsm_tensor* src, const bsm_box* box, const int32_t* 
 int bsm_tile_box_store(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev,
                        int64_t n_boxes, const void* images, int reduce_add, void* stream);
 
+/* Four-row gather, global -> image ([TMA] "Gather4 and scatter4"; [TP] "TMA"): a
+ * rank-2 tensor, a box of one row (box->box = {1, width}, element strides {1, 1}) and,
+ * per issue, four explicit row coordinates that need not be consecutive or distinct.
+ *   src:        the global tensor (rank 2, as for bsm_tile_box_load);
+ *   coords_dev: DEVICE array of n_issues * 5 int32: issue t's column start c at [5t]
+ *               and its rows r0..r3 at [5t+1 .. 5t+4]; any values (the row component of
+ *               the box coordinates is replaced by the four rows);
+ *   images:     DEVICE buffer of n_issues images of shape (4, width): image row i,
+ *               element j = src[r_i, c + j], or the fill when r_i or c + j is out of
+ *               range; compact row-major and swizzled as one (4, width) box image (the
+ *               inner row rules of bsm_box apply to width); image t at t * S, where S =
+ *               bsm_image_stride of the box {4, width} with the same swizzle; aligned
+ *               like a box-load image buffer. Padding bytes between images are not written.
+ * 0 <= n_issues <= 2^33 (0 is a no-op). images must not overlap src's byte range.
+ * Rank, box, stride, swizzle and fill errors as for bsm_tile_box_load. */
+int bsm_tile_gather4(const bsm_tensor* src, const bsm_box* box, const int32_t* coords_dev,
+                     int64_t n_issues, void* images, void* stream);
+
+/* Four-row scatter, image -> global ([TMA] "Gather4 and scatter4": the store form, the
+ * global tensor first). Same box, coordinate and image contract as bsm_tile_gather4:
+ * image row i is written to dst row r_i from column c; elements whose row or column is
+ * out of range are not written (oob_fill is validated but unused). Rows repeated within
+ * or across issues race (one of the writes survives). images must not overlap dst. */
+int bsm_tile_scatter4(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev,
+                      int64_t n_issues, const void* images, void* stream);
+
 /* Grid round trip through LDS: for every tile coordinate t*box (t over
  * ceil(dims/box) per axis) the box of `src` is loaded into a swizzled LDS image,
  * which is then stored to `dst` and/or add-reduced into `dst_add` at the same

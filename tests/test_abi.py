@@ -89,6 +89,25 @@ def test_box_contract_violations(L):
     expect("BSM_E_SHAPE", cp, src, tensor(dims=(64, 32), base=FAKE + (1 << 30)), None, b, 0)
     expect("BSM_E_DTYPE", cp, src, tensor("f16", base=FAKE + (1 << 30)), None, b, 0)
     expect("BSM_E_DTYPE", cp, tensor("u16"), None, tensor("u16", base=FAKE + (1 << 30)), b, 0)
+    g4 = bsm.box_desc((1, 64), (1, 1), 3)
+    for fn in (bsm.bsm_tile_gather4, bsm.bsm_tile_scatter4):
+        call = lambda t, bx, co=FAKE, n=1, img=FAKE + (1 << 30), fn=fn: fn(t, bx, co, n, img, 0)
+        expect("BSM_E_NULL", call, tensor(base=0), g4)
+        expect("BSM_E_RANK", call, tensor(dims=(4, 64, 64)), bsm.box_desc((1, 1, 64)))
+        expect("BSM_E_RANK", call, tensor(), bsm.box_desc((1, 1, 64)))
+        expect("BSM_E_BOX", call, tensor(), bsm.box_desc((4, 64)))              # a box of one row only
+        expect("BSM_E_BOX", call, tensor(), bsm.box_desc((1, 300)))
+        expect("BSM_E_ESTRIDE", call, tensor(), bsm.box_desc((1, 64), (2, 1)))
+        expect("BSM_E_SWIZZLE", call, tensor(), bsm.box_desc((1, 12)))          # 24-byte rows
+        expect("BSM_E_SWIZZLE", call, tensor(), bsm.box_desc((1, 128), (1, 1), 3))  # 256-byte row > 128
+        expect("BSM_E_FILL", call, tensor("u16"), bsm.box_desc((1, 64), (1, 1), 0, 1))
+        expect("BSM_E_SHAPE", call, tensor(), g4, FAKE, -1)
+        expect("BSM_E_SHAPE", call, tensor(), g4, FAKE, (1 << 33) + 1)
+        expect("BSM_E_NULL", call, tensor(), g4, 0)
+        expect("BSM_E_ALIGN", call, tensor(), g4, FAKE + 2)
+        expect("BSM_E_ALIGN", call, tensor(), g4, FAKE, 1, FAKE + (1 << 30) + 512)    # images not 1024-aligned
+        expect("BSM_E_ALIAS", call, tensor(), g4, FAKE, 1, FAKE + 1024)
+        fn(tensor(), g4, 0, 0, 0, 0)                      # n_issues == 0: no-op
     assert bsm.bsm_image_stride(bsm.box_desc((128, 64), (1, 1), 3), "bf16") == 16384
     assert bsm.bsm_image_stride(bsm.box_desc((8, 16)), "u32") == 512
     assert bsm.bsm_image_stride(bsm.box_desc((3, 8), (1, 1), 2), "bf16") == 512

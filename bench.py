@@ -18,6 +18,13 @@ and WRITE_SIZE, calibrated against a plain copy of known size, see --copy-calibr
 it is null when the kernel's sources no longer hash to the ones the counters were
 taken with.
 
+Rows widened beyond the step, timed after it on their own (same stream, HIP events) and
+reported under `widened` (not part of `value`):
+  gather4    four-row gathers from a bf16 65536x4096 table, (1,64) boxes, 128-byte swizzle,
+             rows four at a time from a seeded permutation, 1 048 576 issues (512 MiB of images)
+  scatter4   the images scattered to the rows of a second permutation (a row permutation of
+             the table)
+
 --epilogue silu_affine fuses the scalar epilogue f(x) = x / (1 + exp(-x)) * 2 + 1 (the example call
 of "Explicit CUDA tile patterns", Scalar compositions) into the three GEMMs' stores (bsm_gemm_ewise, bsm_gemm_block_scale_ewise); the
 rest of the step is unchanged, and config.epilogue names it.
@@ -46,6 +53,8 @@ KERNEL_SOURCES = {
     "gemm_mxfp8": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
     "gemm_mxfp4": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
     "add_one": ["k_tile.hip", "bsm_device.hpp"],
+    "gather4": ["k_tile.hip", "bsm_device.hpp"],
+    "scatter4": ["k_tile.hip", "bsm_device.hpp"],
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_busy_bench_step.md")
@@ -138,6 +147,15 @@ def make_inputs():
     log(f"mxfp4 inputs {time.time() - t0:.1f}s")
     inp["add"] = dev(W.add_one_tile())
     inp["add_out"] = torch.empty_like(inp["add"])
+    g = W.gather4_bf16()
+    n = len(g["gather"])
+    raw = torch.empty(n * 1024 + 1024, dtype=torch.uint8, device="cuda")   # 1024-byte aligned images
+    off = (-raw.data_ptr()) % 1024
+    inp["g4"] = {"rows": g["rows"], "cols": g["cols"], "width": g["width"], "n": n, "table": dev(g["table"]),
+                 "gather": dev(g["gather"].reshape(-1)), "scatter": dev(g["scatter"].reshape(-1)),
+                 "images": raw[off:off + n * 1024], "dst": torch.empty((g["rows"], g["cols"]), dtype=torch.int16,
+                                                                       device="cuda")}
+    log(f"gather4 inputs {time.time() - t0:.1f}s")
     return inp
 
 
@@ -179,6 +197,45 @@ def kernels(inp, epilogue="none"):
          PEAK["hbm_GBs"]),
     ]
     return ks
+
+
+def widened(inp):
+    """(name, launch callable, work, unit, peak) for the rows timed beside the step."""
+    import block_scaled_matrix_amd as bsm
+
+    g = inp["g4"]
+    rows, cols, n = g["rows"], g["cols"], g["n"]
+    box = bsm.box_desc((1, g["width"]), (1, 1), 3, 0)
+    src = bsm.tensor_desc(g["table"], "bf16", (rows, cols), (cols * 2, 2))
+    dst = bsm.tensor_desc(g["dst"], "bf16", (rows, cols), (cols * 2, 2))
+    nbytes = 2 * rows * cols * 2                 # every table byte read once and written once (as image bytes)
+    return [
+        ("gather4", lambda: bsm.bsm_tile_gather4(src, box, g["gather"], n, g["images"]), nbytes, "GB/s",
+         PEAK["hbm_GBs"]),
+        ("scatter4", lambda: bsm.bsm_tile_scatter4(dst, box, g["scatter"], n, g["images"]), nbytes, "GB/s",
+         PEAK["hbm_GBs"]),
+    ]
+
+
+def time_launches(ks, steps, stream):
+    """Average HIP-event time (ms) of each launch in ks over `steps` rounds, on `stream`."""
+    import torch
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
+          for _ in range(steps)]
+    for s in range(steps):
+        for i, (_, fn, *_) in enumerate(ks):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    return [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps for i in range(len(ks))]
+
+
+def rate_entry(ms, work, unit, peak):
+    rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
+            "frac": round(rate / peak, 4), "work_per_launch": work}
 
 
 def cpu_baseline():
@@ -289,6 +346,15 @@ def main():
         if mf is not None:   # counter figures of the same kernel sources (profiles/mfma_busy_bench_step.md)
             per[name]["mfma_busy"], per[name]["clock_ghz"] = mf
         log(f"{name}: {ms:.4f} ms  {rate:.1f} {unit}  ({100 * rate / peak:.1f}% of {peak})")
+    wk = widened(inp)
+    for _, fn, *_ in wk:
+        fn()
+    torch.cuda.synchronize()
+    wide = {}
+    for (name, _, work, unit, peak), ms in zip(wk, time_launches(wk, args.steps, stream)):
+        wide[name] = rate_entry(ms, work, unit, peak)
+        wide[name]["traffic"] = measured_traffic(name)
+        log(f"{name} (widened): {ms:.4f} ms  {wide[name]['achieved']:.1f} {unit}")
     dom = max((n for n in per if n != "add_one"), key=lambda n: per[n]["ms"])
     d = per[dom]
     gemm_flops = sum(k[2] for k in ks if k[0].startswith("gemm"))
@@ -311,6 +377,7 @@ def main():
                    "epilogue": args.epilogue if args.epilogue == "none" else
                    f"{args.epilogue}(scale {EPILOGUE_ARGS[0]:g}, bias {EPILOGUE_ARGS[1]:g})"},
         "per_kernel": per,
+        "widened": wide,
         "roofline": {"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
                      "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dom)},
         "cpu_baseline": cpu,

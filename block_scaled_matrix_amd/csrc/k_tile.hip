@@ -528,9 +528,11 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
 // image holds those rows' `width` elements from the column start, swizzled as one image.
 // Each lane moves one 16-byte image chunk per issue; a workgroup pass covers
 // ipw = 256 / (4 * chunks per row) issues and a workgroup makes kRow4Passes passes over
-// consecutive issues, all loads before all stores (kRow4Passes 16-byte accesses in flight
-// per lane).
-constexpr int kRow4Passes = 4;
+// consecutive issues, both loads before both stores. Whole chunks move with non-temporal
+// loads and stores (each byte is touched once). Measured on the 65536 x 4096 bf16
+// permutation workload: 2 passes beat 1, 4 and 8, and the non-temporal accesses gain
+// 10-15% over plain ones.
+constexpr int kRow4Passes = 2;
 
 // Chunk cc of tensor row `row` from column `col` (the fill outside the tensor).
 __device__ __forceinline__ uint4 row_chunk_load(const BoxGeom& g, const uint8_t* src, int64_t row, int64_t col,
@@ -540,7 +542,7 @@ __device__ __forceinline__ uint4 row_chunk_load(const BoxGeom& g, const uint8_t*
   const bool rok = row >= 0 && row < g.dims[0];
   if (rok && g0 >= 0 && g0 + epc <= g.dims[1]) {
     const uint8_t* p = src + row * g.strides[0] + g0 * g.esize;
-    if ((((uintptr_t)p) & 15) == 0) return *(const uint4*)p;
+    if ((((uintptr_t)p) & 15) == 0) return stream_load16(p);
   }
   uint4 v = make_uint4(0, 0, 0, 0);
   for (int e = 0; e < epc; e++) {
@@ -559,7 +561,7 @@ __device__ __forceinline__ void row_chunk_store(const BoxGeom& g, uint8_t* dst, 
   const int64_t g0 = col + (int64_t)cc * epc;
   uint8_t* p = dst + row * g.strides[0] + g0 * g.esize;
   if (g0 >= 0 && g0 + epc <= g.dims[1] && (((uintptr_t)p) & 15) == 0) {
-    *(uint4*)p = v;
+    stream_store16(p, v);
     return;
   }
   for (int e = 0; e < epc; e++) {
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(256) void k_row4(BoxGeom g, uint8_t* tensor, const 
 #pragma unroll
   for (int p = 0; p < kRow4Passes; p++) {
     if (t[p] < n) {
-      if (SCATTER) v[p] = *(const uint4*)(images + t[p] * g.image_stride + ioff);
+      if (SCATTER) v[p] = stream_load16(images + t[p] * g.image_stride + ioff);
       else v[p] = row_chunk_load(g, tensor, coords[5 * t[p] + 1 + r], coords[5 * t[p]], cc);
     }
   }
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(256) void k_row4(BoxGeom g, uint8_t* tensor, const 
   for (int p = 0; p < kRow4Passes; p++) {
     if (t[p] < n) {
       if (SCATTER) row_chunk_store(g, tensor, coords[5 * t[p] + 1 + r], coords[5 * t[p]], cc, v[p]);
-      else *(uint4*)(images + t[p] * g.image_stride + ioff) = v[p];
+      else stream_store16(images + t[p] * g.image_stride + ioff, v[p]);
     }
   }
 }

@@ -100,6 +100,44 @@ def mxfp4(seed: int = 5, M: int = 16384, N: int = 8192, K: int = 8192, exp_range
             "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": "e2m1", "accum": 0, "neg_a": 1, "neg_b": 0}
 
 
+BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """(rows, K) 6-bit codes -> (rows, 3K/4) bytes: element i at bits 6i..6i+5 of the row's
+    little-endian bit string (K a multiple of 4)."""
+    c = codes.astype(np.uint32).reshape(codes.shape[0], -1, 4)
+    w = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
+    out = np.empty(w.shape + (3,), np.uint8)
+    out[..., 0], out[..., 1], out[..., 2] = w & 255, (w >> 8) & 255, (w >> 16) & 255
+    return out.reshape(codes.shape[0], -1)
+
+
+def mx_codes(rng, fmt: str, rows: int, K: int) -> np.ndarray:
+    """Uniform random element codes of a block-scaled format, packed K-major: (rows, K*bits/8)
+    bytes. 8-bit formats draw from their finite codes, E2M1 draws whole bytes (two uniform
+    nibbles), the 6-bit formats draw all 64 codes (all finite)."""
+    if fmt == "e4m3":
+        return FINITE_E4M3[rng.integers(0, FINITE_E4M3.size, (rows, K))]
+    if fmt == "e5m2":
+        return FINITE_E5M2[rng.integers(0, FINITE_E5M2.size, (rows, K))]
+    if fmt == "e2m1":
+        return rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    return pack_fp6(rng.integers(0, 64, (rows, K)))
+
+
+def mx_pair(seed: int, M: int, N: int, K: int, a_fmt: str, b_fmt: str, exp_range: int = 4):
+    """Block-scaled operands of any two formats: codes uniform (mx_codes), E8M0 scales
+    127 + U{-exp_range..exp_range}, both K-major with lda = ldb = K."""
+    rng = np.random.default_rng(seed)
+    a = mx_codes(rng, a_fmt, M, K)
+    b = mx_codes(rng, b_fmt, N, K)
+    sfa = (127 + rng.integers(-exp_range, exp_range + 1, (M, K // 32))).astype(np.uint8)
+    sfb = (127 + rng.integers(-exp_range, exp_range + 1, (N, K // 32))).astype(np.uint8)
+    return {"M": M, "N": N, "K": K, "A": a, "B": b, "SFA": sfa, "SFB": sfb, "lda": K, "ldb": K,
+            "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": a_fmt, "b_fmt": b_fmt, "accum": 0, "neg_a": 0, "neg_b": 0}
+
+
 def gather4_bf16(seed: int = 6, rows: int = 65536, cols: int = 4096, width: int = 64):
     """Table (rows, cols) uint16 bf16 bits; gather and scatter coordinates (n, 5) int32, issue
     t = group * (cols / width) + block: column start block * width, then four rows."""

@@ -13,14 +13,14 @@
 //   [LDM] "ldmatrix / stmatrix"
 //   [TOE] "Tile Operands and Execution"
 //   [MMA] "tcgen05.mma"
-// Storage formats the pages only name (e4m3, e5m2, e2m1, the 8-bit scale) follow the
-// public OCP Microscaling Formats (MX) v1.0 specification, section 5.
+// Storage formats the pages only name (e4m3, e5m2, the 6-bit e2m3 / e3m2, e2m1, the 8-bit
+// scale) follow the public OCP Microscaling Formats (MX) v1.0 specification, section 5.
 //
 // Every function returns 0 on success and a negative value on an argument it
 // cannot interpret; it never guesses.
 //
 // Parity status of each function (what pins it is in tests/test_oracle_*.py):
-//   decoders, encoders, swizzle, box load/store/reduce, gather4/scatter4, grid copy,
+//   decoders (fp6 included), encoders, swizzle, box load/store/reduce, gather4/scatter4, grid copy,
 //   add_scalar, ldmatrix image, dense GEMM, block-scaled GEMM, silu_affine epilogue:
 //   all pinned (none unpinned).
 
@@ -38,7 +38,7 @@ extern "C" {
 // Storage-format codes of this oracle (its own numbering; the Python wrapper maps names).
 enum OracleDtype {
   OD_U8 = 0, OD_U16 = 1, OD_U32 = 2, OD_F16 = 3, OD_BF16 = 4, OD_F32 = 5,
-  OD_E4M3 = 6, OD_E2M1 = 7, OD_E8M0 = 8, OD_E5M2 = 9
+  OD_E4M3 = 6, OD_E2M1 = 7, OD_E8M0 = 8, OD_E5M2 = 9, OD_E2M3 = 10, OD_E3M2 = 11
 };
 
 int oracle_num_threads(void) {
@@ -116,6 +116,32 @@ double oracle_dec_e2m1(uint8_t nib) {
   return s ? -v : v;
 }
 
+// OCP E2M3 (FP6): s.ee.mmm, bias 1, no infinities or NaN; subnormals m * 2^-3,
+// largest 7.5 (OCP MX v1.0, section 5.3.2). Only the low 6 bits of `c` are used.
+double oracle_dec_e2m3(uint8_t c) {
+  int s = (c >> 5) & 1, e = (c >> 3) & 3, m = c & 7;
+  double v = e == 0 ? std::ldexp((double)m, -3) : std::ldexp(8.0 + m, e - 4);
+  return s ? -v : v;
+}
+
+// OCP E3M2 (FP6): s.eee.mm, bias 3, no infinities or NaN; subnormals m * 2^-4,
+// largest 28 (OCP MX v1.0, section 5.3.2). Only the low 6 bits of `c` are used.
+double oracle_dec_e3m2(uint8_t c) {
+  int s = (c >> 5) & 1, e = (c >> 2) & 7, m = c & 3;
+  double v = e == 0 ? std::ldexp((double)m, -4) : std::ldexp(4.0 + m, e - 5);
+  return s ? -v : v;
+}
+
+// Packed 6-bit storage (a reading: the pages name the 6-bit kinds but no memory layout):
+// element i of a row is bits 6i .. 6i+5 of the row's bytes read as one little-endian bit
+// string, so four elements fill three bytes.
+static uint8_t fp6_code(const uint8_t* row, int64_t i) {
+  const int64_t bit = 6 * i;
+  const unsigned lo = row[bit >> 3];
+  const unsigned hi = ((bit & 7) > 2) ? row[(bit >> 3) + 1] : 0u;
+  return (uint8_t)(((lo | (hi << 8)) >> (bit & 7)) & 63);
+}
+
 // OCP E8M0 scale: an unsigned biased exponent, value 2^(c-127); 0xFF is NaN
 // (OCP MX v1.0, section 5.4.1).
 double oracle_dec_e8m0(uint8_t c) {
@@ -169,6 +195,8 @@ int oracle_decode_array(int dtype, const void* src, int64_t n, double* out) {
       case OD_E5M2: out[i] = oracle_dec_e5m2(b[i]); break;
       case OD_E2M1: out[i] = oracle_dec_e2m1((b[i / 2] >> (4 * (i & 1))) & 15); break;
       case OD_E8M0: out[i] = oracle_dec_e8m0(b[i]); break;
+      case OD_E2M3: out[i] = oracle_dec_e2m3(fp6_code(b, i)); break;
+      case OD_E3M2: out[i] = oracle_dec_e3m2(fp6_code(b, i)); break;
       default: return -1;
     }
   }
@@ -530,8 +558,12 @@ int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int dtype,
 // Reading (OCP MX v1.0, section 5): one E8M0 scale per 32 consecutive K
 // elements starting at k = 0; the operand value is decode(element) * 2^(s-127).
 // K-major storage only: element (r,k) at index r*ld + k; for packed E2M1 that
-// index selects byte idx/2 and the low nibble for even idx.
-static bool mx_fmt(int f) { return f == OD_E4M3 || f == OD_E5M2 || f == OD_E2M1; }
+// index selects byte idx/2 and the low nibble for even idx; for the 6-bit formats,
+// bits 6 idx .. 6 idx + 5 of the operand's little-endian bit string (ld * 6 is a
+// multiple of 8, so every row starts on a byte).
+static bool mx_fmt(int f) {
+  return f == OD_E4M3 || f == OD_E5M2 || f == OD_E2M1 || f == OD_E2M3 || f == OD_E3M2;
+}
 
 static double load_op_scaled(int fmt, const uint8_t* p, int64_t ld, const uint8_t* sf,
                              int64_t ld_sf, int64_t r, int64_t k) {
@@ -539,6 +571,8 @@ static double load_op_scaled(int fmt, const uint8_t* p, int64_t ld, const uint8_
   double v;
   if (fmt == OD_E4M3) v = oracle_dec_e4m3(p[idx]);
   else if (fmt == OD_E5M2) v = oracle_dec_e5m2(p[idx]);
+  else if (fmt == OD_E2M3) v = oracle_dec_e2m3(fp6_code(p, idx));
+  else if (fmt == OD_E3M2) v = oracle_dec_e3m2(fp6_code(p, idx));
   else v = oracle_dec_e2m1((p[idx >> 1] >> (4 * (idx & 1))) & 15);
   return v * oracle_dec_e8m0(sf[r * ld_sf + k / 32]);
 }
@@ -603,7 +637,7 @@ int oracle_gemm_block_scale_points(int64_t M, int64_t N, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
-// Scalar epilogue ([TOE] "Scalar compositions": a typed scalar function applied to every
+// Scalar epilogue ([TP] "Scalar compositions": a typed scalar function applied to every
 // element; the pages' example is silu_affine with scalar scale and bias). In fp64:
 //   out = x / (1 + exp(-x)) * scale + bias
 // ---------------------------------------------------------------------------

@@ -17,7 +17,9 @@ _SRC = os.path.join(_HERE, "oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # The oracle's own storage-format codes (see OracleDtype in oracle.cpp).
-DT = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "e4m3": 6, "e2m1": 7, "e8m0": 8, "e5m2": 9}
+DT = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "e4m3": 6, "e2m1": 7, "e8m0": 8, "e5m2": 9,
+      "e2m3": 10, "e3m2": 11}
+BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}   # block-scaled element widths
 ESIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e8m0": 1, "e5m2": 1}
 
 
@@ -43,7 +45,7 @@ def lib():
         L = C.CDLL(_LIB)
         P, I64, I32, D = C.c_void_p, C.c_int64, C.c_int, C.c_double
         L.oracle_num_threads.restype = I32
-        for n in ("f16", "bf16", "e4m3", "e5m2", "e2m1", "e8m0"):
+        for n in ("f16", "bf16", "e4m3", "e5m2", "e2m1", "e8m0", "e2m3", "e3m2"):
             f = getattr(L, "oracle_dec_" + n)
             f.restype = D
             f.argtypes = [C.c_uint16 if n in ("f16", "bf16") else C.c_uint8]
@@ -98,10 +100,11 @@ def num_threads() -> int:
 
 
 def decode(dtype: str, raw: np.ndarray, n: int | None = None) -> np.ndarray:
-    """Decode storage bits to float64. ``raw`` is the backing array; for e2m1, n = element count."""
+    """Decode storage bits to float64. ``raw`` is the backing array; for the packed formats
+    (e2m1, e2m3, e3m2), n = element count (default: every element the bytes hold)."""
     raw = np.ascontiguousarray(raw)
     if n is None:
-        n = raw.nbytes * 2 if dtype == "e2m1" else raw.nbytes // ESIZE[dtype]
+        n = raw.nbytes * 8 // BITS[dtype] if dtype in ("e2m1", "e2m3", "e3m2") else raw.nbytes // ESIZE[dtype]
     out = np.empty(n, dtype=np.float64)
     rc = lib().oracle_decode_array(DT[dtype], _p(raw), n, _p(out))
     assert rc == 0

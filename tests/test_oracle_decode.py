@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+from block_scaled_matrix_amd import workloads as W
+
 
 def _same(a, b):
     a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
@@ -135,3 +137,42 @@ def test_encode_decode_roundtrip(O, dt):
     keep = ~np.isnan(vals)
     back = O.enc(dt, vals[keep])
     assert np.array_equal(back, bits[keep])
+
+
+# OCP MX v1.0, section 5.3.2 (FP6): max normal, min normal, max subnormal, min subnormal.
+FP6_ANCHORS = {"e2m3": (7.5, 1.0, 0.875, 0.125, 3), "e3m2": (28.0, 0.25, 0.1875, 0.0625, 2)}
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_all_codes_vs_spec_and_fp8_grid(O, fmt):
+    """All 64 codes: the specification's anchor values, bit 5 as the sign, strictly increasing
+    magnitudes over codes 0..31, the subnormals evenly spaced and every binade holding 2^m
+    evenly spaced values, and each value on the grid of the 8-bit format with the same
+    mantissa width (E2M3 -> float8_e4m3fn, E3M2 -> float8_e5m2), via torch's round trip."""
+    mx_n, mn_n, mx_s, mn_s, mbits = FP6_ANCHORS[fmt]
+    codes = np.arange(64)
+    got = O.decode(fmt, W.pack_fp6(codes.reshape(1, 64)), 64)
+    pos, neg = got[:32], got[32:]
+    assert _same(neg, -pos) and np.signbit(got[32])
+    assert pos[31] == mx_n and pos[1 << mbits] == mn_n and pos[(1 << mbits) - 1] == mx_s and pos[1] == mn_s
+    assert pos[0] == 0.0 and np.all(np.diff(pos) > 0)
+    sub = pos[:1 << mbits]
+    assert np.allclose(np.diff(sub), mn_s, rtol=0, atol=0)
+    for e in range(1, 32 >> mbits):
+        b = pos[e << mbits:(e + 1) << mbits]
+        assert len(set(np.diff(b))) == 1 and b[0] == 2.0 ** (e - 1) * mn_n
+    t = torch.float8_e4m3fn if fmt == "e2m3" else torch.float8_e5m2
+    assert _same(torch.from_numpy(got).to(t).to(torch.float64).numpy(), got)
+
+
+def test_fp6_packing_vs_unpackbits(O):
+    """Element i of a packed row is bits 6i..6i+5 of the row's little-endian bit string:
+    extracted independently with numpy's unpackbits, then decoded code by code."""
+    rng = np.random.default_rng(3)
+    raw = rng.integers(0, 256, (5, 48), dtype=np.uint8)       # 5 rows of 64 elements
+    bits = np.unpackbits(raw, axis=1, bitorder="little").reshape(5, 64, 6)
+    codes = (bits * (1 << np.arange(6))).sum(axis=2)
+    for fmt in ("e2m3", "e3m2"):
+        table = O.decode(fmt, W.pack_fp6(np.arange(64).reshape(1, 64)), 64)
+        got = O.decode(fmt, raw, 5 * 64).reshape(5, 64)
+        assert _same(got, table[codes])

@@ -123,6 +123,23 @@ def mx_vals(raw, fmt, rows, K):
     return out
 
 
+def fp6_vals(raw, fmt, rows, K):
+    """6-bit elements: codes extracted with numpy's unpackbits (little-endian bit string per
+    row), values from the OCP table of the format (codes 0..31 positive, bit 5 the sign)."""
+    bits = np.unpackbits(raw.reshape(rows, -1), axis=1, bitorder="little")[:, :6 * K].reshape(rows, K, 6)
+    codes = (bits * (1 << np.arange(6))).sum(axis=2)
+    if fmt == "e2m3":   # subnormals m/8; normals (1 + m/8) 2^(e-1)
+        pos = [m / 8 for m in range(8)] + [(1 + m / 8) * 2.0 ** (e - 1) for e in range(1, 4) for m in range(8)]
+    else:               # subnormals m/16; normals (1 + m/4) 2^(e-3)
+        pos = [m / 16 for m in range(4)] + [(1 + m / 4) * 2.0 ** (e - 3) for e in range(1, 8) for m in range(4)]
+    table = np.array(pos + [-v for v in pos])
+    return table[codes]
+
+
+def any_vals(raw, fmt, rows, K):
+    return fp6_vals(raw, fmt, rows, K) if fmt in ("e2m3", "e3m2") else mx_vals(raw, fmt, rows, K)
+
+
 def scaled(vals, sf):
     return vals * np.repeat(np.exp2(sf.astype(np.float64) - 127), 32, axis=1)
 
@@ -241,3 +258,28 @@ def test_check_gemm_flags_planted_errors(O):
     assert O.check_gemm(D3, ref, bound, 2e-3)[0] == 1
     z = np.zeros((2, 2))
     assert O.check_gemm(np.array([[0, -0.0], [1e-30, 0]], np.float32), z, z, 2e-3)[0] == 1  # exact where bound 0
+
+
+PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e5m2"), ("e2m3", "e4m3"), ("e2m1", "e3m2"),
+         ("e3m2", "e2m3")]
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
+def test_block_scale_any_pair_vs_numpy_brute_force(O, a_fmt, b_fmt):
+    """Every pairing of the block-scaled formats (the 6-bit ones and mixed widths), against
+    numpy matmul of operands decoded independently (unpackbits and the OCP tables for the
+    6-bit formats, torch for 8-bit, the OCP table for E2M1)."""
+    rng = np.random.default_rng([19, len(a_fmt + b_fmt), ord(a_fmt[1]), ord(b_fmt[3])])
+    for trial in range(5):
+        M, N = int(rng.choice(SIZES)), int(rng.choice(SIZES))
+        K = int(rng.choice([32, 64, 128, 192]))
+        neg_a, neg_b, accum = (int(v) for v in rng.integers(0, 2, 3))
+        g = W.mx_pair(60 + trial, M, N, K, a_fmt, b_fmt)
+        d0 = rng.standard_normal((M, N)).astype(np.float32)
+        ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], K, g["SFA"], K // 32, b_fmt, g["B"], K, g["SFB"],
+                                        K // 32, d0, N, neg_a, neg_b, accum)
+        av = scaled(any_vals(g["A"], a_fmt, M, K), g["SFA"])
+        bv = scaled(any_vals(g["B"], b_fmt, N, K), g["SFB"])
+        exp = (d0.astype(np.float64) if accum else 0.0) + (-1.0) ** (neg_a + neg_b) * (av @ bv.T)
+        np.testing.assert_allclose(ref, exp, rtol=0, atol=1e-12 * (1 + (np.abs(av) @ np.abs(bv).T).max()))
+        np.testing.assert_allclose(bound, np.abs(av) @ np.abs(bv).T, rtol=1e-12)

@@ -14,7 +14,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsm.so")
 
-DTYPE = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "e4m3": 6, "e2m1": 7, "e8m0": 8, "e5m2": 9}
+DTYPE = {"u8": 0, "u16": 1, "u32": 2, "f16": 3, "bf16": 4, "f32": 5, "e4m3": 6, "e2m1": 7, "e8m0": 8, "e5m2": 9,
+         "e2m3": 10, "e3m2": 11}
 ESIZE = {"u8": 1, "u16": 2, "u32": 4, "f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e8m0": 1, "e5m2": 1}
 STATUS = {0: "BSM_OK", -1: "BSM_E_NULL", -2: "BSM_E_RANK", -3: "BSM_E_BOX", -4: "BSM_E_ESTRIDE",
           -5: "BSM_E_ALIGN", -6: "BSM_E_SWIZZLE", -7: "BSM_E_FILL", -8: "BSM_E_DTYPE", -9: "BSM_E_SHAPE",

@@ -353,11 +353,13 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
   int rc;
   if ((rc = check_flag(neg_a, "neg_a")) || (rc = check_flag(neg_b, "neg_b")) || (rc = check_flag(accum, "accum")))
     return rc;
-  auto mx = [](int32_t f) { return f == BSM_E4M3 || f == BSM_E5M2 || f == BSM_E2M1; };
-  if (!mx(a_fmt) || !mx(b_fmt))
-    return fail(BSM_E_DTYPE, "a_fmt %d / b_fmt %d: block-scaled GEMM takes E4M3, E5M2 or E2M1", a_fmt, b_fmt);
-  if ((a_fmt == BSM_E2M1) != (b_fmt == BSM_E2M1))
-    return fail(BSM_E_DTYPE, "fp4 operand mixed with an fp8 one (%d, %d) is not supported", a_fmt, b_fmt);
+  auto bits = [](int32_t f) {
+    return f == BSM_E4M3 || f == BSM_E5M2 ? 8 : (f == BSM_E2M3 || f == BSM_E3M2 ? 6 : (f == BSM_E2M1 ? 4 : 0));
+  };
+  const int ba = bits(a_fmt), bb = bits(b_fmt);
+  if (!ba || !bb)
+    return fail(BSM_E_DTYPE, "a_fmt %d / b_fmt %d: block-scaled GEMM takes E4M3, E5M2, E2M3, E3M2 or E2M1", a_fmt,
+                b_fmt);
   if (M < 0 || N < 0 || K < 0 || M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
     return fail(BSM_E_SHAPE, "M, N, K = %lld, %lld, %lld out of range", (long long)M, (long long)N, (long long)K);
   if (K % 32) return fail(BSM_E_SHAPE, "K = %lld is not a multiple of the 32-element scale block", (long long)K);
@@ -366,19 +368,18 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
   if (K > 0) {
     if (!A || !B || !SFA || !SFB) return fail(BSM_E_NULL, "A, B, SFA or SFB is NULL");
     if ((uintptr_t)A % 16 || (uintptr_t)B % 16) return fail(BSM_E_ALIGN, "A and B must be 16-byte aligned");
-    const int per_byte = a_fmt == BSM_E2M1 ? 2 : 1;
     if (lda < K || ldb < K) return fail(BSM_E_ALIGN, "lda, ldb must be >= K");
-    if (lda % (16 * per_byte) || ldb % (16 * per_byte))
+    if ((lda * ba) % 128 || (ldb * bb) % 128)
       return fail(BSM_E_ALIGN, "lda = %lld, ldb = %lld: rows must start 16-byte aligned", (long long)lda, (long long)ldb);
     if (ld_sfa < K / 32 || ld_sfb < K / 32) return fail(BSM_E_ALIGN, "ld_sfa, ld_sfb must be >= K/32");
     if (ld_sfa % 4 || ld_sfb % 4 || (uintptr_t)SFA % 4 || (uintptr_t)SFB % 4)
       return fail(BSM_E_ALIGN, "scale rows must start 4-byte aligned (SFA, SFB 4-byte aligned, ld_sfa, ld_sfb multiples of 4)");
-    if (lda / per_byte > (int64_t(1) << 23) || ldb / per_byte > (int64_t(1) << 23) || ld_sfa > (int64_t(1) << 24) ||
+    if (lda * ba / 8 > (int64_t(1) << 23) || ldb * bb / 8 > (int64_t(1) << 23) || ld_sfa > (int64_t(1) << 24) ||
         ld_sfb > (int64_t(1) << 24))
       return fail(BSM_E_SHAPE, "leading dimensions too large for 32-bit in-tile offsets");
     const Range rd{(uintptr_t)D, (uintptr_t)(D + (M - 1) * ldd + N)};
-    const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(((M - 1) * lda + K) / per_byte)};
-    const Range rb{(uintptr_t)B, (uintptr_t)B + (uintptr_t)(((N - 1) * ldb + K) / per_byte)};
+    const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(((M - 1) * lda + K) * ba / 8)};
+    const Range rb{(uintptr_t)B, (uintptr_t)B + (uintptr_t)(((N - 1) * ldb + K) * bb / 8)};
     const Range rsa{(uintptr_t)SFA, (uintptr_t)SFA + (uintptr_t)(M * ld_sfa)};
     const Range rsb{(uintptr_t)SFB, (uintptr_t)SFB + (uintptr_t)(N * ld_sfb)};
     if (overlap(rd, ra) || overlap(rd, rb) || overlap(rd, rsa) || overlap(rd, rsb))

@@ -49,7 +49,7 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
 
 struct GemmArgs {
   int64_t M, N, K;
-  int32_t dtype;        // BSM_F16 / BSM_BF16 (dense) or A's BSM_E4M3 / BSM_E5M2 / BSM_E2M1 (block scaled)
+  int32_t dtype;        // BSM_F16 / BSM_BF16 (dense) or A's block-scaled format (E4M3, E5M2, E2M3, E3M2, E2M1)
   int32_t dtype_b;      // block scaled: B's format (0 for dense)
   const void* A; int64_t lda; int32_t a_kmajor;
   const void* B; int64_t ldb; int32_t b_kmajor;
@@ -64,6 +64,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
+// Any pairing of E4M3, E5M2, E2M3, E3M2, E2M1 except 8-bit x 8-bit and E2M1 x E2M1 (K > 0).
+hipError_t launch_gemm_mx_any(const GemmArgs& a, hipStream_t st);
 
 // Operand-tile geometry of the dense GEMM (rows x K elements per LDS stage).
 constexpr int kDenseTileRows = 256;

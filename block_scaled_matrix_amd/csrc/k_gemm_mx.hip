@@ -413,6 +413,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
 
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
   if (a.K == 0) return launch_empty_gemm(a.D, a.ldd, a.M, a.N, a.accum, a.ew_op, a.ew_scale, a.ew_bias, st);
+  const bool byte_a = a.dtype == BSM_E4M3 || a.dtype == BSM_E5M2, byte_b = a.dtype_b == BSM_E4M3 || a.dtype_b == BSM_E5M2;
+  if (!(byte_a && byte_b) && !(a.dtype == BSM_E2M1 && a.dtype_b == BSM_E2M1)) return launch_gemm_mx_any(a, st);
   const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = (int)tm64, tiles_n = (int)tn64;

@@ -136,7 +136,9 @@ def test_gemm_contract_violations(L):
     s = lambda *a: bsm.bsm_gemm_block_scale(*a, stream=0)
     SA, SB = FAKE + (3 << 32), FAKE + (4 << 32)
     expect("BSM_E_DTYPE", s, 64, 64, 64, "bf16", A, 64, SA, 4, "bf16", B, 64, SB, 4, D, 64)
-    expect("BSM_E_DTYPE", s, 64, 64, 64, "e4m3", A, 64, SA, 4, "e2m1", B, 64, SB, 4, D, 64)
+    expect("BSM_E_DTYPE", s, 64, 64, 64, "e4m3", A, 64, SA, 4, "f16", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e2m3", A, 96, SA, 4, "e4m3", B, 64, SB, 4, D, 64)   # 72-byte fp6 rows
+    expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 64, SA, 4, "e3m2", B, 32, SB, 4, D, 64)   # ldb < K
     expect("BSM_E_SHAPE", s, 64, 64, 48, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
     expect("BSM_E_ALIGN", s, 64, 64, 64, "e4m3", A, 72, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
     expect("BSM_E_ALIGN", s, 64, 64, 64, "e2m1", A, 80, SA, 4, "e2m1", B, 64, SB, 4, D, 64)   # 40-byte rows
@@ -160,7 +162,7 @@ def test_gemm_contract_violations(L):
     expect("BSM_E_ARG", se, 64, 64, 64, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64, 0, 0, 0,
            bsm.ewise_desc(7))
     expect("BSM_E_SHAPE", se, 64, 64, 48, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
-    expect("BSM_E_DTYPE", se, 64, 64, 64, "e4m3", A, 64, SA, 4, "e2m1", B, 64, SB, 4, D, 64)
+    expect("BSM_E_DTYPE", se, 64, 64, 64, "e4m3", A, 64, SA, 4, "bf16", B, 64, SB, 4, D, 64)
     a = lambda *x: bsm.bsm_tile_add_scalar_f32(*x, stream=0)
     expect("BSM_E_SHAPE", a, A, B, -1, 1.0)
     expect("BSM_E_ALIGN", a, A + 4, B, 8, 1.0)

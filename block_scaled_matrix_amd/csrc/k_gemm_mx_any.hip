@@ -15,14 +15,16 @@
 //    6i .. 6i+5 (the same little-endian packing as in memory);
 //  - 4-bit: lane l holds row l%32, k in [32(l/32), +32): 16 bytes, low nibble first.
 //
-// Design (a general path, not the tuned pipeline): workgroup tile 256 x 256, K tiles of
-// 128 elements (128, 96 or 64 bytes of a row), four waves with 128 x 128 sub-tiles.
-// Operand tiles go HBM -> registers -> LDS, one K tile ahead (the loads of tile kt + 2
-// are issued after tile kt + 1 is written to LDS, so they land during tile kt + 1's
-// multiplies). LDS rows are padded by 16 bytes, so the 16 rows read at one offset by a
-// 16-lane group fall in distinct banks for every row width. Scales go straight from HBM
-// to registers (one 32-bit word per row per K tile: the four 32-K blocks). A partial last
-// K tile reads zero elements and unit scales past K.
+// Design (a general path, simpler than the tuned pipeline): workgroup tile 256 x 256, K
+// tiles of 128 elements (128, 96 or 64 bytes of a row), four waves with 128 x 128
+// sub-tiles. Whole K tiles stream HBM -> LDS with direct copies (global_load_lds) into two
+// stages, tile kt + 2 issued as soon as every wave is done reading tile kt's stage. LDS
+// rows are padded by 16 bytes, so the 16 rows read at one offset by a 16-lane group fall
+// in distinct banks for every row width; the copies fill the pads too (with a repeat of
+// the row's first chunk), so every copy is a contiguous 1 KiB of LDS. Each stage also
+// holds the tile's scale words (one 32-bit word per row: the four 32-K blocks), copied
+// 4 bytes per lane. Step 1's fragment reads are spread between step 0's MFMAs. A partial
+// last K tile goes through registers with zero elements and unit scales past K.
 #include "gemm_common.hpp"
 #include "../../include/bsm.h"
 
@@ -42,9 +44,12 @@ struct Op {
   static constexpr int CPR = ROW / 16;    // 16-byte chunks per row per K tile (and per lane)
 };
 
+// A stage: A tile, B tile, then the K tile's scale words of A's and B's 256 rows (4 bytes
+// each: the four 32-K blocks of the tile).
 template <int CA, int CB>
 struct Lay {
-  static constexpr int STAGE = Op<CA>::TILE + Op<CB>::TILE;
+  static constexpr int SCALES = Op<CA>::TILE + Op<CB>::TILE;
+  static constexpr int STAGE = SCALES + 2048;
   static constexpr int BYTES = 2 * STAGE > 131072 ? 2 * STAGE : 131072;  // the epilogue uses 128 KiB
 };
 
@@ -67,11 +72,13 @@ __device__ __forceinline__ void row_offsets(int64_t ld_bytes, int64_t rows, int 
   }
 }
 
-// Chunk i (of CPR) of this lane in K tile kt of one operand: bytes [16 cc, +16) of the
-// tile's row piece of row ro[i]; bytes at or past `kbytes` (the row's K extent) read as zero.
+// This lane's CPR chunks of the partial last K tile kt of one operand (bytes [16 cc, +16)
+// of the tile's row piece of row ro[i]): bytes at or past `kbytes` (the row's K extent)
+// read as zero (rows are whole 16-byte chunks, so a chunk that starts inside the K extent
+// lies inside the row).
 template <int C>
-__device__ __forceinline__ void load_chunks(const uint8_t* base, const uint32_t (&ro)[Op<C>::CPR], int kt,
-                                            int64_t kbytes, int q, uint4 (&v)[Op<C>::CPR]) {
+__device__ __forceinline__ void load_chunks_tail(const uint8_t* base, const uint32_t (&ro)[Op<C>::CPR], int kt,
+                                                 int64_t kbytes, int q, uint4 (&v)[Op<C>::CPR]) {
   typedef Op<C> P;
 #pragma unroll
   for (int i = 0; i < P::CPR; i++) {
@@ -79,7 +86,7 @@ __device__ __forceinline__ void load_chunks(const uint8_t* base, const uint32_t 
     const int64_t off = (int64_t)kt * P::ROW + 16 * cc;
     uint4 x = make_uint4(0, 0, 0, 0);
     if (off < kbytes) {
-      x = *(const uint4*)(base + ro[i] + off);   // inside the row: rows are whole 16-byte chunks
+      x = *(const uint4*)(base + ro[i] + off);
       const int64_t valid = kbytes - off;
       if (valid < 16) {
         uint32_t wd[4] = {x.x, x.y, x.z, x.w};
@@ -105,22 +112,27 @@ __device__ __forceinline__ void store_chunks(uint8_t* tile, int q, const uint4 (
   }
 }
 
-// Scale words of K tile kt for this lane's four rows (row0 + base + 32t + l%32); the bytes
-// of blocks at or past nblk (K / 32) become 127 (unit scale on zero elements).
-__device__ __forceinline__ void load_scales(const uint8_t* sf, int64_t ld_sf, int64_t row0, int64_t rows, int base,
-                                            int lane, int kt, int64_t nblk, uint32_t (&s)[4]) {
+// Thread q's scale word of K tile kt: row q of the tile (clamped to the operand), the four
+// 32-K blocks of the tile. In a partial last tile the bytes of blocks at or past nblk
+// (K / 32) become 127 (unit scale on zero elements).
+__device__ __forceinline__ uint32_t load_scale_word(const uint8_t* sf, int64_t ld_sf, int64_t row0, int64_t rows,
+                                                    int q, int kt) {
+  const int64_t grow = min(row0 + q, rows - 1);
+  return *(const uint32_t*)(sf + grow * ld_sf + 4 * (int64_t)kt);
+}
+
+__device__ __forceinline__ uint32_t mask_scale_word(uint32_t x, int kt, int64_t nblk) {
   const int64_t b0 = 4 * (int64_t)kt;
 #pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const int64_t grow = min(row0 + base + 32 * t + (lane & 31), rows - 1);
-    uint32_t x = *(const uint32_t*)(sf + grow * ld_sf + b0);
-    if (b0 + 4 > nblk) {
+  for (int j = 0; j < 4; j++)
+    if (b0 + j >= nblk) x = (x & ~(0xFFu << (8 * j))) | (127u << (8 * j));
+  return x;
+}
+
+// This lane's scale words for its four rows (base + 32t + l%32) from a stage's scale area.
+__device__ __forceinline__ void read_scales(const uint8_t* area, int base, int lane, uint32_t (&s)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (b0 + j >= nblk) x = (x & ~(0xFFu << (8 * j))) | (127u << (8 * j));
-    }
-    s[t] = x;
-  }
+  for (int t = 0; t < 4; t++) s[t] = *(const BSM_LDS uint32_t*)(area + 4 * (base + 32 * t + (lane & 31)));
 }
 
 // Operand registers of 64-K step s for the lane's row of 32-row block t.
@@ -147,28 +159,36 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t,
   return v;
 }
 
-// The 16 MFMAs of 64-K step S (fragments read first). The MFMA takes B first (its format
-// code and scales as src0); after the per-lane shift by 8 (l/32), op_sel byte 2S holds the
-// scale of the lane's 32-K block of this step.
+// Operand registers of 64-K step S for the wave: A blocks t = 0..3 (rows wa + 32t + l%32),
+// B blocks (rows wb + ...).
 template <int CA, int CB, int S>
-__device__ __forceinline__ void mx_step(const uint8_t* ta, const uint8_t* tb, int wa, int wb, int lane, int sh,
-                                        const uint32_t (&sa)[4], const uint32_t (&sb)[4], f32x16 (&acc)[4][4]) {
-  i32x8 fa[4], fb[4];
+__device__ __forceinline__ void read_frags(const uint8_t* ta, const uint8_t* tb, int wa, int wb, int lane,
+                                           i32x8 (&fa)[4], i32x8 (&fb)[4]) {
 #pragma unroll
   for (int t = 0; t < 4; t++) {
     fa[t] = read_frag<CA>(ta, wa, t, S, lane);
     fb[t] = read_frag<CB>(tb, wb, t, S, lane);
   }
+}
+
+// The 16 MFMAs of 64-K step S (accumulator rows mt-major). The MFMA takes B first (its
+// format code and scales as src0); after the per-lane shift by 8 (l/32), op_sel byte 2S
+// holds the scale of the lane's 32-K block of this step. side(i) runs after MFMA i: the
+// empty asm statements around each MFMA (accumulators kept in AGPRs, memory clobbered)
+// keep the side work - LDS reads and writes - between the MFMAs, where it overlaps the
+// matrix pipe instead of waiting for it.
+template <int CA, int CB, int S, typename Side>
+__device__ __forceinline__ void mfma16(const i32x8 (&fa)[4], const i32x8 (&fb)[4], const uint32_t (&sa)[4],
+                                       const uint32_t (&sb)[4], int sh, f32x16 (&acc)[4][4], Side side) {
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++)
-    {
-      asm volatile("" : "+a"(acc[mt][nt]));   // keep the accumulators in AGPRs
-      acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[nt], fa[mt], acc[mt][nt], CB, CA, 2 * S,
-                                                                     (int)(sb[nt] >> sh), 2 * S, (int)(sa[mt] >> sh));
-      asm volatile("" : "+a"(acc[mt][nt]));
-    }
+  for (int i = 0; i < 16; i++) {
+    const int mt = i >> 2, nt = i & 3;
+    asm volatile("" : "+a"(acc[mt][nt])::"memory");
+    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[nt], fa[mt], acc[mt][nt], CB, CA, 2 * S,
+                                                                   (int)(sb[nt] >> sh), 2 * S, (int)(sa[mt] >> sh));
+    asm volatile("" : "+a"(acc[mt][nt])::"memory");
+    side(i);
+  }
 }
 
 template <int CA, int CB>
@@ -184,7 +204,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   const int wa = 128 * (w >> 1), wb = 128 * (w & 1);
   const float sgn = a.negate ? -1.0f : 1.0f;
   const int64_t nblk = a.K / 32;
-  const int nkt = (int)((a.K + KT - 1) / KT);
   const int64_t lda_b = a.lda * PA::BITS / 8, ldb_b = a.ldb * PB::BITS / 8;
   const int64_t ka = a.K * PA::BITS / 8, kb = a.K * PB::BITS / 8;   // a row's K extent in bytes
   const uint8_t* A = (const uint8_t*)a.A + m0 * lda_b;
@@ -194,46 +213,87 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
 
   f32x16 acc[4][4];
   gemm::zero_acc(acc);
-  uint4 va[PA::CPR], vb[PB::CPR];
-  uint32_t sa[4], sb[4], na[4], nb[4], roa[PA::CPR], rob[PB::CPR];
-  row_offsets<CA>(lda_b, rows_a, q, roa);
-  row_offsets<CB>(ldb_b, rows_b, q, rob);
-
-  load_chunks<CA>(A, roa, 0, ka, q, va);
-  load_chunks<CB>(B, rob, 0, kb, q, vb);
-  load_scales(a.SFA, a.ld_sfa, m0, a.M, wa, lane, 0, nblk, sa);
-  load_scales(a.SFB, a.ld_sfb, n0, a.N, wb, lane, 0, nblk, sb);
-  store_chunks<CA>(lds, q, va);
-  store_chunks<CB>(lds + PA::TILE, q, vb);
-  if (nkt > 1) {
-    load_chunks<CA>(A, roa, 1, ka, q, va);
-    load_chunks<CB>(B, rob, 1, kb, q, vb);
-    load_scales(a.SFA, a.ld_sfa, m0, a.M, wa, lane, 1, nblk, na);
-    load_scales(a.SFB, a.ld_sfb, n0, a.N, wb, lane, 1, nblk, nb);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; kt++) {
-    const uint8_t* ta = lds + (kt & 1) * L::STAGE;
-    const uint8_t* tb = ta + PA::TILE;
-    mx_step<CA, CB, 0>(ta, tb, wa, wb, lane, sh, sa, sb, acc);
-    mx_step<CA, CB, 1>(ta, tb, wa, wb, lane, sh, sa, sb, acc);
-    if (kt + 1 < nkt) {
-      uint8_t* na_t = lds + ((kt + 1) & 1) * L::STAGE;
-      store_chunks<CA>(na_t, q, va);
-      store_chunks<CB>(na_t + PA::TILE, q, vb);
+  // Direct copies of one stage: NA (NB) 1 KiB copies for the A (B) tile, copy j going to
+  // wave j % 4, then one 256-byte scale copy per operand per wave.
+  constexpr int NA = PA::PITCH / 4, NB = PB::PITCH / 4;   // = 256 * PITCH / 1024
+  constexpr int DA = NA / 4, DB = NB / 4, DPW = DA + DB + 2;
+  uint32_t oa[DA], ob[DB], osa, osb;
+  {
+    auto offs = [&](auto P, int64_t ld_bytes, int64_t rows, int j) -> uint32_t {
+      typedef decltype(P) PP;
+      const int p = 1024 * (w + 4 * j) + 16 * lane;
+      const int r = p / PP::PITCH, slot = (p - r * PP::PITCH) >> 4;
+      return (uint32_t)(min((int64_t)r, rows - 1) * ld_bytes + (slot < PP::CPR ? 16 * slot : 0));
+    };
 #pragma unroll
-      for (int t = 0; t < 4; t++) {
-        sa[t] = na[t];
-        sb[t] = nb[t];
+    for (int j = 0; j < DA; j++) oa[j] = offs(PA{}, lda_b, rows_a, j);
+#pragma unroll
+    for (int j = 0; j < DB; j++) ob[j] = offs(PB{}, ldb_b, rows_b, j);
+    osa = (uint32_t)(min((int64_t)(64 * w + lane), rows_a - 1) * a.ld_sfa);
+    osb = (uint32_t)(min((int64_t)(64 * w + lane), rows_b - 1) * a.ld_sfb);
+  }
+  const uint8_t* SA = a.SFA + m0 * a.ld_sfa;
+  const uint8_t* SB = a.SFB + n0 * a.ld_sfb;
+  const uint32_t lds0 = gemm::lds_addr(lds);
+  auto issue = [&](int kt, int stage) {
+    const uint32_t st = lds0 + stage * L::STAGE;
+#pragma unroll
+    for (int j = 0; j < DA; j++) gemm::dma16s(A + kt * PA::ROW, oa[j], st + 1024 * (w + 4 * j));
+#pragma unroll
+    for (int j = 0; j < DB; j++) gemm::dma16s(B + kt * PB::ROW, ob[j], st + PA::TILE + 1024 * (w + 4 * j));
+    gemm::dma4s(SA + 4 * kt, osa, st + L::SCALES + 256 * w);
+    gemm::dma4s(SB + 4 * kt, osb, st + L::SCALES + 1024 + 256 * w);
+  };
+  // Multiply the tile in stage st: step 1's fragment reads go out between step 0's MFMAs.
+  auto multiply = [&](const uint8_t* st) {
+    uint32_t sa[4], sb[4];
+    i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    read_scales(st + L::SCALES, wa, lane, sa);
+    read_scales(st + L::SCALES + 1024, wb, lane, sb);
+    read_frags<CA, CB, 0>(st, st + PA::TILE, wa, wb, lane, fa0, fb0);
+    mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, [&](int i) {
+      if (i < 8) {
+        if (i & 1) fb1[i >> 1] = read_frag<CB>(st + PA::TILE, wb, i >> 1, 1, lane);
+        else fa1[i >> 1] = read_frag<CA>(st, wa, i >> 1, 1, lane);
       }
-      if (kt + 2 < nkt) {
-        load_chunks<CA>(A, roa, kt + 2, ka, q, va);
-        load_chunks<CB>(B, rob, kt + 2, kb, q, vb);
-        load_scales(a.SFA, a.ld_sfa, m0, a.M, wa, lane, kt + 2, nblk, na);
-        load_scales(a.SFB, a.ld_sfb, n0, a.N, wb, lane, kt + 2, nblk, nb);
-      }
-    }
+    });
+    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [](int) {});
+  };
+
+  // Whole K tiles. Past the last one the copies re-read the last tile into the stage just
+  // released (nobody reads it again), so every iteration issues the same copies and the
+  // wait counts stay fixed.
+  const int nfull = (int)(a.K / KT);
+  if (nfull > 0) {
+    issue(0, 0);
+    issue(min(1, nfull - 1), 1);
+    gemm::stage_barrier<DPW>();
+  }
+  for (int kt = 0; kt < nfull; kt++) {
+    multiply(lds + (kt & 1) * L::STAGE);
+    gemm::lds_barrier();                     // every wave is done with this stage
+    issue(min(kt + 2, nfull - 1), kt & 1);
+    gemm::stage_barrier<DPW>();              // tile kt + 1 has landed
+  }
+  gemm::wait_dma();                          // the repeated copies too, before LDS is reused
+  __syncthreads();
+  // A partial last K tile (K not a multiple of 128), loaded with zeros past K.
+  if (a.K % KT) {
+    uint4 va[PA::CPR], vb[PB::CPR];
+    uint32_t roa[PA::CPR], rob[PB::CPR];
+    row_offsets<CA>(lda_b, rows_a, q, roa);
+    row_offsets<CB>(ldb_b, rows_b, q, rob);
+    uint8_t* st = lds + (nfull & 1) * L::STAGE;
+    load_chunks_tail<CA>(A, roa, nfull, ka, q, va);
+    load_chunks_tail<CB>(B, rob, nfull, kb, q, vb);
+    const uint32_t wsa = mask_scale_word(load_scale_word(a.SFA, a.ld_sfa, m0, a.M, q, nfull), nfull, nblk);
+    const uint32_t wsb = mask_scale_word(load_scale_word(a.SFB, a.ld_sfb, n0, a.N, q, nfull), nfull, nblk);
+    store_chunks<CA>(st, q, va);
+    store_chunks<CB>(st + PA::TILE, q, vb);
+    *(BSM_LDS uint32_t*)(st + L::SCALES + 4 * q) = wsa;
+    *(BSM_LDS uint32_t*)(st + L::SCALES + 1024 + 4 * q) = wsb;
+    __syncthreads();
+    multiply(st);
     __syncthreads();
   }
   gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, a.accum != 0,

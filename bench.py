@@ -24,6 +24,10 @@ reported under `widened` (not part of `value`):
              rows four at a time from a seeded permutation, 1 048 576 issues (512 MiB of images)
   scatter4   the images scattered to the rows of a second permutation (a row permutation of
              the table)
+  gemm_e4m3_e2m1   block-scaled M=N=8192, K=16384, A E4M3, B E2M1 (mixed widths), fresh D
+  gemm_e2m3_e2m3   block-scaled M=N=8192, K=16384, both FP6 E2M3, fresh D
+(the mixed pair runs at the 8-bit MFMA rate, peak 5033.2 TFLOP/s; FP6 pairs at the 4-bit
+rate, peak 10066.3 TFLOP/s)
 
 --epilogue silu_affine fuses the scalar epilogue f(x) = x / (1 + exp(-x)) * 2 + 1 (the example call
 of "Explicit CUDA tile patterns", Scalar compositions) into the three GEMMs' stores (bsm_gemm_ewise, bsm_gemm_block_scale_ewise); the
@@ -55,6 +59,8 @@ KERNEL_SOURCES = {
     "add_one": ["k_tile.hip", "bsm_device.hpp"],
     "gather4": ["k_tile.hip", "bsm_device.hpp"],
     "scatter4": ["k_tile.hip", "bsm_device.hpp"],
+    "gemm_e4m3_e2m1": ["k_gemm_mx_any.hip", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_e2m3_e2m3": ["k_gemm_mx_any.hip", "gemm_common.hpp", "bsm_device.hpp"],
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_busy_bench_step.md")
@@ -156,6 +162,11 @@ def make_inputs():
                  "images": raw[off:off + n * 1024], "dst": torch.empty((g["rows"], g["cols"]), dtype=torch.int16,
                                                                        device="cuda")}
     log(f"gather4 inputs {time.time() - t0:.1f}s")
+    for key, (af, bf, seed) in {"mix": ("e4m3", "e2m1", 21), "fp6": ("e2m3", "e2m3", 22)}.items():
+        g = W.mx_pair(seed, 8192, 8192, 16384, af, bf)
+        inp[key] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+        inp[key]["D"] = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
+    log(f"mixed / fp6 GEMM inputs {time.time() - t0:.1f}s")
     return inp
 
 
@@ -209,11 +220,20 @@ def widened(inp):
     src = bsm.tensor_desc(g["table"], "bf16", (rows, cols), (cols * 2, 2))
     dst = bsm.tensor_desc(g["dst"], "bf16", (rows, cols), (cols * 2, 2))
     nbytes = 2 * rows * cols * 2                 # every table byte read once and written once (as image bytes)
+
+    def mx(key):
+        x = inp[key]
+        return lambda: bsm.bsm_gemm_block_scale(x["M"], x["N"], x["K"], x["fmt"], x["A"], x["lda"], x["SFA"],
+                                                x["ld_sfa"], x["b_fmt"], x["B"], x["ldb"], x["SFB"], x["ld_sfb"],
+                                                x["D"], x["N"], 0, 0, 0)
+    flops = 2.0 * 8192 * 8192 * 16384
     return [
         ("gather4", lambda: bsm.bsm_tile_gather4(src, box, g["gather"], n, g["images"]), nbytes, "GB/s",
          PEAK["hbm_GBs"]),
         ("scatter4", lambda: bsm.bsm_tile_scatter4(dst, box, g["scatter"], n, g["images"]), nbytes, "GB/s",
          PEAK["hbm_GBs"]),
+        ("gemm_e4m3_e2m1", mx("mix"), flops, "TFLOP/s", PEAK["fp8_TFs"]),
+        ("gemm_e2m3_e2m3", mx("fp6"), flops, "TFLOP/s", PEAK["fp4_TFs"]),
     ]
 
 
@@ -354,6 +374,9 @@ def main():
     for (name, _, work, unit, peak), ms in zip(wk, time_launches(wk, args.steps, stream)):
         wide[name] = rate_entry(ms, work, unit, peak)
         wide[name]["traffic"] = measured_traffic(name)
+        mf = measured_mfma(name)
+        if mf is not None:
+            wide[name]["mfma_busy"], wide[name]["clock_ghz"] = mf
         log(f"{name} (widened): {ms:.4f} ms  {wide[name]['achieved']:.1f} {unit}")
     dom = max((n for n in per if n != "add_one"), key=lambda n: per[n]["ms"])
     d = per[dom]

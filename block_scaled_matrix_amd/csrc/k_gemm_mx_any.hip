@@ -17,14 +17,17 @@
 //
 // Design (a general path, simpler than the tuned pipeline): workgroup tile 256 x 256, K
 // tiles of 128 elements (128, 96 or 64 bytes of a row), four waves with 128 x 128
-// sub-tiles. Whole K tiles stream HBM -> LDS with direct copies (global_load_lds) into two
-// stages, tile kt + 2 issued as soon as every wave is done reading tile kt's stage. LDS
-// rows are padded by 16 bytes, so the 16 rows read at one offset by a 16-lane group fall
-// in distinct banks for every row width; the copies fill the pads too (with a repeat of
-// the row's first chunk), so every copy is a contiguous 1 KiB of LDS. Each stage also
-// holds the tile's scale words (one 32-bit word per row: the four 32-K blocks), copied
-// 4 bytes per lane. Step 1's fragment reads are spread between step 0's MFMAs. A partial
-// last K tile goes through registers with zero elements and unit scales past K.
+// sub-tiles. Whole K tiles stream HBM -> LDS with direct copies (global_load_lds, 1 KiB of
+// LDS per copy) into three stages (two when an 8-bit operand meets a 6-bit one: three do
+// not fit), the copy of tile kt + NST issued as soon as every wave is done reading tile kt,
+// so the copies have NST - 1 K tiles of multiplies to land in (one K tile of 6- or 4-bit
+// operands is only 1024 MFMA cycles). Each row's 16-byte chunks are permuted (by the
+// copies' global addresses) so that the 16 rows one 16-lane group reads at one offset fall
+// in distinct banks: chunk c of row r sits at c ^ ((r >> 1) & 7) for 128-byte rows,
+// (c + ((r >> 3) & 1)) % 6 for 96-byte rows and c ^ ((r >> 2) & 3) for 64-byte rows. Each
+// stage also holds the tile's scale words (one 32-bit word per row: the four 32-K blocks),
+// copied 4 bytes per lane. Step 1's fragment reads are spread between step 0's MFMAs. A
+// partial last K tile goes through registers with zero elements and unit scales past K.
 #include "gemm_common.hpp"
 #include "../../include/bsm.h"
 
@@ -39,18 +42,25 @@ template <int C>
 struct Op {
   static constexpr int BITS = fmt_bits(C);
   static constexpr int ROW = 16 * BITS;   // bytes of a row per K tile: 128, 96, 64
-  static constexpr int PITCH = ROW + 16;  // LDS row pitch
-  static constexpr int TILE = 256 * PITCH;
+  static constexpr int TILE = 256 * ROW;
   static constexpr int CPR = ROW / 16;    // 16-byte chunks per row per K tile (and per lane)
+  // physical chunk of logical chunk c in row r, and back
+  __device__ static int phys(int c, int r) {
+    return CPR == 8 ? c ^ ((r >> 1) & 7) : (CPR == 6 ? (c + ((r >> 3) & 1)) % 6 : c ^ ((r >> 2) & 3));
+  }
+  __device__ static int logical(int pc, int r) {
+    return CPR == 8 ? pc ^ ((r >> 1) & 7) : (CPR == 6 ? (pc + 6 - ((r >> 3) & 1)) % 6 : pc ^ ((r >> 2) & 3));
+  }
 };
 
 // A stage: A tile, B tile, then the K tile's scale words of A's and B's 256 rows (4 bytes
-// each: the four 32-K blocks of the tile).
+// each: the four 32-K blocks of the tile). NST stages of the 160 KiB of LDS.
 template <int CA, int CB>
 struct Lay {
   static constexpr int SCALES = Op<CA>::TILE + Op<CB>::TILE;
   static constexpr int STAGE = SCALES + 2048;
-  static constexpr int BYTES = 2 * STAGE > 131072 ? 2 * STAGE : 131072;  // the epilogue uses 128 KiB
+  static constexpr int NST = 3 * STAGE <= 163840 ? 3 : 2;
+  static constexpr int BYTES = NST * STAGE > 131072 ? NST * STAGE : 131072;  // the epilogue uses 128 KiB
 };
 
 __device__ __forceinline__ uint2 lds_read_b64(const void* p) {
@@ -108,7 +118,7 @@ __device__ __forceinline__ void store_chunks(uint8_t* tile, int q, const uint4 (
 #pragma unroll
   for (int i = 0; i < P::CPR; i++) {
     const int c = q + 256 * i, r = c / P::CPR, cc = c - r * P::CPR;
-    lds_write_b128(tile + r * P::PITCH + 16 * cc, v[i]);
+    lds_write_b128(tile + r * P::ROW + 16 * P::phys(cc, r), v[i]);
   }
 }
 
@@ -139,20 +149,22 @@ __device__ __forceinline__ void read_scales(const uint8_t* area, int base, int l
 template <int C>
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t, int s, int lane) {
   typedef Op<C> P;
-  const int h = lane >> 5;
-  const uint8_t* row = tile + (base + 32 * t + (lane & 31)) * P::PITCH;
+  const int h = lane >> 5, r = base + 32 * t + (lane & 31);
+  const uint8_t* row = tile + r * P::ROW;
+  // logical byte offset o of the row -> its place in the permuted row
+  auto at = [&](int o) { return row + 16 * P::phys(o >> 4, r) + (o & 15); };
   i32x8 v;
   if (P::BITS == 8) {
-    const uint4 x = lds_read_b128(row + 64 * s + 16 * h), y = lds_read_b128(row + 64 * s + 32 + 16 * h);
+    const uint4 x = lds_read_b128(at(64 * s + 16 * h)), y = lds_read_b128(at(64 * s + 32 + 16 * h));
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
   } else if (P::BITS == 6) {
-    const uint8_t* p = row + 48 * s + 24 * h;
-    const uint2 x = lds_read_b64(p), y = lds_read_b64(p + 8), z = lds_read_b64(p + 16);
+    const int o = 48 * s + 24 * h;
+    const uint2 x = lds_read_b64(at(o)), y = lds_read_b64(at(o + 8)), z = lds_read_b64(at(o + 16));
     v[0] = x.x; v[1] = x.y; v[2] = y.x; v[3] = y.y; v[4] = z.x; v[5] = z.y;
     v[6] = v[7] = 0;
   } else {
-    const uint4 x = lds_read_b128(row + 32 * s + 16 * h);
+    const uint4 x = lds_read_b128(at(32 * s + 16 * h));
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     v[4] = v[5] = v[6] = v[7] = 0;
   }
@@ -215,15 +227,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   gemm::zero_acc(acc);
   // Direct copies of one stage: NA (NB) 1 KiB copies for the A (B) tile, copy j going to
   // wave j % 4, then one 256-byte scale copy per operand per wave.
-  constexpr int NA = PA::PITCH / 4, NB = PB::PITCH / 4;   // = 256 * PITCH / 1024
-  constexpr int DA = NA / 4, DB = NB / 4, DPW = DA + DB + 2;
+  constexpr int NA = PA::ROW / 4, NB = PB::ROW / 4;   // = 256 * ROW / 1024
+  constexpr int DA = NA / 4, DB = NB / 4, DPW = DA + DB + 2, NST = L::NST;
   uint32_t oa[DA], ob[DB], osa, osb;
   {
+    // lane l of copy j lands at LDS chunk 64 (w + 4j) + l of the tile: row p / CPR, physical
+    // chunk p % CPR, which holds the row's logical chunk `logical(...)`
     auto offs = [&](auto P, int64_t ld_bytes, int64_t rows, int j) -> uint32_t {
       typedef decltype(P) PP;
-      const int p = 1024 * (w + 4 * j) + 16 * lane;
-      const int r = p / PP::PITCH, slot = (p - r * PP::PITCH) >> 4;
-      return (uint32_t)(min((int64_t)r, rows - 1) * ld_bytes + (slot < PP::CPR ? 16 * slot : 0));
+      const int p = 64 * (w + 4 * j) + lane;
+      const int r = p / PP::CPR, pc = p - r * PP::CPR;
+      return (uint32_t)(min((int64_t)r, rows - 1) * ld_bytes + 16 * PP::logical(pc, r));
     };
 #pragma unroll
     for (int j = 0; j < DA; j++) oa[j] = offs(PA{}, lda_b, rows_a, j);
@@ -235,17 +249,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   const uint8_t* SA = a.SFA + m0 * a.ld_sfa;
   const uint8_t* SB = a.SFB + n0 * a.ld_sfb;
   const uint32_t lds0 = gemm::lds_addr(lds);
-  auto issue = [&](int kt, int stage) {
+  // Copy d (of DPW) of tile kt into stage `stage`.
+  auto copy = [&](int kt, int stage, int d) {
     const uint32_t st = lds0 + stage * L::STAGE;
-#pragma unroll
-    for (int j = 0; j < DA; j++) gemm::dma16s(A + kt * PA::ROW, oa[j], st + 1024 * (w + 4 * j));
-#pragma unroll
-    for (int j = 0; j < DB; j++) gemm::dma16s(B + kt * PB::ROW, ob[j], st + PA::TILE + 1024 * (w + 4 * j));
-    gemm::dma4s(SA + 4 * kt, osa, st + L::SCALES + 256 * w);
-    gemm::dma4s(SB + 4 * kt, osb, st + L::SCALES + 1024 + 256 * w);
+    if (d < DA) gemm::dma16s(A + kt * PA::ROW, oa[d], st + 1024 * (w + 4 * d));
+    else if (d < DA + DB) gemm::dma16s(B + kt * PB::ROW, ob[d - DA], st + PA::TILE + 1024 * (w + 4 * (d - DA)));
+    else if (d == DA + DB) gemm::dma4s(SA + 4 * kt, osa, st + L::SCALES + 256 * w);
+    else gemm::dma4s(SB + 4 * kt, osb, st + L::SCALES + 1024 + 256 * w);
   };
-  // Multiply the tile in stage st: step 1's fragment reads go out between step 0's MFMAs.
-  auto multiply = [&](const uint8_t* st) {
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int d = 0; d < DPW; d++) copy(kt, stage, d);
+  };
+  static_assert(DPW <= 16, "one copy per MFMA slot of step 1");
+  // Multiply the tile in stage st: step 1's fragment reads go out between step 0's MFMAs;
+  // then every wave is done with the stage (barrier) and side1(i) runs after step 1's
+  // MFMA i (the copies of the tile that replaces this one, spread one per MFMA slot:
+  // issued in one burst they would hold the waves behind the shared copy path).
+  auto multiply = [&](const uint8_t* st, auto side1) {
     uint32_t sa[4], sb[4];
     i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
     read_scales(st + L::SCALES, wa, lane, sa);
@@ -257,23 +278,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
         else fa1[i >> 1] = read_frag<CA>(st, wa, i >> 1, 1, lane);
       }
     });
-    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [](int) {});
+    gemm::lds_barrier();
+    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, side1);
   };
 
-  // Whole K tiles. Past the last one the copies re-read the last tile into the stage just
-  // released (nobody reads it again), so every iteration issues the same copies and the
-  // wait counts stay fixed.
+  // Whole K tiles; tile kt lives in stage kt % NST. Past the last one the copies re-read
+  // the last tile into the stage just released (nobody reads it again), so every
+  // iteration issues the same copies and the wait counts stay fixed.
   const int nfull = (int)(a.K / KT);
   if (nfull > 0) {
-    issue(0, 0);
-    issue(min(1, nfull - 1), 1);
-    gemm::stage_barrier<DPW>();
+#pragma unroll
+    for (int i = 0; i < NST; i++) issue(min(i, nfull - 1), i);
+    gemm::stage_barrier<(NST - 1) * DPW>();  // tile 0 has landed
   }
+  int cur = 0;                               // kt % NST
   for (int kt = 0; kt < nfull; kt++) {
-    multiply(lds + (kt & 1) * L::STAGE);
-    gemm::lds_barrier();                     // every wave is done with this stage
-    issue(min(kt + 2, nfull - 1), kt & 1);
-    gemm::stage_barrier<DPW>();              // tile kt + 1 has landed
+    const int knext = min(kt + NST, nfull - 1);
+    multiply(lds + cur * L::STAGE, [&](int i) {
+      if (i < DPW) copy(knext, cur, i);
+    });
+    gemm::stage_barrier<(NST - 1) * DPW>();  // tile kt + 1 has landed
+    cur = cur + 1 == NST ? 0 : cur + 1;
   }
   gemm::wait_dma();                          // the repeated copies too, before LDS is reused
   __syncthreads();
@@ -283,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     uint32_t roa[PA::CPR], rob[PB::CPR];
     row_offsets<CA>(lda_b, rows_a, q, roa);
     row_offsets<CB>(ldb_b, rows_b, q, rob);
-    uint8_t* st = lds + (nfull & 1) * L::STAGE;
+    uint8_t* st = lds;                       // every copy has landed: any stage will do
     load_chunks_tail<CA>(A, roa, nfull, ka, q, va);
     load_chunks_tail<CB>(B, rob, nfull, kb, q, vb);
     const uint32_t wsa = mask_scale_word(load_scale_word(a.SFA, a.ld_sfa, m0, a.M, q, nfull), nfull, nblk);
@@ -293,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     *(BSM_LDS uint32_t*)(st + L::SCALES + 4 * q) = wsa;
     *(BSM_LDS uint32_t*)(st + L::SCALES + 1024 + 4 * q) = wsb;
     __syncthreads();
-    multiply(st);
+    multiply(st, [](int) {});
     __syncthreads();
   }
   gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, a.accum != 0,

@@ -1,5 +1,6 @@
 // k_gemm_mx.hip - block-scaled GEMM (MXFP8 E4M3 or E5M2 / MXFP4 E2M1 with E8M0 scales per 32
-// K elements) D = s * A * B^T (+ D) on gfx950 v_mfma_scale_f32_32x32x64_f8f6f4.
+// K elements) D = s * A * B^T (+ D) on gfx950 v_mfma_scale_f32_32x32x64_f8f6f4. The other
+// pairings (6-bit formats, mixed widths) go to the general kernel of k_gemm_mx_any.hip.
 //
 // Semantics ("tcgen05.mma": Weight-stationary and block scaling, Call parameters;
 // "Explicit CUDA tile patterns": tcgen05 MMA): operand value = element * 2^(scale-127)

@@ -153,6 +153,35 @@ def box_store(mem: np.ndarray, dtype: str, dims, strides, box, estr, coords, ima
         raise ValueError(f"oracle_box_store rc={rc}")
 
 
+def repeat_coords(coords, repeats, steps) -> np.ndarray:
+    """Box coordinates of a call with repeat axes ("cp.async.bulk.tensor", Call parameters:
+    coord_steps holds one increment vector per repeat axis; Code generation: one box per
+    repeat coordinate, row-major over the repeat axes): box t = (j_0, .., j_{n-1}) in
+    row-major order starts at coords + sum_a j_a * steps[a]. Shape (prod(repeats), rank)."""
+    coords = np.asarray(coords, np.int64)
+    out = []
+    for js in np.ndindex(*repeats) if len(repeats) else [()]:
+        c = coords.copy()
+        for a, j in enumerate(js):
+            c = c + j * np.asarray(steps[a], np.int64)
+        out.append(c)
+    return np.array(out, np.int64).reshape(-1, coords.size)
+
+
+def box_load_steps(mem, dtype, dims, strides, box, estr, coords, repeats, steps, swz=0, fill=0) -> np.ndarray:
+    """Images of every repeat coordinate, concatenated (each image_stride bytes)."""
+    return np.concatenate([box_load(mem, dtype, dims, strides, box, estr, c, swz, fill)
+                           for c in repeat_coords(coords, repeats, steps)])
+
+
+def box_store_steps(mem, dtype, dims, strides, box, estr, coords, repeats, steps, images, swz=0, reduce_add=0):
+    """In place on ``mem``: image t (of image_stride bytes) to repeat coordinate t, in order."""
+    st = image_stride(dtype, box, estr, swz)
+    images = np.ascontiguousarray(images).reshape(-1)
+    for t, c in enumerate(repeat_coords(coords, repeats, steps)):
+        box_store(mem, dtype, dims, strides, box, estr, c, images[t * st:(t + 1) * st], swz, reduce_add)
+
+
 def gather4(mem: np.ndarray, dtype: str, dims, strides, width: int, col: int, rows, swz=0, fill=0) -> np.ndarray:
     """Image bytes of one four-row gather: a (4, width) image, length = the image stride of
     a (4, width) box."""

@@ -231,3 +231,37 @@ def test_ldmatrix_transpose_identity(O, nmat):
                 lo, hi = int(regs[lane, i]) & 0xFFFF, int(regs[lane, i]) >> 16
                 src = S[i].T if trans else S[i]
                 assert (lo, hi) == (src[j, 2 * w], src[j, 2 * w + 1])
+
+
+# ----------------------------------------------------------------------------- repeats (coord_steps)
+def test_pages_two_box_example_as_coord_steps(O):
+    """The same example as written on the page: coords (0,0), coord_steps ((8,0),) over a
+    repeat axis of 2 -> boxes at (0,0) and (8,0), images in repeat order."""
+    exp = np.loadtxt(os.path.join(GOLD, "tma_two_box_expected.txt"), dtype=np.uint64).astype(np.uint32)
+    x = np.arange(256, dtype=np.uint32).reshape(16, 16)
+    assert O.repeat_coords((0, 0), (2,), ((8, 0),)).tolist() == [[0, 0], [8, 0]]
+    imgs = O.box_load_steps(x, "u32", (16, 16), (64, 4), (8, 16), (1, 1), (0, 0), (2,), ((8, 0),))
+    assert imgs.size == 1024                              # 512 bytes per box, two boxes
+    assert np.array_equal(imgs.view(np.uint32).reshape(16, 16), exp)
+
+
+def test_repeat_coords_row_major_and_steps_vs_numpy_slicing(O):
+    """Two repeat axes (3 x 2), negative steps and out-of-range boxes: box t of the
+    row-major repeat order equals numpy slicing at coords + j0 s0 + j1 s1."""
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 1 << 16, (20, 30, 40), dtype=np.uint64).astype(np.uint16)
+    coords, reps, steps = (2, 5, -3), (3, 2), ((6, -4, 0), (0, 7, 16))
+    rc = O.repeat_coords(coords, reps, steps)
+    assert rc.tolist() == [[2 + 6 * a, 5 - 4 * a + 7 * b, -3 + 16 * b] for a in range(3) for b in range(2)]
+    box = (4, 5, 16)
+    imgs = O.box_load_steps(x, "u16", x.shape, x.strides, box, (1, 1, 1), coords, reps, steps, 0, 0)
+    st = O.image_stride("u16", box, (1, 1, 1), 0)
+    for t, c in enumerate(rc):
+        want = _numpy_box(x, 0, box, (1, 1, 1), c)
+        assert np.array_equal(imgs[t * st:t * st + want.nbytes].view(np.uint16).reshape(box), want)
+    y = np.zeros_like(x)
+    O.box_store_steps(y, "u16", x.shape, x.strides, box, (1, 1, 1), coords, reps, steps, imgs)
+    z = np.zeros_like(x)
+    for t, c in enumerate(rc):
+        O.box_store(z, "u16", x.shape, x.strides, box, (1, 1, 1), c, imgs[t * st:(t + 1) * st])
+    assert np.array_equal(y, z) and y.any()

@@ -22,7 +22,7 @@ STATUS = {0: "BSM_OK", -1: "BSM_E_NULL", -2: "BSM_E_RANK", -3: "BSM_E_BOX", -4: 
           -10: "BSM_E_MAJOR", -11: "BSM_E_ALIAS", -12: "BSM_E_HIP", -13: "BSM_E_ARG"}
 EWISE = {"none": 0, "silu_affine": 1}
 EXPORTS = ("bsm_image_stride", "bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy",
-           "bsm_tile_gather4", "bsm_tile_scatter4", "bsm_gemm",
+           "bsm_tile_box_load_steps", "bsm_tile_box_store_steps", "bsm_tile_gather4", "bsm_tile_scatter4", "bsm_gemm",
            "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise", "bsm_tile_add_scalar_f32", "bsm_debug_fragments",
            "bsm_debug_fragment_shape", "bsm_last_error")
 
@@ -67,6 +67,8 @@ def lib():
         L.bsm_tile_box_store.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I64, P, C.c_int, P]
         L.bsm_tile_box_copy.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_tensor), C.POINTER(bsm_tensor),
                                         C.POINTER(bsm_box), P]
+        L.bsm_tile_box_load_steps.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I32, P, P, P, P]
+        L.bsm_tile_box_store_steps.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I32, P, P, P, C.c_int, P]
         L.bsm_tile_gather4.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I64, P, P]
         L.bsm_tile_scatter4.argtypes = [C.POINTER(bsm_tensor), C.POINTER(bsm_box), P, I64, P, P]
         L.bsm_gemm.argtypes = [I64, I64, I64, I32, P, I64, C.c_char, P, I64, C.c_char, P, I64, C.c_int, C.c_int,
@@ -79,7 +81,8 @@ def lib():
         L.bsm_debug_fragments.argtypes = [P, I64, I64, C.c_char, P, P]
         L.bsm_debug_fragment_shape.restype = None
         L.bsm_debug_fragment_shape.argtypes = [C.POINTER(I64), C.POINTER(I64)]
-        for rc_fn in ("bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_tile_gather4",
+        for rc_fn in ("bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy", "bsm_tile_box_load_steps",
+                      "bsm_tile_box_store_steps", "bsm_tile_gather4",
                       "bsm_tile_scatter4", "bsm_gemm",
                       "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise",
                       "bsm_tile_add_scalar_f32", "bsm_debug_fragments"):
@@ -160,6 +163,32 @@ def bsm_tile_box_copy(src: bsm_tensor, dst: bsm_tensor | None, dst_add: bsm_tens
     _check(lib().bsm_tile_box_copy(C.byref(src), C.byref(dst) if dst is not None else None,
                                    C.byref(dst_add) if dst_add is not None else None, C.byref(box),
                                    _stream(stream)))
+
+
+def _host_i64(xs):
+    a = (C.c_int64 * max(len(xs), 1))(*[int(x) for x in xs])
+    return a
+
+
+def _repeat_args(coords, repeats, steps):
+    rank = len(coords)
+    flat = [int(v) for st in steps for v in st]
+    assert len(flat) == rank * len(repeats)
+    return (_host_i64(coords), len(repeats), (C.c_int32 * max(len(repeats), 1))(*[int(r) for r in repeats]),
+            _host_i64(flat))
+
+
+def bsm_tile_box_load_steps(src: bsm_tensor, box: bsm_box, coords, repeats, steps, images, stream=None):
+    """coords: rank ints; repeats: one extent per repeat axis; steps: one rank-length vector per axis."""
+    c, n, r, s = _repeat_args(coords, repeats, steps)
+    _check(lib().bsm_tile_box_load_steps(C.byref(src), C.byref(box), c, n, r, s, _ptr(images), _stream(stream)))
+
+
+def bsm_tile_box_store_steps(dst: bsm_tensor, box: bsm_box, coords, repeats, steps, images, reduce_add: int = 0,
+                             stream=None):
+    c, n, r, s = _repeat_args(coords, repeats, steps)
+    _check(lib().bsm_tile_box_store_steps(C.byref(dst), C.byref(box), c, n, r, s, _ptr(images), reduce_add,
+                                          _stream(stream)))
 
 
 def bsm_tile_gather4(src: bsm_tensor, box: bsm_box, coords, n_issues: int, images, stream=None):

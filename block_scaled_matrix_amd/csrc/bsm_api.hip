@@ -169,8 +169,8 @@ int64_t bsm_image_stride(const bsm_box* box, int32_t dtype) {
   return g.image_stride;
 }
 
-int bsm_tile_box_load(const bsm_tensor* src, const bsm_box* box, const int32_t* coords_dev, int64_t n_boxes,
-                      void* images, void* stream) {
+static int box_load_impl(const bsm_tensor* src, const bsm_box* box, const int32_t* coords_dev,
+                         const bsm::BoxRepeat* rp, int64_t n_boxes, void* images, void* stream, const char* name) {
   int rc = check_tensor(src, "src");
   if (rc) return rc;
   bsm::BoxGeom g;
@@ -178,21 +178,24 @@ int bsm_tile_box_load(const bsm_tensor* src, const bsm_box* box, const int32_t* 
   if (box->rank != src->rank) return fail(BSM_E_RANK, "box rank %d != tensor rank %d", box->rank, src->rank);
   if (n_boxes < 0 || n_boxes > 0x7FFFFFFF) return fail(BSM_E_SHAPE, "n_boxes %lld out of range", (long long)n_boxes);
   if (n_boxes == 0) return ok();
-  if (!coords_dev) return fail(BSM_E_NULL, "coords is NULL");
+  if (!rp && !coords_dev) return fail(BSM_E_NULL, "coords is NULL");
   if (!images) return fail(BSM_E_NULL, "images is NULL");
-  if ((uintptr_t)coords_dev % 4) return fail(BSM_E_ALIGN, "coords not 4-byte aligned");
+  if (!rp && (uintptr_t)coords_dev % 4) return fail(BSM_E_ALIGN, "coords not 4-byte aligned");
   const uintptr_t ia = box->swizzle ? (uintptr_t(1) << (7 + box->swizzle)) : 128;
   if ((uintptr_t)images % ia) return fail(BSM_E_ALIGN, "images not %u-byte aligned", (unsigned)ia);
   Range ir{(uintptr_t)images, (uintptr_t)images + (uintptr_t)(n_boxes * g.image_stride)};
   if (overlap(ir, tensor_range(src))) return fail(BSM_E_ALIAS, "images overlap src");
   fill_tensor_geom(src, &g);
-  hipError_t e = bsm::launch_box_load(g, src->base, coords_dev, n_boxes, images, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "bsm_tile_box_load");
+  const bsm::BoxRepeat none{};
+  hipError_t e = bsm::launch_box_load(g, src->base, rp ? nullptr : coords_dev, rp ? *rp : none, n_boxes, images,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
   return ok();
 }
 
-int bsm_tile_box_store(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev, int64_t n_boxes,
-                       const void* images, int reduce_add, void* stream) {
+static int box_store_impl(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev,
+                          const bsm::BoxRepeat* rp, int64_t n_boxes, const void* images, int reduce_add, void* stream,
+                          const char* name) {
   int rc = check_tensor(dst, "dst");
   if (rc) return rc;
   bsm::BoxGeom g;
@@ -203,17 +206,83 @@ int bsm_tile_box_store(const bsm_tensor* dst, const bsm_box* box, const int32_t*
     return fail(BSM_E_DTYPE, "add-reduction needs an F32, F16 or BF16 destination (got %d)", dst->dtype);
   if (n_boxes < 0 || n_boxes > 0x7FFFFFFF) return fail(BSM_E_SHAPE, "n_boxes %lld out of range", (long long)n_boxes);
   if (n_boxes == 0) return ok();
-  if (!coords_dev) return fail(BSM_E_NULL, "coords is NULL");
+  if (!rp && !coords_dev) return fail(BSM_E_NULL, "coords is NULL");
   if (!images) return fail(BSM_E_NULL, "images is NULL");
-  if ((uintptr_t)coords_dev % 4) return fail(BSM_E_ALIGN, "coords not 4-byte aligned");
+  if (!rp && (uintptr_t)coords_dev % 4) return fail(BSM_E_ALIGN, "coords not 4-byte aligned");
   const uintptr_t ia = box->swizzle ? (uintptr_t(1) << (7 + box->swizzle)) : 128;
   if ((uintptr_t)images % ia) return fail(BSM_E_ALIGN, "images not %u-byte aligned", (unsigned)ia);
   Range ir{(uintptr_t)images, (uintptr_t)images + (uintptr_t)(n_boxes * g.image_stride)};
   if (overlap(ir, tensor_range(dst))) return fail(BSM_E_ALIAS, "images overlap dst");
   fill_tensor_geom(dst, &g);
-  hipError_t e = bsm::launch_box_store(g, dst->base, coords_dev, n_boxes, images, reduce_add, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "bsm_tile_box_store");
+  const bsm::BoxRepeat none{};
+  hipError_t e = bsm::launch_box_store(g, dst->base, rp ? nullptr : coords_dev, rp ? *rp : none, n_boxes, images,
+                                       reduce_add, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
   return ok();
+}
+
+// Repeat axes of a box call: checks them and every coordinate they generate against the
+// 32-bit range the kernels use; n_boxes = product of the repeat extents.
+static int make_repeat(const bsm_box* box, const int64_t* coords, int32_t n_axes, const int32_t* repeats,
+                       const int64_t* steps, bsm::BoxRepeat* rp, int64_t* n_boxes) {
+  if (!box) return fail(BSM_E_NULL, "box descriptor is NULL");
+  if (box->rank < 1 || box->rank > 5) return fail(BSM_E_RANK, "box rank %d not in 1..5", box->rank);
+  if (!coords) return fail(BSM_E_NULL, "coords is NULL");
+  if (n_axes < 0 || n_axes > 4) return fail(BSM_E_ARG, "n_axes = %d not in 0..4", n_axes);
+  if (n_axes > 0 && (!repeats || !steps)) return fail(BSM_E_NULL, "repeats or steps is NULL");
+  memset(rp, 0, sizeof *rp);
+  rp->naxes = n_axes;
+  int64_t n = 1;
+  for (int a = 0; a < n_axes; a++) {
+    if (repeats[a] < 1) return fail(BSM_E_SHAPE, "repeats[%d] = %d is not positive", a, repeats[a]);
+    n *= repeats[a];
+    if (n > 0x7FFFFFFF) return fail(BSM_E_SHAPE, "more than 2^31 - 1 boxes");
+    rp->rep[a] = repeats[a];
+  }
+  const int64_t lim = int64_t(1) << 31;
+  for (int i = 0; i < box->rank; i++) {
+    __int128 lo = coords[i], hi = coords[i];
+    for (int a = 0; a < n_axes; a++) {
+      const __int128 d = (__int128)(repeats[a] - 1) * steps[a * box->rank + i];
+      if (d < 0) lo += d; else hi += d;
+      if (steps[a * box->rank + i] < -lim || steps[a * box->rank + i] >= lim)
+        return fail(BSM_E_SHAPE, "steps[%d][%d] outside the 32-bit range", a, i);
+      rp->step[a][i] = (int32_t)steps[a * box->rank + i];
+    }
+    if (lo < -lim || hi >= lim) return fail(BSM_E_SHAPE, "a repeat coordinate of dimension %d leaves the 32-bit range", i);
+    rp->base[i] = (int32_t)coords[i];
+  }
+  *n_boxes = n;
+  return BSM_OK;
+}
+
+int bsm_tile_box_load(const bsm_tensor* src, const bsm_box* box, const int32_t* coords_dev, int64_t n_boxes,
+                      void* images, void* stream) {
+  return box_load_impl(src, box, coords_dev, nullptr, n_boxes, images, stream, "bsm_tile_box_load");
+}
+
+int bsm_tile_box_store(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev, int64_t n_boxes,
+                       const void* images, int reduce_add, void* stream) {
+  return box_store_impl(dst, box, coords_dev, nullptr, n_boxes, images, reduce_add, stream, "bsm_tile_box_store");
+}
+
+int bsm_tile_box_load_steps(const bsm_tensor* src, const bsm_box* box, const int64_t* coords, int32_t n_axes,
+                            const int32_t* repeats, const int64_t* steps, void* images, void* stream) {
+  bsm::BoxRepeat rp;
+  int64_t n = 0;
+  int rc = make_repeat(box, coords, n_axes, repeats, steps, &rp, &n);
+  if (rc) return rc;
+  return box_load_impl(src, box, nullptr, &rp, n, images, stream, "bsm_tile_box_load_steps");
+}
+
+int bsm_tile_box_store_steps(const bsm_tensor* dst, const bsm_box* box, const int64_t* coords, int32_t n_axes,
+                             const int32_t* repeats, const int64_t* steps, const void* images, int reduce_add,
+                             void* stream) {
+  bsm::BoxRepeat rp;
+  int64_t n = 0;
+  int rc = make_repeat(box, coords, n_axes, repeats, steps, &rp, &n);
+  if (rc) return rc;
+  return box_store_impl(dst, box, nullptr, &rp, n, images, reduce_add, stream, "bsm_tile_box_store_steps");
 }
 
 int bsm_tile_box_copy(const bsm_tensor* src, const bsm_tensor* dst, const bsm_tensor* dst_add, const bsm_box* box,

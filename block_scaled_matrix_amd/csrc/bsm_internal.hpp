@@ -34,9 +34,20 @@ hipError_t launch_empty_gemm(float* D, int64_t ldd, int64_t M, int64_t N, int ac
 
 hipError_t launch_add_scalar_f32(const float* src, float* dst, int64_t n, float s, hipStream_t st);
 
-hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coords, int64_t n_boxes,
-                           void* images, hipStream_t st);
-hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, int64_t n_boxes,
+// Box coordinates generated on the device for a call with repeat axes: box t (row-major
+// over rep[0..naxes)) starts at base + sum_a j_a * step[a]. The host has checked that every
+// such coordinate fits in 32 bits.
+struct BoxRepeat {
+  int32_t naxes;       // 0..4
+  int32_t rep[4];
+  int32_t base[5];
+  int32_t step[4][5];
+};
+
+// coords: DEVICE array of n_boxes * rank int32, or NULL to generate them from rp.
+hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coords, const BoxRepeat& rp,
+                           int64_t n_boxes, void* images, hipStream_t st);
+hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, const BoxRepeat& rp, int64_t n_boxes,
                             const void* images, int reduce_add, hipStream_t st);
 // Four-row gather (scatter = 0: tensor -> images) or scatter (1: images -> tensor) of
 // n_issues issues; g describes the rank-2 tensor and the (4, width) image; coords holds

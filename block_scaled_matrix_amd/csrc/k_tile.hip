@@ -222,12 +222,35 @@ __device__ __forceinline__ void scatter_chunk(const BoxGeom& g, uint8_t* dst, co
 }
 
 // ------------------------------------------------------------------ box load / store
+// Coordinates of box t: from the device array, or generated from the repeat axes
+// ("cp.async.bulk.tensor", Call parameters: coord_steps; one box per repeat coordinate in
+// row-major repeat order).
+__device__ __forceinline__ void box_coords(const BoxGeom& g, const int32_t* coords, const BoxRepeat& rp, uint32_t t,
+                                           int32_t (&c)[5]) {
+  if (coords) {
+#pragma unroll
+    for (int i = 0; i < 5; i++) c[i] = i < g.rank ? coords[(int64_t)t * g.rank + i] : 0;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 5; i++) c[i] = i < g.rank ? rp.base[i] : 0;
+#pragma unroll
+  for (int a = 3; a >= 0; a--) {
+    if (a < rp.naxes) {
+      const uint32_t j = t % (uint32_t)rp.rep[a];
+      t /= (uint32_t)rp.rep[a];
+#pragma unroll
+      for (int i = 0; i < 5; i++) c[i] += (int32_t)j * rp.step[a][i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_box_load(BoxGeom g, const uint8_t* __restrict__ src,
-                                                  const int32_t* __restrict__ coords, uint8_t* __restrict__ images) {
+                                                  const int32_t* __restrict__ coords, BoxRepeat rp,
+                                                  uint8_t* __restrict__ images) {
   const int64_t t = blockIdx.x;
   int32_t c[5];
-#pragma unroll
-  for (int i = 0; i < 5; i++) c[i] = i < g.rank ? coords[t * g.rank + i] : 0;
+  box_coords(g, coords, rp, (uint32_t)t, c);
   uint8_t* img = images + t * g.image_stride;
   const int cpr = g.row_bytes >> 4;
   const int nchunks = g.nrows * cpr;
@@ -239,11 +262,10 @@ __global__ __launch_bounds__(256) void k_box_load(BoxGeom g, const uint8_t* __re
 }
 
 __global__ __launch_bounds__(256) void k_box_store(BoxGeom g, uint8_t* dst, const int32_t* __restrict__ coords,
-                                                   const uint8_t* __restrict__ images, int reduce) {
+                                                   BoxRepeat rp, const uint8_t* __restrict__ images, int reduce) {
   const int64_t t = blockIdx.x;
   int32_t c[5];
-#pragma unroll
-  for (int i = 0; i < 5; i++) c[i] = i < g.rank ? coords[t * g.rank + i] : 0;
+  box_coords(g, coords, rp, (uint32_t)t, c);
   const uint8_t* img = images + t * g.image_stride;
   const int cpr = g.row_bytes >> 4;
   const int nchunks = g.nrows * cpr;
@@ -254,16 +276,16 @@ __global__ __launch_bounds__(256) void k_box_store(BoxGeom g, uint8_t* dst, cons
   }
 }
 
-hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coords, int64_t n_boxes, void* images,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(k_box_load, dim3((unsigned)n_boxes), dim3(256), 0, st, g, (const uint8_t*)src, coords,
+hipError_t launch_box_load(const BoxGeom& g, const void* src, const int32_t* coords, const BoxRepeat& rp,
+                           int64_t n_boxes, void* images, hipStream_t st) {
+  hipLaunchKernelGGL(k_box_load, dim3((unsigned)n_boxes), dim3(256), 0, st, g, (const uint8_t*)src, coords, rp,
                      (uint8_t*)images);
   return hipGetLastError();
 }
 
-hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, int64_t n_boxes, const void* images,
-                            int reduce_add, hipStream_t st) {
-  hipLaunchKernelGGL(k_box_store, dim3((unsigned)n_boxes), dim3(256), 0, st, g, (uint8_t*)dst, coords,
+hipError_t launch_box_store(const BoxGeom& g, void* dst, const int32_t* coords, const BoxRepeat& rp, int64_t n_boxes,
+                            const void* images, int reduce_add, hipStream_t st) {
+  hipLaunchKernelGGL(k_box_store, dim3((unsigned)n_boxes), dim3(256), 0, st, g, (uint8_t*)dst, coords, rp,
                      (const uint8_t*)images, reduce_add);
   return hipGetLastError();
 }

@@ -130,6 +130,27 @@ int bsm_tile_box_load(const bsm_tensor* src, const bsm_box* box, const int32_t* 
 int bsm_tile_box_store(const bsm_tensor* dst, const bsm_box* box, const int32_t* coords_dev,
                        int64_t n_boxes, const void* images, int reduce_add, void* stream);
 
+/* Box load and store / add-reduction with repeat axes ([TMA] "Call parameters": coords
+ * plus coord_steps, one increment vector per repeat axis; "Code generation": one box per
+ * repeat coordinate, in row-major repeat order; "Example: two explicit 8x16 boxes" is
+ * coords (0, 0), coord_steps ((8, 0),) over one repeat axis of 2):
+ *   coords:  HOST array of rank int64 starting coordinates, outer to inner;
+ *   n_axes:  number of repeat axes, 0..4 (0: one box at coords);
+ *   repeats: HOST array of n_axes extents, each >= 1, their product <= 2^31 - 1;
+ *   steps:   HOST array of n_axes * rank int64 increments, axis a's vector at
+ *            [a * rank, a * rank + rank);
+ * box t, t = row-major index of (j_0, .., j_{n_axes-1}), has coordinates
+ * coords + sum_a j_a * steps[a] and its image sits at t * bsm_image_stride(). The host
+ * arrays are read during the call only. Every generated coordinate must fit in 32 bits
+ * (BSM_E_SHAPE otherwise); n_axes outside 0..4 -> BSM_E_ARG; coords, or repeats / steps
+ * with n_axes > 0, NULL -> BSM_E_NULL. Everything else as for bsm_tile_box_load /
+ * bsm_tile_box_store (the coordinates need no device array). */
+int bsm_tile_box_load_steps(const bsm_tensor* src, const bsm_box* box, const int64_t* coords, int32_t n_axes,
+                            const int32_t* repeats, const int64_t* steps, void* images, void* stream);
+int bsm_tile_box_store_steps(const bsm_tensor* dst, const bsm_box* box, const int64_t* coords, int32_t n_axes,
+                             const int32_t* repeats, const int64_t* steps, const void* images, int reduce_add,
+                             void* stream);
+
 /* Four-row gather, global -> image ([TMA] "Gather4 and scatter4"; [TP] "TMA"): a
  * rank-2 tensor, a box of one row (box->box = {1, width}, element strides {1, 1}) and,
  * per issue, four explicit row coordinates that need not be consecutive or distinct.

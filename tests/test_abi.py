@@ -89,6 +89,20 @@ def test_box_contract_violations(L):
     expect("BSM_E_SHAPE", cp, src, tensor(dims=(64, 32), base=FAKE + (1 << 30)), None, b, 0)
     expect("BSM_E_DTYPE", cp, src, tensor("f16", base=FAKE + (1 << 30)), None, b, 0)
     expect("BSM_E_DTYPE", cp, tensor("u16"), None, tensor("u16", base=FAKE + (1 << 30)), b, 0)
+    sl = lambda *a: bsm.bsm_tile_box_load_steps(*a, stream=0)
+    expect("BSM_E_ARG", sl, tensor(), b, (0, 0), (1, 1, 1, 1, 1), [(0, 0)] * 5, FAKE + (1 << 30))  # 5 axes
+    expect("BSM_E_SHAPE", sl, tensor(), b, (0, 0), (0,), [(8, 0)], FAKE + (1 << 30))              # empty axis
+    expect("BSM_E_SHAPE", sl, tensor(), b, (0, 0), (3,), [(1 << 30, 0)], FAKE + (1 << 30))        # 2^31 reached
+    expect("BSM_E_SHAPE", sl, tensor(), b, (0, -(1 << 31)), (2,), [(0, -1)], FAKE + (1 << 30))    # below -2^31
+    expect("BSM_E_SHAPE", sl, tensor(), b, (0, 0), (1 << 16, 1 << 16), [(0, 0), (0, 0)], FAKE + (1 << 30))
+    expect("BSM_E_RANK", sl, tensor(), bsm.box_desc((16, 64, 8)), (0, 0, 0), (), [], FAKE + (1 << 30))
+    expect("BSM_E_NULL", sl, tensor(), b, (0, 0), (2,), [(8, 0)], 0)                              # images NULL
+    expect("BSM_E_ALIAS", sl, tensor(), b, (0, 0), (2,), [(8, 0)], FAKE + 1024)
+    expect("BSM_E_NULL", lambda: bsm._check(L.bsm_tile_box_load_steps(C.byref(tensor()), C.byref(b), None, 0, None,
+                                                                      None, C.c_void_p(FAKE + (1 << 30)), None)))
+    ss = lambda *a: bsm.bsm_tile_box_store_steps(*a, stream=0)
+    expect("BSM_E_DTYPE", ss, tensor("u16"), b, (0, 0), (2,), [(8, 0)], FAKE + (1 << 30), 1)
+    expect("BSM_E_ARG", ss, tensor(), b, (0, 0), (2,), [(8, 0)], FAKE + (1 << 30), 2)
     g4 = bsm.box_desc((1, 64), (1, 1), 3)
     for fn in (bsm.bsm_tile_gather4, bsm.bsm_tile_scatter4):
         call = lambda t, bx, co=FAKE, n=1, img=FAKE + (1 << 30), fn=fn: fn(t, bx, co, n, img, 0)

@@ -220,3 +220,75 @@ def test_box_copy_full_size_vs_oracle(O):
     assert np.array_equal(got_d, dst)
     assert np.array_equal(got_a, add)
     assert np.array_equal(got_d[:, :cols], w["src"][:, :cols]) and (got_d[:, cols:] == W.SENTINEL_BF16).all()
+
+
+# ----------------------------------------------------------------------------- repeat axes
+def test_box_load_steps_pages_example(O):
+    """cp.async.bulk.tensor, Example: two explicit 8x16 boxes, written as on the page: coords
+    (0, 0), coord_steps ((8, 0),) over one repeat axis of 2."""
+    x = np.arange(256, dtype=np.uint32).reshape(16, 16)
+    say("box_load_steps pages example")
+    dimg = dev_like(1024, 0xA5)
+    bsm.bsm_tile_box_load_steps(bsm.tensor_desc(dev(x), "u32", (16, 16), (64, 4)), bsm.box_desc((8, 16)), (0, 0), (2,),
+                                [(8, 0)], dimg)
+    got = host(dimg, np.uint8)
+    assert np.array_equal(got, O.box_load_steps(x, "u32", (16, 16), (64, 4), (8, 16), (1, 1), (0, 0), (2,), [(8, 0)]))
+    assert np.array_equal(got.view(np.uint32).reshape(16, 16), x)
+
+
+@pytest.mark.parametrize("dtype,swz", [("bf16", 3), ("u8", 0), ("f32", 1), ("e4m3", 2)])
+def test_box_steps_vs_oracle(O, dtype, swz):
+    """Rank 3, two repeat axes (3 x 4) with negative and zero steps, boxes partly out of range:
+    images against the oracle; then the images stored back with the same repeats."""
+    rng = np.random.default_rng([11, bsm.DTYPE[dtype], swz])
+    esz = bsm.ESIZE[dtype]
+    inner = {0: 48 // esz, 1: 32 // esz, 2: 64 // esz, 3: 128 // esz}[swz]
+    dims = (9, 23, 3 * inner + 5)
+    pitch = (dims[2] * esz + 15) // 16 * 16 // esz + 16 // esz
+    mem = rng.integers(0, 1 << (8 * esz), (dims[0], dims[1], pitch), dtype=np.uint64).astype(NPDT[dtype])
+    strides = (mem.strides[0], mem.strides[1], esz)
+    box, estr = (2, 5, inner), (1, 2, 1)
+    coords, reps, steps = (-1, 3, inner - 3), (3, 4), [(3, -2, 0), (0, 6, inner)]
+    fill = 1 if dtype in ("bf16", "f32", "e4m3") else 0
+    stride = O.image_stride(dtype, box, estr, swz)
+    n = 12
+    say("box_load_steps", dtype, swz, dims, box, reps)
+    dimg = dev_like(n * stride, 0xA5)
+    td = bsm.tensor_desc(dev(mem), dtype, dims, strides)
+    bd = bsm.box_desc(box, estr, swz, fill)
+    bsm.bsm_tile_box_load_steps(td, bd, coords, reps, steps, dimg)
+    got = host(dimg, np.uint8).reshape(n, stride)
+    exp = O.box_load_steps(mem, dtype, dims, strides, box, estr, coords, reps, steps, swz, fill).reshape(n, stride)
+    nbytes = int(np.prod(O.image_extents(box, estr))) * esz
+    written = np.zeros(stride, bool)
+    written[[O.swizzle(o, swz) for o in range(nbytes)]] = True
+    assert np.array_equal(got[:, written], exp[:, written])
+    assert (got[:, ~written] == 0xA5).all()
+    # store back into a sentinel tensor (boxes overlap: equal bytes wherever they do, since
+    # every image came from the same source)
+    say("box_store_steps", dtype, swz)
+    sent = np.full_like(mem, 0x3C if esz == 1 else 0x3C00)
+    dd = dev(sent)
+    bsm.bsm_tile_box_store_steps(bsm.tensor_desc(dd, dtype, dims, strides), bd, coords, reps, steps, dimg)
+    want = sent.copy()
+    O.box_store_steps(want, dtype, dims, strides, box, estr, coords, reps, steps, got, swz)
+    assert np.array_equal(host(dd, NPDT[dtype], mem.shape), want)
+
+
+def test_box_store_steps_reduce_add(O):
+    """Add-reduction with repeat axes onto disjoint boxes (a 3 x 2 grid of (16, 32) bf16 boxes)."""
+    rng = np.random.default_rng(12)
+    dims = (48, 64)
+    base = W.to_half_bits(rng.standard_normal(dims).astype(np.float32), "bf16")
+    box = (16, 32)
+    stride = O.image_stride("bf16", box, (1, 1), 3)
+    imgs = W.to_half_bits(rng.standard_normal(6 * stride // 2).astype(np.float32), "bf16").view(np.uint8)
+    say("box_store_steps reduce")
+    dd = dev(base)
+    dimg = dev_like(6 * stride, 0)
+    dimg.copy_(torch.from_numpy(imgs.copy()))
+    bsm.bsm_tile_box_store_steps(bsm.tensor_desc(dd, "bf16", dims, (128, 2)), bsm.box_desc(box, (1, 1), 3, 0), (0, 0),
+                                 (3, 2), [(16, 0), (0, 32)], dimg, 1)
+    want = base.copy()
+    O.box_store_steps(want, "bf16", dims, (128, 2), box, (1, 1), (0, 0), (3, 2), [(16, 0), (0, 32)], imgs, 3, 1)
+    assert np.array_equal(host(dd, np.uint16, dims), want)

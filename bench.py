@@ -24,6 +24,8 @@ reported under `widened` (not part of `value`):
              rows four at a time from a seeded permutation, 1 048 576 issues (512 MiB of images)
   scatter4   the images scattered to the rows of a second permutation (a row permutation of
              the table)
+  box_load_rank3   a bf16 (64, 2048, 2048) tensor into (2, 64, 128) box images at element
+             strides (1, 2, 1), the 32 x 32 x 16 boxes given as repeat axes (one call)
   gemm_e4m3_e2m1   block-scaled M=N=8192, K=16384, A E4M3, B E2M1 (mixed widths), fresh D
   gemm_e2m3_e2m3   block-scaled M=N=8192, K=16384, both FP6 E2M3, fresh D
 (the mixed pair runs at the 8-bit MFMA rate, peak 5033.2 TFLOP/s; FP6 pairs at the 4-bit
@@ -59,6 +61,7 @@ KERNEL_SOURCES = {
     "add_one": ["k_tile.hip", "bsm_device.hpp"],
     "gather4": ["k_tile.hip", "bsm_device.hpp"],
     "scatter4": ["k_tile.hip", "bsm_device.hpp"],
+    "box_load_rank3": ["k_tile.hip", "bsm_device.hpp"],
     "gemm_e4m3_e2m1": ["k_gemm_mx_any.hip", "gemm_common.hpp", "bsm_device.hpp"],
     "gemm_e2m3_e2m3": ["k_gemm_mx_any.hip", "gemm_common.hpp", "bsm_device.hpp"],
 }
@@ -167,6 +170,14 @@ def make_inputs():
         inp[key] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
         inp[key]["D"] = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
     log(f"mixed / fp6 GEMM inputs {time.time() - t0:.1f}s")
+    b3 = W.box_rank3_bf16()
+    inp["b3"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in b3.items()}
+    n3 = int(np.prod(b3["repeats"]))
+    img3 = 2 * 32 * 128 * 2                     # (2, 32, 128) bf16 image, already a multiple of 128 bytes
+    raw3 = torch.empty(n3 * img3 + 1024, dtype=torch.uint8, device="cuda")
+    off3 = (-raw3.data_ptr()) % 1024
+    inp["b3"]["images"] = raw3[off3:off3 + n3 * img3]
+    log(f"rank-3 box inputs {time.time() - t0:.1f}s")
     return inp
 
 
@@ -227,7 +238,14 @@ def widened(inp):
                                                 x["ld_sfa"], x["b_fmt"], x["B"], x["ldb"], x["SFB"], x["ld_sfb"],
                                                 x["D"], x["N"], 0, 0, 0)
     flops = 2.0 * 8192 * 8192 * 16384
+    b3 = inp["b3"]
+    d3 = b3["dims"]
+    t3 = bsm.tensor_desc(b3["x"], "bf16", d3, (d3[1] * d3[2] * 2, d3[2] * 2, 2))
+    bx3 = bsm.box_desc(b3["box"], b3["estr"], 0, 0)
+    bytes3 = 2 * (d3[0] * d3[1] // 2 * d3[2] * 2)   # the sampled half of the rows read, written as images
     return [
+        ("box_load_rank3", lambda: bsm.bsm_tile_box_load_steps(t3, bx3, b3["coords"], b3["repeats"], b3["steps"],
+                                                               b3["images"]), bytes3, "GB/s", PEAK["hbm_GBs"]),
         ("gather4", lambda: bsm.bsm_tile_gather4(src, box, g["gather"], n, g["images"]), nbytes, "GB/s",
          PEAK["hbm_GBs"]),
         ("scatter4", lambda: bsm.bsm_tile_scatter4(dst, box, g["scatter"], n, g["images"]), nbytes, "GB/s",

@@ -18,6 +18,8 @@ Workloads (sizes are the ones the benchmark runs):
                     E8M0 scales 127+U{-4..4}, both K-major, fresh D, seed 4.
   mxfp4_16384_8192  M=16384, N=8192, K=8192, E2M1 bytes uniform (two uniform nibbles),
                     E8M0 scales 127+U{-6..6}, neg_a, fresh D, seed 5.
+  box_rank3_bf16    a bf16 (64, 2048, 2048) tensor N(0,1), seed 7, read as (2, 64, 128) boxes
+                    with element strides (1, 2, 1) tiling it (32 x 32 x 16 repeats).
   gather4_bf16      a bf16 65536x4096 table N(0,1), seed 6; four-row gathers with a (1,64)
                     box and 128-byte swizzle (512-byte images), rows taken four at a time
                     from a seeded permutation, every 64-column block of each row group;
@@ -157,6 +159,18 @@ def gather4_bf16(seed: int = 6, rows: int = 65536, cols: int = 4096, width: int 
     return {"rows": rows, "cols": cols, "width": width, "table": table, "gather": coords(perm_g),
             "scatter": coords(perm_s), "perm_gather": perm_g, "perm_scatter": perm_s, "swizzle": 3, "fill": 0,
             "dtype": "bf16"}
+
+
+def box_rank3_bf16(seed: int = 7, dims=(64, 2048, 2048)):
+    """A rank-3 bf16 tensor and the repeat axes that tile it with (2, 64, 128) boxes sampled at
+    element strides (1, 2, 1)."""
+    rng = np.random.default_rng(seed)
+    x = to_half_bits(rng.standard_normal(dims, dtype=np.float32), "bf16")
+    box, estr = (2, 64, 128), (1, 2, 1)
+    reps = tuple(d // b for d, b in zip(dims, box))
+    steps = [tuple(box[i] if i == a else 0 for i in range(3)) for a in range(3)]
+    return {"x": x, "dims": dims, "box": box, "estr": estr, "coords": (0, 0, 0), "repeats": reps, "steps": steps,
+            "swizzle": 0, "fill": 0, "dtype": "bf16"}
 
 
 def sample_points(M: int, N: int, n: int, seed: int = 99):

@@ -292,3 +292,27 @@ def test_box_store_steps_reduce_add(O):
     want = base.copy()
     O.box_store_steps(want, "bf16", dims, (128, 2), box, (1, 1), (0, 0), (3, 2), [(16, 0), (0, 32)], imgs, 3, 1)
     assert np.array_equal(host(dd, np.uint16, dims), want)
+
+
+def test_box_load_steps_rank3_full_size(O):
+    """The timed rank-3 workload: a bf16 (64, 2048, 2048) tensor tiled by (2, 64, 128) boxes at
+    element strides (1, 2, 1) through repeat axes (32 x 32 x 16 boxes): 256 sampled boxes
+    against the oracle, every image against numpy slicing of the tensor."""
+    w = W.box_rank3_bf16()
+    x, dims, box, estr = w["x"], w["dims"], w["box"], w["estr"]
+    strides = (dims[1] * dims[2] * 2, dims[2] * 2, 2)
+    bd = bsm.box_desc(box, estr, 0, 0)
+    stride = bsm.bsm_image_stride(bd, "bf16")
+    reps = w["repeats"]
+    n = int(np.prod(reps))
+    say("box_load_steps rank3 full", dims, box, estr, n)
+    dimg = dev_like(n * stride, 0)
+    bsm.bsm_tile_box_load_steps(bsm.tensor_desc(dev(x), "bf16", dims, strides), bd, w["coords"], reps, w["steps"], dimg)
+    got = host(dimg, np.uint8).reshape(n, stride)
+    rc = O.repeat_coords(w["coords"], reps, w["steps"])
+    for t in np.random.default_rng(3).integers(0, n, 256):
+        assert np.array_equal(got[t], O.box_load(x, "bf16", dims, strides, box, estr, rc[t])), t
+    # image (a, b, c) = x[2a:2a+2, 64b:64b+64:2, 128c:128c+128], row-major over (a, b, c)
+    v = x.reshape(reps[0], 2, reps[1], 32, 2, reps[2], 128)[:, :, :, :, 0, :, :]
+    want = np.ascontiguousarray(v.transpose(0, 2, 4, 1, 3, 5)).reshape(n, -1)
+    assert np.array_equal(got.view(np.uint16), want)

@@ -557,17 +557,18 @@ int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int dtype,
 // block-scaled kinds carry 8-bit scale factors per K group; [TP] "tcgen05 MMA").
 // Reading (OCP MX v1.0, section 5): one E8M0 scale per 32 consecutive K
 // elements starting at k = 0; the operand value is decode(element) * 2^(s-127).
-// K-major storage only: element (r,k) at index r*ld + k; for packed E2M1 that
-// index selects byte idx/2 and the low nibble for even idx; for the 6-bit formats,
-// bits 6 idx .. 6 idx + 5 of the operand's little-endian bit string (ld * 6 is a
-// multiple of 8, so every row starts on a byte).
+// Storage ([MMA] "Call parameters": a_major / b_major select "k" or "mn"): K-major
+// element (r,k) at index r*ld + k, MN-major (K rows, M or N contiguous) at k*ld + r; for
+// packed E2M1 the index selects byte idx/2 and the low nibble for even idx; for the 6-bit
+// formats, bits 6 idx .. 6 idx + 5 of the operand's little-endian bit string (ld * 6 is a
+// multiple of 8, so every row starts on a byte). Scales stay per (r, k/32) either way.
 static bool mx_fmt(int f) {
   return f == OD_E4M3 || f == OD_E5M2 || f == OD_E2M1 || f == OD_E2M3 || f == OD_E3M2;
 }
 
-static double load_op_scaled(int fmt, const uint8_t* p, int64_t ld, const uint8_t* sf,
+static double load_op_scaled(int fmt, const uint8_t* p, int64_t ld, int mn, const uint8_t* sf,
                              int64_t ld_sf, int64_t r, int64_t k) {
-  int64_t idx = r * ld + k;
+  int64_t idx = mn ? k * ld + r : r * ld + k;
   double v;
   if (fmt == OD_E4M3) v = oracle_dec_e4m3(p[idx]);
   else if (fmt == OD_E5M2) v = oracle_dec_e5m2(p[idx]);
@@ -581,7 +582,7 @@ int oracle_gemm_block_scale(int64_t M, int64_t N, int64_t K,
                             int a_fmt, const void* A, int64_t lda, const uint8_t* SFA, int64_t ld_sfa,
                             int b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
                             const float* D0, int64_t ldd, int neg_a, int neg_b, int accum,
-                            int64_t m_begin, int64_t m_end, double* ref, double* bound) {
+                            int64_t m_begin, int64_t m_end, double* ref, double* bound, int a_mn, int b_mn) {
   if (!mx_fmt(a_fmt) || !mx_fmt(b_fmt)) return -1;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || m_begin < 0 || m_end > M || m_begin > m_end) return -2;
   if (accum && !D0) return -4;
@@ -593,8 +594,8 @@ int oracle_gemm_block_scale(int64_t M, int64_t N, int64_t K,
     for (int64_t n = 0; n < N; n++) {
       double s = 0.0, b = 0.0;
       for (int64_t k = 0; k < K; k++) {
-        double a = load_op_scaled(a_fmt, pa, lda, SFA, ld_sfa, m, k);
-        double bb = load_op_scaled(b_fmt, pb, ldb, SFB, ld_sfb, n, k);
+        double a = load_op_scaled(a_fmt, pa, lda, a_mn, SFA, ld_sfa, m, k);
+        double bb = load_op_scaled(b_fmt, pb, ldb, b_mn, SFB, ld_sfb, n, k);
         s += a * bb;
         b += std::fabs(a * bb);
       }
@@ -611,7 +612,7 @@ int oracle_gemm_block_scale_points(int64_t M, int64_t N, int64_t K,
                                    int b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
                                    const float* D0, int64_t ldd, int neg_a, int neg_b, int accum,
                                    const int64_t* pm, const int64_t* pn, int64_t npts,
-                                   double* ref, double* bound) {
+                                   double* ref, double* bound, int a_mn, int b_mn) {
   if (!mx_fmt(a_fmt) || !mx_fmt(b_fmt)) return -1;
   if (K % 32 != 0) return -2;
   if (accum && !D0) return -4;
@@ -624,8 +625,8 @@ int oracle_gemm_block_scale_points(int64_t M, int64_t N, int64_t K,
     const int64_t m = pm[i], n = pn[i];
     double s = 0.0, b = 0.0;
     for (int64_t k = 0; k < K; k++) {
-      double a = load_op_scaled(a_fmt, pa, lda, SFA, ld_sfa, m, k);
-      double bb = load_op_scaled(b_fmt, pb, ldb, SFB, ld_sfb, n, k);
+      double a = load_op_scaled(a_fmt, pa, lda, a_mn, SFA, ld_sfa, m, k);
+      double bb = load_op_scaled(b_fmt, pb, ldb, b_mn, SFB, ld_sfb, n, k);
       s += a * bb;
       b += std::fabs(a * bb);
     }

@@ -73,9 +73,9 @@ def lib():
         L.oracle_gemm_points.argtypes = [I64, I64, I64, I32, P, I64, I32, P, I64, I32, P, I64,
                                          I32, I32, I32, P, P, I64, P, P]
         L.oracle_gemm_block_scale.argtypes = [I64, I64, I64, I32, P, I64, P, I64, I32, P, I64, P, I64,
-                                              P, I64, I32, I32, I32, I64, I64, P, P]
+                                              P, I64, I32, I32, I32, I64, I64, P, P, I32, I32]
         L.oracle_gemm_block_scale_points.argtypes = [I64, I64, I64, I32, P, I64, P, I64, I32, P, I64,
-                                                     P, I64, P, I64, I32, I32, I32, P, P, I64, P, P]
+                                                     P, I64, P, I64, I32, I32, I32, P, P, I64, P, P, I32, I32]
         L.oracle_check_gemm.restype = I64
         L.oracle_check_gemm.argtypes = [P, I64, I64, I64, P, P, D, P, P]
         L.oracle_ewise_silu_affine.argtypes = [P, I64, D, D, P]
@@ -264,7 +264,8 @@ def gemm_points(M, N, K, dtype, A, lda, a_major, B, ldb, b_major, D0, ldd, neg_a
 
 
 def gemm_block_scale(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld_sfb, D0=None, ldd=0,
-                     neg_a=0, neg_b=0, accum=0, m_begin=0, m_end=None):
+                     neg_a=0, neg_b=0, accum=0, m_begin=0, m_end=None, a_major="k", b_major="k"):
+    """a_major 'k' or 'm', b_major 'k' or 'n': MN-major operands store (K rows, M or N contiguous)."""
     m_end = M if m_end is None else m_end
     A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
     SFA, SFB = np.ascontiguousarray(SFA, dtype=np.uint8), np.ascontiguousarray(SFB, dtype=np.uint8)
@@ -273,14 +274,14 @@ def gemm_block_scale(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld
     bound = np.empty_like(ref)
     rc = lib().oracle_gemm_block_scale(M, N, K, DT[a_fmt], _p(A), lda, _p(SFA), ld_sfa, DT[b_fmt], _p(B), ldb,
                                        _p(SFB), ld_sfb, _p(D0), ldd, neg_a, neg_b, accum, m_begin, m_end,
-                                       _p(ref), _p(bound))
+                                       _p(ref), _p(bound), int(a_major != "k"), int(b_major != "k"))
     if rc:
         raise ValueError(f"oracle_gemm_block_scale rc={rc}")
     return ref, bound
 
 
 def gemm_block_scale_points(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld_sfb, D0, ldd,
-                            neg_a, neg_b, accum, pm, pn):
+                            neg_a, neg_b, accum, pm, pn, a_major="k", b_major="k"):
     A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
     SFA, SFB = np.ascontiguousarray(SFA, dtype=np.uint8), np.ascontiguousarray(SFB, dtype=np.uint8)
     D0 = None if D0 is None else np.ascontiguousarray(D0, dtype=np.float32)
@@ -289,7 +290,8 @@ def gemm_block_scale_points(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, 
     bound = np.empty_like(ref)
     rc = lib().oracle_gemm_block_scale_points(M, N, K, DT[a_fmt], _p(A), lda, _p(SFA), ld_sfa, DT[b_fmt], _p(B),
                                               ldb, _p(SFB), ld_sfb, _p(D0), ldd, neg_a, neg_b, accum,
-                                              _p(pm), _p(pn), pm.size, _p(ref), _p(bound))
+                                              _p(pm), _p(pn), pm.size, _p(ref), _p(bound), int(a_major != "k"),
+                                              int(b_major != "k"))
     if rc:
         raise ValueError(f"oracle_gemm_block_scale_points rc={rc}")
     return ref, bound

@@ -283,3 +283,39 @@ def test_block_scale_any_pair_vs_numpy_brute_force(O, a_fmt, b_fmt):
         exp = (d0.astype(np.float64) if accum else 0.0) + (-1.0) ** (neg_a + neg_b) * (av @ bv.T)
         np.testing.assert_allclose(ref, exp, rtol=0, atol=1e-12 * (1 + (np.abs(av) @ np.abs(bv).T).max()))
         np.testing.assert_allclose(bound, np.abs(av) @ np.abs(bv).T, rtol=1e-12)
+
+
+def transpose_codes(raw, fmt, rows, K):
+    """K-major packed codes (rows, K) -> MN-major packed codes (K, rows), by numpy: unpack the
+    elements (bytes, nibbles low first, or 6-bit fields), transpose, repack."""
+    bits = W.BITS[fmt]
+    r = np.ascontiguousarray(raw).reshape(rows, -1)
+    if bits == 8:
+        return np.ascontiguousarray(r[:, :K].T)
+    if bits == 4:
+        codes = np.stack([r & 15, r >> 4], axis=2).reshape(rows, -1)[:, :K].T
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    bs = np.unpackbits(r, axis=1, bitorder="little")[:, :6 * K].reshape(rows, K, 6)
+    codes = (bs * (1 << np.arange(6))).sum(axis=2).T
+    return W.pack_fp6(np.ascontiguousarray(codes))
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt,amaj,bmaj", [("e4m3", "e4m3", "m", "k"), ("e2m1", "e2m1", "k", "n"),
+                                                   ("e5m2", "e2m1", "m", "n"), ("e2m3", "e4m3", "m", "k")])
+def test_block_scale_mn_major_vs_numpy(O, a_fmt, b_fmt, amaj, bmaj):
+    """MN-major operands (K rows, M or N contiguous): the oracle on storage transposed by numpy
+    against numpy matmul of the values decoded from the original K-major codes."""
+    rng = np.random.default_rng(23)
+    for trial in range(4):
+        M, N = int(rng.choice(SIZES)) * 4, int(rng.choice(SIZES)) * 4     # whole bytes of packed elements
+        K = int(rng.choice([32, 64, 96]))
+        g = W.mx_pair(80 + trial, M, N, K, a_fmt, b_fmt)
+        A = transpose_codes(g["A"], a_fmt, M, K) if amaj == "m" else g["A"]
+        B = transpose_codes(g["B"], b_fmt, N, K) if bmaj == "n" else g["B"]
+        lda, ldb = (M if amaj == "m" else K), (N if bmaj == "n" else K)
+        ref, bound = O.gemm_block_scale(M, N, K, a_fmt, A, lda, g["SFA"], K // 32, b_fmt, B, ldb, g["SFB"], K // 32,
+                                        a_major=amaj, b_major=bmaj)
+        av = scaled(any_vals(g["A"], a_fmt, M, K), g["SFA"])
+        bv = scaled(any_vals(g["B"], b_fmt, N, K), g["SFB"])
+        np.testing.assert_allclose(ref, av @ bv.T, rtol=0, atol=1e-12 * (1 + (np.abs(av) @ np.abs(bv).T).max()))
+        np.testing.assert_allclose(bound, np.abs(av) @ np.abs(bv).T, rtol=1e-12)

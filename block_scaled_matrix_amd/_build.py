@@ -9,7 +9,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsm.so")
-SOURCES = ["bsm_api.hip", "k_tile.hip", "k_gemm_dense.hip", "k_gemm_mx.hip", "k_gemm_mx_any.hip"]
+SOURCES = ["bsm_api.hip", "k_tile.hip", "k_gemm_dense.hip", "k_gemm_mx.hip", "k_gemm_mx_any.hip",
+           "k_gemm_mx_mn_a.hip", "k_gemm_mx_mn_b.hip", "k_gemm_mx_mn_ab.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: never emit packed fp32 arithmetic (v_pk_*_f32).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -26,7 +27,7 @@ def _compile(src: str, obj: str) -> None:
             print(line)
 
 
-def build(jobs: int = 4) -> str:
+def build(jobs: int = min(8, os.cpu_count() or 4)) -> str:
     """Compile every source for gfx950 and link libbsm.so next to this file."""
     with tempfile.TemporaryDirectory(prefix="bsm_build_") as tmp:
         objs = [os.path.join(tmp, s.replace(".hip", ".o")) for s in SOURCES]

@@ -416,9 +416,9 @@ int bsm_gemm_ewise(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, i
 }
 
 static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
-                            const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
-                            const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
-                            const bsm_ewise& ew, void* stream, const char* name) {
+                            char a_major, const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B,
+                            int64_t ldb, char b_major, const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd,
+                            int neg_a, int neg_b, int accum, const bsm_ewise& ew, void* stream, const char* name) {
   int rc;
   if ((rc = check_flag(neg_a, "neg_a")) || (rc = check_flag(neg_b, "neg_b")) || (rc = check_flag(accum, "accum")))
     return rc;
@@ -429,6 +429,10 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
   if (!ba || !bb)
     return fail(BSM_E_DTYPE, "a_fmt %d / b_fmt %d: block-scaled GEMM takes E4M3, E5M2, E2M3, E3M2 or E2M1", a_fmt,
                 b_fmt);
+  if (a_major != 'k' && a_major != 'm') return fail(BSM_E_MAJOR, "a_major '%c' is not 'k' or 'm'", a_major);
+  if (b_major != 'k' && b_major != 'n') return fail(BSM_E_MAJOR, "b_major '%c' is not 'k' or 'n'", b_major);
+  if ((a_major == 'm' && ba == 6) || (b_major == 'n' && bb == 6))
+    return fail(BSM_E_MAJOR, "MN-major block-scaled operands are E4M3, E5M2 or E2M1 (not the 6-bit formats)");
   if (M < 0 || N < 0 || K < 0 || M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
     return fail(BSM_E_SHAPE, "M, N, K = %lld, %lld, %lld out of range", (long long)M, (long long)N, (long long)K);
   if (K % 32) return fail(BSM_E_SHAPE, "K = %lld is not a multiple of the 32-element scale block", (long long)K);
@@ -437,7 +441,11 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
   if (K > 0) {
     if (!A || !B || !SFA || !SFB) return fail(BSM_E_NULL, "A, B, SFA or SFB is NULL");
     if ((uintptr_t)A % 16 || (uintptr_t)B % 16) return fail(BSM_E_ALIGN, "A and B must be 16-byte aligned");
-    if (lda < K || ldb < K) return fail(BSM_E_ALIGN, "lda, ldb must be >= K");
+    // (rows, row length) of each operand's storage
+    const int64_t arows = a_major == 'k' ? M : K, alen = a_major == 'k' ? K : M;
+    const int64_t brows = b_major == 'k' ? N : K, blen = b_major == 'k' ? K : N;
+    if (lda < alen) return fail(BSM_E_ALIGN, "lda = %lld must be >= %lld", (long long)lda, (long long)alen);
+    if (ldb < blen) return fail(BSM_E_ALIGN, "ldb = %lld must be >= %lld", (long long)ldb, (long long)blen);
     if ((lda * ba) % 128 || (ldb * bb) % 128)
       return fail(BSM_E_ALIGN, "lda = %lld, ldb = %lld: rows must start 16-byte aligned", (long long)lda, (long long)ldb);
     if (ld_sfa < K / 32 || ld_sfb < K / 32) return fail(BSM_E_ALIGN, "ld_sfa, ld_sfb must be >= K/32");
@@ -447,8 +455,8 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
         ld_sfb > (int64_t(1) << 24))
       return fail(BSM_E_SHAPE, "leading dimensions too large for 32-bit in-tile offsets");
     const Range rd{(uintptr_t)D, (uintptr_t)(D + (M - 1) * ldd + N)};
-    const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(((M - 1) * lda + K) * ba / 8)};
-    const Range rb{(uintptr_t)B, (uintptr_t)B + (uintptr_t)(((N - 1) * ldb + K) * bb / 8)};
+    const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(((arows - 1) * lda + alen) * ba / 8)};
+    const Range rb{(uintptr_t)B, (uintptr_t)B + (uintptr_t)(((brows - 1) * ldb + blen) * bb / 8)};
     const Range rsa{(uintptr_t)SFA, (uintptr_t)SFA + (uintptr_t)(M * ld_sfa)};
     const Range rsb{(uintptr_t)SFB, (uintptr_t)SFB + (uintptr_t)(N * ld_sfb)};
     if (overlap(rd, ra) || overlap(rd, rb) || overlap(rd, rsa) || overlap(rd, rsb))
@@ -456,8 +464,8 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
   }
   bsm::GemmArgs g{};
   g.M = M; g.N = N; g.K = K; g.dtype = a_fmt; g.dtype_b = b_fmt;
-  g.A = A; g.lda = lda; g.a_kmajor = 1;
-  g.B = B; g.ldb = ldb; g.b_kmajor = 1;
+  g.A = A; g.lda = lda; g.a_kmajor = a_major == 'k';
+  g.B = B; g.ldb = ldb; g.b_kmajor = b_major == 'k';
   g.SFA = SFA; g.ld_sfa = ld_sfa; g.SFB = SFB; g.ld_sfb = ld_sfb;
   g.D = D; g.ldd = ldd; g.negate = neg_a ^ neg_b; g.accum = accum;
   g.ew_op = ew.op; g.ew_scale = ew.scale; g.ew_bias = ew.bias;
@@ -470,8 +478,8 @@ int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const v
                          const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
                          const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b, int accum,
                          void* stream) {
-  return gemm_block_scale(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld_sfb, D, ldd, neg_a, neg_b,
-                          accum, bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream, "bsm_gemm_block_scale");
+  return gemm_block_scale(M, N, K, a_fmt, A, lda, 'k', SFA, ld_sfa, b_fmt, B, ldb, 'k', SFB, ld_sfb, D, ldd, neg_a,
+                          neg_b, accum, bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream, "bsm_gemm_block_scale");
 }
 
 int bsm_gemm_block_scale_ewise(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
@@ -480,8 +488,19 @@ int bsm_gemm_block_scale_ewise(int64_t M, int64_t N, int64_t K, int32_t a_fmt, c
                                int accum, const bsm_ewise* ew, void* stream) {
   int rc;
   if ((rc = check_ewise(ew))) return rc;
-  return gemm_block_scale(M, N, K, a_fmt, A, lda, SFA, ld_sfa, b_fmt, B, ldb, SFB, ld_sfb, D, ldd, neg_a, neg_b,
-                          accum, *ew, stream, "bsm_gemm_block_scale_ewise");
+  return gemm_block_scale(M, N, K, a_fmt, A, lda, 'k', SFA, ld_sfa, b_fmt, B, ldb, 'k', SFB, ld_sfb, D, ldd, neg_a,
+                          neg_b, accum, *ew, stream, "bsm_gemm_block_scale_ewise");
+}
+
+int bsm_gemm_block_scale_major(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
+                               char a_major, const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B,
+                               int64_t ldb, char b_major, const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd,
+                               int neg_a, int neg_b, int accum, const bsm_ewise* ew, void* stream) {
+  int rc;
+  if (ew && (rc = check_ewise(ew))) return rc;
+  return gemm_block_scale(M, N, K, a_fmt, A, lda, a_major, SFA, ld_sfa, b_fmt, B, ldb, b_major, SFB, ld_sfb, D, ldd,
+                          neg_a, neg_b, accum, ew ? *ew : bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream,
+                          "bsm_gemm_block_scale_major");
 }
 
 int bsm_tile_add_scalar_f32(const float* src, float* dst, int64_t n, float s, void* stream) {

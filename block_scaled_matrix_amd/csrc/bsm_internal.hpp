@@ -77,6 +77,11 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
 // Any pairing of E4M3, E5M2, E2M3, E3M2, E2M1 except 8-bit x 8-bit and E2M1 x E2M1 (K > 0).
 hipError_t launch_gemm_mx_any(const GemmArgs& a, hipStream_t st);
+// One or both operands MN-major (A only, B only, both); an MN-major operand is E4M3, E5M2 or
+// E2M1 (K > 0).
+hipError_t launch_gemm_mx_mn_a(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mx_mn_b(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mx_mn_ab(const GemmArgs& a, hipStream_t st);
 
 // Operand-tile geometry of the dense GEMM (rows x K elements per LDS stage).
 constexpr int kDenseTileRows = 256;

@@ -1,6 +1,7 @@
 // k_gemm_mx.hip - block-scaled GEMM (MXFP8 E4M3 or E5M2 / MXFP4 E2M1 with E8M0 scales per 32
-// K elements) D = s * A * B^T (+ D) on gfx950 v_mfma_scale_f32_32x32x64_f8f6f4. The other
-// pairings (6-bit formats, mixed widths) go to the general kernel of k_gemm_mx_any.hip.
+// K elements) D = s * A * B^T (+ D) on gfx950 v_mfma_scale_f32_32x32x64_f8f6f4, K-major
+// operands. The other pairings (6-bit formats, mixed widths) and MN-major operands go to
+// the general kernel (gemm_mx_any.hpp; k_gemm_mx_any.hip, k_gemm_mx_mn_*.hip).
 //
 // Semantics ("tcgen05.mma": Weight-stationary and block scaling, Call parameters;
 // "Explicit CUDA tile patterns": tcgen05 MMA): operand value = element * 2^(scale-127)
@@ -415,6 +416,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
   if (a.K == 0) return launch_empty_gemm(a.D, a.ldd, a.M, a.N, a.accum, a.ew_op, a.ew_scale, a.ew_bias, st);
   const bool byte_a = a.dtype == BSM_E4M3 || a.dtype == BSM_E5M2, byte_b = a.dtype_b == BSM_E4M3 || a.dtype_b == BSM_E5M2;
+  if (!a.a_kmajor && !a.b_kmajor) return launch_gemm_mx_mn_ab(a, st);
+  if (!a.a_kmajor) return launch_gemm_mx_mn_a(a, st);
+  if (!a.b_kmajor) return launch_gemm_mx_mn_b(a, st);
   if (!(byte_a && byte_b) && !(a.dtype == BSM_E2M1 && a.dtype_b == BSM_E2M1)) return launch_gemm_mx_any(a, st);
   const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;

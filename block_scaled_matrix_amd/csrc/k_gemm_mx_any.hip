@@ -1,377 +1,10 @@
-// k_gemm_mx_any.hip - block-scaled GEMM for any pairing of the f8f6f4 element formats
-// (E4M3, E5M2, E2M3, E3M2, E2M1) on gfx950 v_mfma_scale_f32_32x32x64_f8f6f4: the 6-bit
-// formats and operands of different widths (say E4M3 x E2M1). Pairs of equal width that
-// the tuned kernel of k_gemm_mx.hip covers (8-bit x 8-bit, E2M1 x E2M1) do not come here.
-//
-// Semantics as there ("tcgen05.mma": Weight-stationary and block scaling; "Explicit CUDA
-// tile patterns": tcgen05 MMA): value = element * 2^(scale - 127), one scale per 32 K of a
-// row, float32 accumulation, D = s * A * B^T (+ D), then the scalar epilogue.
-//
-// Operand registers (probed on the device; each operand follows its own format's layout,
-// so mixed pairs need no conversion):
-//  - 8-bit: lane l holds row l%32, k in [16(l/32), +16) and [32 + 16(l/32), +16) of the
-//    64-K step (two 16-byte groups);
-//  - 6-bit: lane l holds row l%32, k in [32(l/32), +32): 24 bytes, element i at bits
-//    6i .. 6i+5 (the same little-endian packing as in memory);
-//  - 4-bit: lane l holds row l%32, k in [32(l/32), +32): 16 bytes, low nibble first.
-//
-// Design (a general path, simpler than the tuned pipeline): workgroup tile 256 x 256, K
-// tiles of 128 elements (128, 96 or 64 bytes of a row), four waves with 128 x 128
-// sub-tiles. Whole K tiles stream HBM -> LDS with direct copies (global_load_lds, 1 KiB of
-// LDS per copy) into three stages (two when an 8-bit operand meets a 6-bit one: three do
-// not fit), the copy of tile kt + NST issued as soon as every wave is done reading tile kt,
-// so the copies have NST - 1 K tiles of multiplies to land in (one K tile of 6- or 4-bit
-// operands is only 1024 MFMA cycles). Each row's 16-byte chunks are permuted (by the
-// copies' global addresses) so that the 16 rows one 16-lane group reads at one offset fall
-// in distinct banks: chunk c of row r sits at c ^ ((r >> 1) & 7) for 128-byte rows,
-// (c + ((r >> 3) & 1)) % 6 for 96-byte rows and c ^ ((r >> 2) & 3) for 64-byte rows. Each
-// stage also holds the tile's scale words (one 32-bit word per row: the four 32-K blocks),
-// copied 4 bytes per lane. Step 1's fragment reads are spread between step 0's MFMAs. A
-// partial last K tile goes through registers with zero elements and unit scales past K.
-#include "gemm_common.hpp"
-#include "../../include/bsm.h"
+// k_gemm_mx_any.hip - launches of the general block-scaled kernel (gemm_mx_any.hpp) for
+// K-major operands: every pairing of E4M3, E5M2, E2M3, E3M2, E2M1 except the ones the
+// tuned kernel of k_gemm_mx.hip runs.
+#include "gemm_mx_any.hpp"
 
 namespace bsm {
-namespace {
 
-constexpr int BM = 256, BN = 256, KT = 128;
-
-__host__ __device__ constexpr int fmt_bits(int c) { return c <= 1 ? 8 : (c <= 3 ? 6 : 4); }
-
-template <int C>
-struct Op {
-  static constexpr int BITS = fmt_bits(C);
-  static constexpr int ROW = 16 * BITS;   // bytes of a row per K tile: 128, 96, 64
-  static constexpr int TILE = 256 * ROW;
-  static constexpr int CPR = ROW / 16;    // 16-byte chunks per row per K tile (and per lane)
-  // physical chunk of logical chunk c in row r, and back
-  __device__ static int phys(int c, int r) {
-    return CPR == 8 ? c ^ ((r >> 1) & 7) : (CPR == 6 ? (c + ((r >> 3) & 1)) % 6 : c ^ ((r >> 2) & 3));
-  }
-  __device__ static int logical(int pc, int r) {
-    return CPR == 8 ? pc ^ ((r >> 1) & 7) : (CPR == 6 ? (pc + 6 - ((r >> 3) & 1)) % 6 : pc ^ ((r >> 2) & 3));
-  }
-};
-
-// A stage: A tile, B tile, then the K tile's scale words of A's and B's 256 rows (4 bytes
-// each: the four 32-K blocks of the tile). NST stages of the 160 KiB of LDS.
-template <int CA, int CB>
-struct Lay {
-  static constexpr int SCALES = Op<CA>::TILE + Op<CB>::TILE;
-  static constexpr int STAGE = SCALES + 2048;
-  static constexpr int NST = 3 * STAGE <= 163840 ? 3 : 2;
-  static constexpr int BYTES = NST * STAGE > 131072 ? NST * STAGE : 131072;  // the epilogue uses 128 KiB
-};
-
-__device__ __forceinline__ uint2 lds_read_b64(const void* p) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = *(const BSM_LDS u32x2*)(p);
-  return make_uint2(v[0], v[1]);
-}
-
-// Byte offsets (from the tile's first row) of the rows of this lane's CPR chunks, rows past
-// the operand clamped to its last row (the host keeps 256 rows of a leading dimension below
-// 2^31 bytes).
-template <int C>
-__device__ __forceinline__ void row_offsets(int64_t ld_bytes, int64_t rows, int q, uint32_t (&ro)[Op<C>::CPR]) {
-  typedef Op<C> P;
-#pragma unroll
-  for (int i = 0; i < P::CPR; i++) {
-    const int c = q + 256 * i, r = c / P::CPR;
-    ro[i] = (uint32_t)(min((int64_t)r, rows - 1) * ld_bytes);
-  }
-}
-
-// This lane's CPR chunks of the partial last K tile kt of one operand (bytes [16 cc, +16)
-// of the tile's row piece of row ro[i]): bytes at or past `kbytes` (the row's K extent)
-// read as zero (rows are whole 16-byte chunks, so a chunk that starts inside the K extent
-// lies inside the row).
-template <int C>
-__device__ __forceinline__ void load_chunks_tail(const uint8_t* base, const uint32_t (&ro)[Op<C>::CPR], int kt,
-                                                 int64_t kbytes, int q, uint4 (&v)[Op<C>::CPR]) {
-  typedef Op<C> P;
-#pragma unroll
-  for (int i = 0; i < P::CPR; i++) {
-    const int c = q + 256 * i, r = c / P::CPR, cc = c - r * P::CPR;
-    const int64_t off = (int64_t)kt * P::ROW + 16 * cc;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (off < kbytes) {
-      x = *(const uint4*)(base + ro[i] + off);
-      const int64_t valid = kbytes - off;
-      if (valid < 16) {
-        uint32_t wd[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-          const int64_t nb = valid - 4 * d;
-          wd[d] &= nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (1u << (8 * nb)) - 1u);
-        }
-        x = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      }
-    }
-    v[i] = x;
-  }
-}
-
-template <int C>
-__device__ __forceinline__ void store_chunks(uint8_t* tile, int q, const uint4 (&v)[Op<C>::CPR]) {
-  typedef Op<C> P;
-#pragma unroll
-  for (int i = 0; i < P::CPR; i++) {
-    const int c = q + 256 * i, r = c / P::CPR, cc = c - r * P::CPR;
-    lds_write_b128(tile + r * P::ROW + 16 * P::phys(cc, r), v[i]);
-  }
-}
-
-// Thread q's scale word of K tile kt: row q of the tile (clamped to the operand), the four
-// 32-K blocks of the tile. In a partial last tile the bytes of blocks at or past nblk
-// (K / 32) become 127 (unit scale on zero elements).
-__device__ __forceinline__ uint32_t load_scale_word(const uint8_t* sf, int64_t ld_sf, int64_t row0, int64_t rows,
-                                                    int q, int kt) {
-  const int64_t grow = min(row0 + q, rows - 1);
-  return *(const uint32_t*)(sf + grow * ld_sf + 4 * (int64_t)kt);
-}
-
-__device__ __forceinline__ uint32_t mask_scale_word(uint32_t x, int kt, int64_t nblk) {
-  const int64_t b0 = 4 * (int64_t)kt;
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-    if (b0 + j >= nblk) x = (x & ~(0xFFu << (8 * j))) | (127u << (8 * j));
-  return x;
-}
-
-// This lane's scale words for its four rows (base + 32t + l%32) from a stage's scale area.
-__device__ __forceinline__ void read_scales(const uint8_t* area, int base, int lane, uint32_t (&s)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; t++) s[t] = *(const BSM_LDS uint32_t*)(area + 4 * (base + 32 * t + (lane & 31)));
-}
-
-// Operand registers of 64-K step s for the lane's row of 32-row block t.
-template <int C>
-__device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t, int s, int lane) {
-  typedef Op<C> P;
-  const int h = lane >> 5, r = base + 32 * t + (lane & 31);
-  const uint8_t* row = tile + r * P::ROW;
-  // logical byte offset o of the row -> its place in the permuted row
-  auto at = [&](int o) { return row + 16 * P::phys(o >> 4, r) + (o & 15); };
-  i32x8 v;
-  if (P::BITS == 8) {
-    const uint4 x = lds_read_b128(at(64 * s + 16 * h)), y = lds_read_b128(at(64 * s + 32 + 16 * h));
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-  } else if (P::BITS == 6) {
-    const int o = 48 * s + 24 * h;
-    const uint2 x = lds_read_b64(at(o)), y = lds_read_b64(at(o + 8)), z = lds_read_b64(at(o + 16));
-    v[0] = x.x; v[1] = x.y; v[2] = y.x; v[3] = y.y; v[4] = z.x; v[5] = z.y;
-    v[6] = v[7] = 0;
-  } else {
-    const uint4 x = lds_read_b128(at(32 * s + 16 * h));
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    v[4] = v[5] = v[6] = v[7] = 0;
-  }
-  return v;
-}
-
-// Operand registers of 64-K step S for the wave: A blocks t = 0..3 (rows wa + 32t + l%32),
-// B blocks (rows wb + ...).
-template <int CA, int CB, int S>
-__device__ __forceinline__ void read_frags(const uint8_t* ta, const uint8_t* tb, int wa, int wb, int lane,
-                                           i32x8 (&fa)[4], i32x8 (&fb)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; t++) {
-    fa[t] = read_frag<CA>(ta, wa, t, S, lane);
-    fb[t] = read_frag<CB>(tb, wb, t, S, lane);
-  }
-}
-
-// The 16 MFMAs of 64-K step S (accumulator rows mt-major). The MFMA takes B first (its
-// format code and scales as src0); after the per-lane shift by 8 (l/32), op_sel byte 2S
-// holds the scale of the lane's 32-K block of this step. side(i) runs after MFMA i: the
-// empty asm statements around each MFMA (accumulators kept in AGPRs, memory clobbered)
-// keep the side work - LDS reads and writes - between the MFMAs, where it overlaps the
-// matrix pipe instead of waiting for it.
-template <int CA, int CB, int S, typename Side>
-__device__ __forceinline__ void mfma16(const i32x8 (&fa)[4], const i32x8 (&fb)[4], const uint32_t (&sa)[4],
-                                       const uint32_t (&sb)[4], int sh, f32x16 (&acc)[4][4], Side side) {
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int mt = i >> 2, nt = i & 3;
-    asm volatile("" : "+a"(acc[mt][nt])::"memory");
-    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[nt], fa[mt], acc[mt][nt], CB, CA, 2 * S,
-                                                                   (int)(sb[nt] >> sh), 2 * S, (int)(sa[mt] >> sh));
-    asm volatile("" : "+a"(acc[mt][nt])::"memory");
-    side(i);
-  }
-}
-
-template <int CA, int CB>
-__global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m, int tiles_n) {
-  typedef Op<CA> PA;
-  typedef Op<CB> PB;
-  typedef Lay<CA, CB> L;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
-  const int q = threadIdx.x, lane = q & 63, w = __builtin_amdgcn_readfirstlane(q >> 6);
-  int tm, tn;
-  gemm::tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int wa = 128 * (w >> 1), wb = 128 * (w & 1);
-  const float sgn = a.negate ? -1.0f : 1.0f;
-  const int64_t nblk = a.K / 32;
-  const int64_t lda_b = a.lda * PA::BITS / 8, ldb_b = a.ldb * PB::BITS / 8;
-  const int64_t ka = a.K * PA::BITS / 8, kb = a.K * PB::BITS / 8;   // a row's K extent in bytes
-  const uint8_t* A = (const uint8_t*)a.A + m0 * lda_b;
-  const uint8_t* B = (const uint8_t*)a.B + n0 * ldb_b;
-  const int64_t rows_a = a.M - m0, rows_b = a.N - n0;
-  const int sh = 8 * (lane >> 5);
-
-  f32x16 acc[4][4];
-  gemm::zero_acc(acc);
-  // Direct copies of one stage: NA (NB) 1 KiB copies for the A (B) tile, copy j going to
-  // wave j % 4, then one 256-byte scale copy per operand per wave.
-  constexpr int NA = PA::ROW / 4, NB = PB::ROW / 4;   // = 256 * ROW / 1024
-  constexpr int DA = NA / 4, DB = NB / 4, DPW = DA + DB + 2, NST = L::NST;
-  uint32_t oa[DA], ob[DB], osa, osb;
-  {
-    // lane l of copy j lands at LDS chunk 64 (w + 4j) + l of the tile: row p / CPR, physical
-    // chunk p % CPR, which holds the row's logical chunk `logical(...)`
-    auto offs = [&](auto P, int64_t ld_bytes, int64_t rows, int j) -> uint32_t {
-      typedef decltype(P) PP;
-      const int p = 64 * (w + 4 * j) + lane;
-      const int r = p / PP::CPR, pc = p - r * PP::CPR;
-      return (uint32_t)(min((int64_t)r, rows - 1) * ld_bytes + 16 * PP::logical(pc, r));
-    };
-#pragma unroll
-    for (int j = 0; j < DA; j++) oa[j] = offs(PA{}, lda_b, rows_a, j);
-#pragma unroll
-    for (int j = 0; j < DB; j++) ob[j] = offs(PB{}, ldb_b, rows_b, j);
-    osa = (uint32_t)(min((int64_t)(64 * w + lane), rows_a - 1) * a.ld_sfa);
-    osb = (uint32_t)(min((int64_t)(64 * w + lane), rows_b - 1) * a.ld_sfb);
-  }
-  const uint8_t* SA = a.SFA + m0 * a.ld_sfa;
-  const uint8_t* SB = a.SFB + n0 * a.ld_sfb;
-  const uint32_t lds0 = gemm::lds_addr(lds);
-  // Copy d (of DPW) of tile kt into stage `stage`.
-  auto copy = [&](int kt, int stage, int d) {
-    const uint32_t st = lds0 + stage * L::STAGE;
-    if (d < DA) gemm::dma16s(A + kt * PA::ROW, oa[d], st + 1024 * (w + 4 * d));
-    else if (d < DA + DB) gemm::dma16s(B + kt * PB::ROW, ob[d - DA], st + PA::TILE + 1024 * (w + 4 * (d - DA)));
-    else if (d == DA + DB) gemm::dma4s(SA + 4 * kt, osa, st + L::SCALES + 256 * w);
-    else gemm::dma4s(SB + 4 * kt, osb, st + L::SCALES + 1024 + 256 * w);
-  };
-  auto issue = [&](int kt, int stage) {
-#pragma unroll
-    for (int d = 0; d < DPW; d++) copy(kt, stage, d);
-  };
-  static_assert(DPW <= 16, "one copy per MFMA slot of step 1");
-  // Multiply the tile in stage st: step 1's fragment reads go out between step 0's MFMAs;
-  // then every wave is done with the stage (barrier) and side1(i) runs after step 1's
-  // MFMA i (the copies of the tile that replaces this one, spread one per MFMA slot:
-  // issued in one burst they would hold the waves behind the shared copy path).
-  auto multiply = [&](const uint8_t* st, auto side1) {
-    uint32_t sa[4], sb[4];
-    i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    read_scales(st + L::SCALES, wa, lane, sa);
-    read_scales(st + L::SCALES + 1024, wb, lane, sb);
-    read_frags<CA, CB, 0>(st, st + PA::TILE, wa, wb, lane, fa0, fb0);
-    mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, [&](int i) {
-      if (i < 8) {
-        if (i & 1) fb1[i >> 1] = read_frag<CB>(st + PA::TILE, wb, i >> 1, 1, lane);
-        else fa1[i >> 1] = read_frag<CA>(st, wa, i >> 1, 1, lane);
-      }
-    });
-    gemm::lds_barrier();
-    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, side1);
-  };
-
-  // Whole K tiles; tile kt lives in stage kt % NST. Past the last one the copies re-read
-  // the last tile into the stage just released (nobody reads it again), so every
-  // iteration issues the same copies and the wait counts stay fixed.
-  const int nfull = (int)(a.K / KT);
-  if (nfull > 0) {
-#pragma unroll
-    for (int i = 0; i < NST; i++) issue(min(i, nfull - 1), i);
-    gemm::stage_barrier<(NST - 1) * DPW>();  // tile 0 has landed
-  }
-  int cur = 0;                               // kt % NST
-  for (int kt = 0; kt < nfull; kt++) {
-    const int knext = min(kt + NST, nfull - 1);
-    multiply(lds + cur * L::STAGE, [&](int i) {
-      if (i < DPW) copy(knext, cur, i);
-    });
-    gemm::stage_barrier<(NST - 1) * DPW>();  // tile kt + 1 has landed
-    cur = cur + 1 == NST ? 0 : cur + 1;
-  }
-  gemm::wait_dma();                          // the repeated copies too, before LDS is reused
-  __syncthreads();
-  // A partial last K tile (K not a multiple of 128), loaded with zeros past K.
-  if (a.K % KT) {
-    uint4 va[PA::CPR], vb[PB::CPR];
-    uint32_t roa[PA::CPR], rob[PB::CPR];
-    row_offsets<CA>(lda_b, rows_a, q, roa);
-    row_offsets<CB>(ldb_b, rows_b, q, rob);
-    uint8_t* st = lds;                       // every copy has landed: any stage will do
-    load_chunks_tail<CA>(A, roa, nfull, ka, q, va);
-    load_chunks_tail<CB>(B, rob, nfull, kb, q, vb);
-    const uint32_t wsa = mask_scale_word(load_scale_word(a.SFA, a.ld_sfa, m0, a.M, q, nfull), nfull, nblk);
-    const uint32_t wsb = mask_scale_word(load_scale_word(a.SFB, a.ld_sfb, n0, a.N, q, nfull), nfull, nblk);
-    store_chunks<CA>(st, q, va);
-    store_chunks<CB>(st + PA::TILE, q, vb);
-    *(BSM_LDS uint32_t*)(st + L::SCALES + 4 * q) = wsa;
-    *(BSM_LDS uint32_t*)(st + L::SCALES + 1024 + 4 * q) = wsb;
-    __syncthreads();
-    multiply(st, [](int) {});
-    __syncthreads();
-  }
-  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, a.accum != 0,
-                         a.ew_op, a.ew_scale, a.ew_bias);
-}
-
-// Pairs of equal width (8-bit x 8-bit, E2M1 x E2M1) belong to the tuned kernel.
-template <int CA, int CB>
-hipError_t launch_pair(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t st) {
-  if constexpr ((fmt_bits(CA) == 8 && fmt_bits(CB) == 8) || (CA == 4 && CB == 4)) {
-    return hipErrorInvalidValue;
-  } else {
-    hipLaunchKernelGGL((k_gemm_mx_any<CA, CB>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m, tiles_n);
-    return hipGetLastError();
-  }
-}
-
-template <int CA>
-hipError_t launch_b(int cb, const GemmArgs& a, int tm, int tn, hipStream_t st) {
-  switch (cb) {
-    case 0: return launch_pair<CA, 0>(a, tm, tn, st);
-    case 1: return launch_pair<CA, 1>(a, tm, tn, st);
-    case 2: return launch_pair<CA, 2>(a, tm, tn, st);
-    case 3: return launch_pair<CA, 3>(a, tm, tn, st);
-    default: return launch_pair<CA, 4>(a, tm, tn, st);
-  }
-}
-
-// bsm_dtype -> MFMA format code
-int mfma_code(int32_t dt) {
-  switch (dt) {
-    case BSM_E4M3: return 0;
-    case BSM_E5M2: return 1;
-    case BSM_E2M3: return 2;
-    case BSM_E3M2: return 3;
-    default: return 4;  // BSM_E2M1
-  }
-}
-
-}  // namespace
-
-hipError_t launch_gemm_mx_any(const GemmArgs& a, hipStream_t st) {
-  const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
-  if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int tm = (int)tm64, tn = (int)tn64;
-  const int ca = mfma_code(a.dtype), cb = mfma_code(a.dtype_b);
-  switch (ca) {
-    case 0: return launch_b<0>(cb, a, tm, tn, st);
-    case 1: return launch_b<1>(cb, a, tm, tn, st);
-    case 2: return launch_b<2>(cb, a, tm, tn, st);
-    case 3: return launch_b<3>(cb, a, tm, tn, st);
-    default: return launch_b<4>(cb, a, tm, tn, st);
-  }
-}
+hipError_t launch_gemm_mx_any(const GemmArgs& a, hipStream_t st) { return mxany::launch_formats<false, false>(a, st); }
 
 }  // namespace bsm

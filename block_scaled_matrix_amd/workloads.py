@@ -140,6 +140,41 @@ def mx_pair(seed: int, M: int, N: int, K: int, a_fmt: str, b_fmt: str, exp_range
             "ld_sfa": K // 32, "ld_sfb": K // 32, "fmt": a_fmt, "b_fmt": b_fmt, "accum": 0, "neg_a": 0, "neg_b": 0}
 
 
+def unpack_codes(raw: np.ndarray, fmt: str, rows: int, K: int) -> np.ndarray:
+    """Packed element codes (rows, K) (8-bit bytes; E2M1 two per byte, low nibble first; 6-bit
+    fields of a little-endian bit string per row) -> one uint8 code per element."""
+    bits = BITS[fmt]
+    r = np.ascontiguousarray(raw).reshape(rows, -1)
+    if bits == 8:
+        return r[:, :K].copy()
+    if bits == 4:
+        return np.stack([r & 15, r >> 4], axis=2).reshape(rows, -1)[:, :K].copy()
+    bs = np.unpackbits(r, axis=1, bitorder="little")[:, :6 * K].reshape(rows, K, 6)
+    return (bs * (1 << np.arange(6, dtype=np.uint8))).sum(axis=2, dtype=np.uint8)
+
+
+def pack_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """One code per element (rows, n) -> packed rows (the inverse of unpack_codes)."""
+    bits = BITS[fmt]
+    if bits == 8:
+        return np.ascontiguousarray(codes, dtype=np.uint8)
+    if bits == 4:
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return pack_fp6(np.ascontiguousarray(codes))
+
+
+def mn_major(raw: np.ndarray, fmt: str, rows: int, K: int, ld: int, seed: int | None = None) -> np.ndarray:
+    """K-major packed codes (rows, K) -> MN-major storage: K rows of ld elements, element
+    (k, m) = code (m, k); the ld - rows padding elements of each row are random codes
+    (seed given) or zero."""
+    codes = unpack_codes(raw, fmt, rows, K).T
+    out = np.zeros((K, ld), np.uint8)
+    if seed is not None:
+        out[:] = np.random.default_rng(seed).integers(0, 1 << BITS[fmt], (K, ld), dtype=np.uint8)
+    out[:, :rows] = codes
+    return pack_codes(out, fmt)
+
+
 def gather4_bf16(seed: int = 6, rows: int = 65536, cols: int = 4096, width: int = 64):
     """Table (rows, cols) uint16 bf16 bits; gather and scatter coordinates (n, 5) int32, issue
     t = group * (cols / width) + block: column start block * width, then four rows."""

@@ -269,6 +269,32 @@ int bsm_gemm_block_scale_ewise(int64_t M, int64_t N, int64_t K,
                                float* D, int64_t ldd, int neg_a, int neg_b, int accum,
                                const bsm_ewise* ew, void* stream);
 
+/* Block-scaled GEMM with the major order of each operand chosen ([MMA] "Shared
+ * descriptors are byte-stride contracts": a_major / b_major are "k" or "mn", MN-major rows
+ * enumerate K; "Weight-stationary and block scaling"; [TP] "tcgen05 MMA"):
+ *   a_major 'k': A(m,k) = dec(A[m*lda + k]),  lda >= K;
+ *           'm': A(m,k) = dec(A[k*lda + m]),  lda >= M   (K rows of M contiguous elements);
+ *   b_major 'k': B(n,k) = dec(B[n*ldb + k]),  ldb >= K;
+ *           'n': B(n,k) = dec(B[k*ldb + n]),  ldb >= N;
+ * element index i of a row read as for bsm_gemm_block_scale (E2M1 low nibble first). The
+ * scales keep their layout whatever the major order: SFA[m*ld_sfa + k/32],
+ * SFB[n*ld_sfb + k/32]. An MN-major operand is BSM_E4M3, BSM_E5M2 or BSM_E2M1 (6-bit
+ * MN-major operands -> BSM_E_MAJOR); the other operand may be any format and either
+ * order. ew as for bsm_gemm_block_scale_ewise, or NULL for no epilogue. A major order
+ * other than 'k' / 'm' ('k' / 'n' for B) -> BSM_E_MAJOR. Every other argument, rule and
+ * the precision are those of bsm_gemm_block_scale: rows (K-major: M or N of them, MN-major:
+ * K) 16-byte aligned (ld * bits a multiple of 128), every buffer spans whole rows
+ * (rows * ld elements), ld * bits / 8 at most 2^23 bytes. With both orders 'k' the call
+ * is bsm_gemm_block_scale_ewise (bit-identical results). MN-major operands run the
+ * general kernel, which reads them through the gfx950 transposing LDS reads. */
+int bsm_gemm_block_scale_major(int64_t M, int64_t N, int64_t K,
+                               int32_t a_fmt, const void* A, int64_t lda, char a_major,
+                               const uint8_t* SFA, int64_t ld_sfa,
+                               int32_t b_fmt, const void* B, int64_t ldb, char b_major,
+                               const uint8_t* SFB, int64_t ld_sfb,
+                               float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                               const bsm_ewise* ew, void* stream);
+
 /* Element-wise scalar add on float32 ([TOE] "A Load, Compute, and Store Example"
  * adds one to a (2,32,3,4) tile; [TP] "Scalar compositions"): dst[i] = src[i] + s,
  * i < n, each lane moving 16-byte vectors. src, dst 16-byte aligned; they may be

@@ -177,6 +177,21 @@ def test_gemm_contract_violations(L):
            bsm.ewise_desc(7))
     expect("BSM_E_SHAPE", se, 64, 64, 48, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
     expect("BSM_E_DTYPE", se, 64, 64, 64, "e4m3", A, 64, SA, 4, "bf16", B, 64, SB, 4, D, 64)
+    sm = lambda *a, ew=None: bsm.bsm_gemm_block_scale_major(*a, ew=ew, stream=0)
+    expect("BSM_E_MAJOR", sm, 64, 64, 64, "e4m3", A, 64, "n", SA, 4, "e4m3", B, 64, "k", SB, 4, D, 64)
+    expect("BSM_E_MAJOR", sm, 64, 64, 64, "e4m3", A, 64, "k", SA, 4, "e4m3", B, 64, "m", SB, 4, D, 64)
+    expect("BSM_E_MAJOR", sm, 64, 64, 64, "e2m3", A, 64, "m", SA, 4, "e4m3", B, 64, "k", SB, 4, D, 64)  # fp6 MN
+    expect("BSM_E_MAJOR", sm, 64, 64, 64, "e4m3", A, 64, "k", SA, 4, "e3m2", B, 64, "n", SB, 4, D, 64)
+    expect("BSM_E_ALIGN", sm, 96, 64, 64, "e4m3", A, 64, "m", SA, 4, "e4m3", B, 64, "k", SB, 4, D, 64)  # lda < M
+    expect("BSM_E_ALIGN", sm, 64, 96, 64, "e4m3", A, 64, "k", SA, 4, "e2m1", B, 64, "n", SB, 4, D, 64)  # ldb < N
+    expect("BSM_E_ALIGN", sm, 64, 64, 64, "e2m1", A, 72, "m", SA, 4, "e4m3", B, 64, "k", SB, 4, D, 64)  # 36-byte rows
+    expect("BSM_E_SHAPE", sm, 64, 64, 48, "e4m3", A, 64, "m", SA, 4, "e4m3", B, 64, "n", SB, 4, D, 64)
+    expect("BSM_E_SHAPE", sm, 64, 64, 64, "e4m3", A, 1 << 24, "m", SA, 4, "e4m3", B, 64, "n", SB, 4, D, 64)
+    expect("BSM_E_ARG", lambda: sm(64, 64, 64, "e4m3", A, 64, "m", SA, 4, "e4m3", B, 64, "n", SB, 4, D, 64,
+                                   ew=bsm.ewise_desc(5)))
+    # an MN-major A spans K = 128 rows of lda = 64 bytes (8 KiB, where M rows of it would span 4 KiB)
+    expect("BSM_E_ALIAS", sm, 64, 64, 128, "e4m3", A, 64, "m", SA, 4, "e4m3", B, 128, "k", SB, 4, A + 4096, 64)
+    bsm.bsm_gemm_block_scale_major(64, 0, 64, "e4m3", 0, 0, "m", 0, 0, "e4m3", 0, 0, "n", 0, 0, 0, 0, stream=0)
     a = lambda *x: bsm.bsm_tile_add_scalar_f32(*x, stream=0)
     expect("BSM_E_SHAPE", a, A, B, -1, 1.0)
     expect("BSM_E_ALIGN", a, A + 4, B, 8, 1.0)

@@ -379,7 +379,7 @@ def main():
         ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
         rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         per[name] = {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
-                     "frac": round(rate / peak, 4), "work_per_launch": work}
+                     "frac": round(rate / peak, 4), "work_per_launch": work, "traffic": measured_traffic(name)}
         mf = measured_mfma(name)
         if mf is not None:   # counter figures of the same kernel sources (profiles/mfma_busy_bench_step.md)
             per[name]["mfma_busy"], per[name]["clock_ghz"] = mf

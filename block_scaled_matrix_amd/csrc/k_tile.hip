@@ -368,17 +368,22 @@ struct Copy2D {
   int64_t s_src, s_dst, s_add;          // row strides (bytes)
   uint32_t tiles1;                      // boxes per row of boxes
   uint32_t groups1;                     // workgroups per row of boxes: ceil(tiles1 / 2^lg_nb)
-  uint32_t slices;                      // row slices per box: ceil(box0 / (4 * rows per pass))
+  uint32_t slices;                      // row slices per box: ceil(box0 / (kCopyPasses * rows per pass))
   int32_t box0, box1;                   // box extents (rows, elements)
   int32_t esize, dtype, swizzle, lg_cpr, lg_nb, row_bytes;
   uint32_t fill_word;                   // the fill element replicated over 32 bits
 };
 
+// Rows of a slice each lane moves (one 16-byte chunk per row): two keep 8 KiB of every
+// tensor per workgroup, which measured faster on HBM than four (the grid doubles, and
+// each workgroup's accesses are all in flight at once).
+constexpr int kCopyPasses = 2;
+
 // A workgroup moves one row slice of 2^lg_nb horizontally adjacent boxes (the bf16 (128,
-// 64) box: 16 rows x 8 boxes, i.e. rows of 1 KiB contiguous bytes, which HBM serves
+// 64) box: 8 rows x 8 boxes, i.e. rows of 1 KiB contiguous bytes, which HBM serves
 // markedly faster than the 128-byte rows of a single box at a power-of-two row pitch).
 // Lane l takes chunk column l % (nb cpr) (box (l % (nb cpr)) / cpr) of slice rows
-// l / (nb cpr) + k * rstep, k < 4. Each box keeps its own image region in LDS: the slice's
+// l / (nb cpr) + k * rstep, k < kCopyPasses. Each box keeps its own image region in LDS: the slice's
 // rows sit there at the swizzled offsets they have in the full box image (a slice spans a
 // whole number of swizzle periods, so the pattern is the same). All source and
 // reduce-add chunks are fetched first with 128-bit streaming loads, so every HBM read of the
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
   const int call = threadIdx.x & ((1 << lg_row) - 1);
   const int bx = call >> a.lg_cpr, cc = call & (cpr - 1);
   const int rr0 = threadIdx.x >> lg_row, rstep = 256 >> lg_row;
-  const int rs = 4 * rstep;                               // rows per slice
+  const int rs = kCopyPasses * rstep;                     // rows per slice
   const uint32_t t1 = (g1 << a.lg_nb) + bx;
   const bool boxok = t1 < a.tiles1;
   const int64_t c0 = (int64_t)t0 * a.box0, c1 = (int64_t)t1 * a.box1;
@@ -414,10 +419,10 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
   const int64_t kc = whole || part ? k0 : ((a.dims1 / epc) - 1) * epc;  // a whole chunk stands in
   const uint4 fill4 = make_uint4(a.fill_word, a.fill_word, a.fill_word, a.fill_word);
   uint8_t* region = image + bx * rs * a.row_bytes;      // this box's slice of its image
-  uint4 v[4], d[4];
-  bool rin[4], last[4];
+  uint4 v[kCopyPasses], d[kCopyPasses];
+  bool rin[kCopyPasses], last[kCopyPasses];
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
+  for (int k = 0; k < kCopyPasses; k++) {
     const int r = (int)sl * rs + rr0 + k * rstep;        // row within the box
     const int64_t row = c0 + r;
     rin[k] = boxok && r < a.box0 && row < a.dims0;
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
     if (ADD) d[k] = stream_load16(a.add + rowc * a.s_add + col);
   }
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
+  for (int k = 0; k < kCopyPasses; k++) {
     v[k] = select4(rin[k] && (whole || part), v[k], fill4);
     if (part) {
       for (int e = 0; e < epc; e++)
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
   if (__builtin_expect(part && a.dims0 - 1 < c0 + a.box0, 0)) {
     // the straddling chunk of the tensor's last row, element by element
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
+    for (int k = 0; k < kCopyPasses; k++) {
       if (!rin[k] || !last[k]) continue;
       const uint8_t* row = a.src + (c0 + (int)sl * rs + rr0 + k * rstep) * a.s_src;
       for (int e = 0; e < epc; e++)
@@ -446,14 +451,14 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
     }
   }
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
+  for (int k = 0; k < kCopyPasses; k++) {
     const int rr = rr0 + k * rstep;
     if ((int)sl * rs + rr < a.box0)
       lds_write_b128(region + image_swizzle((uint32_t)(rr * a.row_bytes + cc * 16), a.swizzle), v[k]);
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
+  for (int k = 0; k < kCopyPasses; k++) {
     const int rr = rr0 + k * rstep;
     const int64_t row = c0 + (int)sl * rs + rr;
     if (!rin[k] || !(whole || part)) continue;
@@ -518,15 +523,15 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
     // (at least 2 rows per pass) and the row of boxes has that many boxes
     a.lg_nb = 0;
     while (a.lg_nb < 3 && (2 * cpr << a.lg_nb) <= 128 && (int64_t(2) << a.lg_nb) <= (int64_t)o.tiles[1]) a.lg_nb++;
-    const int rs = 4 * (256 >> (a.lg_cpr + a.lg_nb));      // rows per slice
+    const int rs = kCopyPasses * (256 >> (a.lg_cpr + a.lg_nb));  // rows per slice
     a.groups1 = (uint32_t)((o.tiles[1] + (1u << a.lg_nb) - 1) >> a.lg_nb);
     a.slices = (uint32_t)((g.box[0] + rs - 1) / rs);
     a.fill_word = g.esize == 1 ? g.fill_bits * 0x01010101u : (g.esize == 2 ? g.fill_bits * 0x00010001u : g.fill_bits);
     const int64_t wgs = (int64_t)o.tiles[0] * a.slices * a.groups1;
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-    // every box's slice region is rs * row_bytes = 16 KiB / 2^lg_nb >= 2 KiB, a whole number
+    // every box's slice region is rs * row_bytes = 8 KiB / 2^lg_nb >= 1 KiB, a whole number
     // of swizzle periods (the swizzle stays inside aligned 2^(7 + mode)-byte windows)
-    const size_t lds_bytes = (size_t)4 * 256 * 16;
+    const size_t lds_bytes = (size_t)kCopyPasses * 256 * 16;
     if (!dst_add)
       hipLaunchKernelGGL(k_box_copy2d<0>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
     else if (g.dtype == BSM_F32)

@@ -15,7 +15,7 @@
 //    6i .. 6i+5 (the same little-endian packing as in memory);
 //  - 4-bit: lane l holds row l%32, k in [32(l/32), +32): 16 bytes, low nibble first.
 //
-// Design (a general path, simpler than the tuned pipeline): workgroup tile 256 x 256, K
+// Design: workgroup tile 256 x 256, K
 // tiles of 128 elements (128, 96 or 64 bytes of a row), four waves with 128 x 128
 // sub-tiles. Whole K tiles stream HBM -> LDS with direct copies (global_load_lds, 1 KiB of
 // LDS per copy) into three stages (two when an 8-bit operand meets a 6-bit one: three do
@@ -24,10 +24,15 @@
 // operands is only 1024 MFMA cycles). Each row's 16-byte chunks are permuted (by the
 // copies' global addresses) so that the 16 rows one 16-lane group reads at one offset fall
 // in distinct banks: chunk c of row r sits at c ^ ((r >> 1) & 7) for 128-byte rows,
-// (c + ((r >> 3) & 1)) % 6 for 96-byte rows and c ^ ((r >> 2) & 3) for 64-byte rows. Each
-// stage also holds the tile's scale words (one 32-bit word per row: the four 32-K blocks),
-// copied 4 bytes per lane. Step 1's fragment reads are spread between step 0's MFMAs. A
-// partial last K tile goes through registers with zero elements and unit scales past K.
+// (c + ((r >> 3) & 1)) % 6 for 96-byte rows and c ^ ((r >> 2) & 3) for 64-byte rows. The
+// scale words (one 32-bit word per row and K tile: its four 32-K blocks) come through a
+// ring of two buffers, each holding a group of four K tiles (16 bytes per row), a quarter
+// of a group copied with every K tile's data as 16-row copies of 4 bytes per lane: a copy
+// whose 64 lanes touch 64 rows, one word per row and K tile, held the shared copy path
+// four times as long. One barrier per K tile, at the start of its step 1; step 1's
+// fragment reads go out between step 0's MFMAs, the next tile's scales and step-0
+// fragments between step 1's, so no K tile starts by waiting for the LDS. A partial last
+// K tile goes through registers with zero elements and unit scales past K.
 //
 // MN-major operands (K rows with M or N contiguous; 8-bit and E2M1 elements): the tile is
 // 128 k-rows of the workgroup's 256 M/N elements, copied as they are, and the fragments
@@ -84,15 +89,30 @@ struct Op {
   }
 };
 
-// A stage: A tile, B tile, then the K tile's scale words of A's and B's 256 rows (4 bytes
-// each: the four 32-K blocks of the tile). NST stages of the 160 KiB of LDS.
+// A stage: A tile, B tile. NST stages, then the scale ring: two buffers of one group of
+// four K tiles each, A's 256 rows then B's, 16 bytes per row (the row's scale words of the
+// group's tiles), all within the 160 KiB of LDS.
 template <int CA, int CB>
 struct Lay {
-  static constexpr int SCALES = Op<CA, false>::TILE + Op<CB, false>::TILE;
-  static constexpr int STAGE = SCALES + 2048;
-  static constexpr int NST = 3 * STAGE <= 163840 ? 3 : 2;
-  static constexpr int BYTES = NST * STAGE > 131072 ? NST * STAGE : 131072;  // the epilogue uses 128 KiB
+  static constexpr int STAGE = Op<CA, false>::TILE + Op<CB, false>::TILE;
+  static constexpr int RING_BUF = 2 * 256 * 16;
+  static constexpr int NST = 3 * STAGE + 2 * RING_BUF <= 163840 ? 3 : 2;
+  static constexpr int RING = NST * STAGE;
+  static constexpr int END = RING + 2 * RING_BUF;
+  static constexpr int BYTES = END > 131072 ? END : 131072;  // the epilogue uses 128 KiB
 };
+
+// Scale ring: word q (K tile 4g + q) of row R of a group buffer sits at physical word
+// q ^ ((R >> 4) & 3), so the 32 consecutive rows one read instruction touches fall in 32
+// distinct banks.
+__device__ __forceinline__ uint32_t ring_word_offset(int R, int q) { return (uint32_t)(16 * R + 4 * (q ^ ((R >> 4) & 3))); }
+
+// This lane's scale words of K tile kt for its four rows (base + 32t + l%32) from the ring
+// buffer of kt's group (A's or B's half).
+__device__ __forceinline__ void read_scales_ring(const uint8_t* half, int kt, int base, int lane, uint32_t (&s)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) s[t] = *(const BSM_LDS uint32_t*)(half + ring_word_offset(base + 32 * t + (lane & 31), kt & 3));
+}
 
 __device__ __forceinline__ uint2 lds_read_b64(const void* p) {
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -303,10 +323,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   f32x16 acc[4][4];
   gemm::zero_acc(acc);
   // Direct copies of one stage: NA (NB) 1 KiB copies for the A (B) tile, copy j going to
-  // wave j % 4, then one 256-byte scale copy per operand per wave.
+  // wave j % 4. A batch of copies (one per K tile) also carries a quarter of a scale group:
+  // two 256-byte copies per wave, each 16 rows x 16 bytes.
   constexpr int NA = PA::TILE / 1024, NB = PB::TILE / 1024;
-  constexpr int DA = NA / 4, DB = NB / 4, DPW = DA + DB + 2, NST = L::NST;
-  uint32_t oa[DA], ob[DB], osa, osb;
+  constexpr int DA = NA / 4, DB = NB / 4, DD = DA + DB, DPW = DD + 2, NST = L::NST;
+  uint32_t oa[DA], ob[DB];
   {
     // lane l of copy j lands at LDS chunk 64 (w + 4j) + l of the tile: row p / CPR, physical
     // chunk p % CPR, which holds the row's logical chunk `logical(...)`. K-major rows past
@@ -323,34 +344,45 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     for (int j = 0; j < DA; j++) oa[j] = offs(PA{}, lda_b, rows_a, mlima, j);
 #pragma unroll
     for (int j = 0; j < DB; j++) ob[j] = offs(PB{}, ldb_b, rows_b, mlimb, j);
-    osa = (uint32_t)(min((int64_t)(64 * w + lane), rows_a - 1) * a.ld_sfa);
-    osb = (uint32_t)(min((int64_t)(64 * w + lane), rows_b - 1) * a.ld_sfb);
   }
   const uint8_t* SA = a.SFA + m0 * a.ld_sfa;
   const uint8_t* SB = a.SFB + n0 * a.ld_sfb;
   const uint32_t lds0 = gemm::lds_addr(lds);
-  // Copy d (of DPW) of tile kt into stage `stage`.
+  const int nfull = (int)(a.K / KT);
+  // Data copy d (of DD) of tile kt into stage `stage`.
   auto copy = [&](int kt, int stage, int d) {
     const uint32_t st = lds0 + stage * L::STAGE;
     if (d < DA) gemm::dma16s(A + kt * stepa, oa[d], st + 1024 * (w + 4 * d));
-    else if (d < DA + DB) gemm::dma16s(B + kt * stepb, ob[d - DA], st + PA::TILE + 1024 * (w + 4 * (d - DA)));
-    else if (d == DA + DB) gemm::dma4s(SA + 4 * kt, osa, st + L::SCALES + 256 * w);
-    else gemm::dma4s(SB + 4 * kt, osb, st + L::SCALES + 1024 + 256 * w);
+    else gemm::dma16s(B + kt * stepb, ob[d - DA], st + PA::TILE + 1024 * (w + 4 * (d - DA)));
   };
-  auto issue = [&](int kt, int stage) {
-#pragma unroll
-    for (int d = 0; d < DPW; d++) copy(kt, stage, d);
+  // Copy c (0, 1) of this wave for quarter j of scale group g (K tiles 4g .. 4g + 3):
+  // rows 64j + 16p .. +15 of operand op (k = 2w + c: op = k / 4, p = k % 4), lane l moving
+  // physical word l % 4 of row 64j + 16p + l / 4. Words of tiles past the last whole
+  // tile re-read the last one, and rows past the operand its last row (unused values).
+  auto slice = [&](int g, int j, int c) {
+    const int k = 2 * w + c, op = k >> 2, R = 64 * j + 16 * (k & 3) + (lane >> 2);
+    const int qw = (lane & 3) ^ ((R >> 4) & 3);
+    const int64_t rows = op ? rows_b : rows_a;
+    const uint32_t off = (uint32_t)(min((int64_t)R, rows - 1) * (op ? a.ld_sfb : a.ld_sfa)) +
+                         4u * (uint32_t)min(4 * g + qw, nfull - 1);
+    gemm::dma4s(op ? SB : SA, off, lds0 + L::RING + (g & 1) * L::RING_BUF + op * 4096 + 16 * (64 * j + 16 * (k & 3)));
+  };
+  // Batch b (issued once tile b's stage has been read): quarter (b + 5) % 4 of scale group
+  // (b + 5) / 4, then the data of tile kb into stage `stage`. Group g's buffer is free once
+  // every wave has read the scales of tile 4g - 5 (before batch 4g - 5), and its quarters are
+  // all in batches 4g - 5 .. 4g - 2, which have landed when tile 4g's scales are read.
+  auto batch_copy = [&](int b, int kb, int stage, int d) {
+    if (d < 2) slice((b + 5) >> 2, (b + 5) & 3, d);
+    else copy(kb, stage, d - 2);
   };
   static_assert(DPW <= 32, "at most two copies per MFMA slot of step 1");
-  // Multiply the tile in stage st: step 1's fragment reads go out between step 0's MFMAs;
-  // then every wave is done with the stage (barrier) and side1(i) runs after step 1's
-  // MFMA i (the copies of the tile that replaces this one, spread over the MFMA slots:
-  // issued in one burst they would hold the waves behind the shared copy path).
-  auto multiply = [&](const uint8_t* st, auto side1) {
+  // Multiply the partial last K tile, held in stage st with its scale words (one per row,
+  // A's then B's) at `scales`: step 1's fragment reads go out between step 0's MFMAs.
+  auto multiply = [&](const uint8_t* st, const uint8_t* scales) {
     uint32_t sa[4], sb[4];
     i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    read_scales(st + L::SCALES, wa, lane, sa);
-    read_scales(st + L::SCALES + 1024, wb, lane, sb);
+    read_scales(scales, wa, lane, sa);
+    read_scales(scales + 1024, wb, lane, sb);
     read_frags<CA, CB, AMN, BMN, 0>(st, st + PA::TILE, wa, wb, lane, fa0, fb0);
     mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, [&](int i) {
       if (i < 8) {
@@ -359,27 +391,72 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
       }
     });
     gemm::lds_barrier();
-    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, side1);
+    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [](int) {});
   };
 
-  // Whole K tiles; tile kt lives in stage kt % NST. Past the last one the copies re-read
-  // the last tile into the stage just released (nobody reads it again), so every
-  // iteration issues the same copies and the wait counts stay fixed.
-  const int nfull = (int)(a.K / KT);
+  // Whole K tiles; tile kt lives in stage kt % NST. One barrier per tile, at the start of
+  // its step 1: every wave has then read the stage's step-1 fragments (issued between the
+  // step-0 MFMAs) and the copies of tile kt + 1 have landed, so the copies of tile kt + NST
+  // go into the stage just read and the scales and step-0 fragments of tile kt + 1 are read
+  // between the step-1 MFMAs, ahead of their use. Past the last tile the copies re-read
+  // the last tile into the stage just released (nobody reads it again), so every iteration
+  // issues the same copies and the wait counts stay fixed; the last iteration's reads of
+  // the next stage and ring buffer fetch values nobody uses.
   if (nfull > 0) {
+    uint32_t sa[4], sb[4], na[4], nb[4];
+    i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    // scale group 0 and the first quarter of group 1 (batches -5 .. -1), then the data of
+    // tiles 0 .. NST - 1
 #pragma unroll
-    for (int i = 0; i < NST; i++) issue(min(i, nfull - 1), i);
-    gemm::stage_barrier<(NST - 1) * DPW>();  // tile 0 has landed
-  }
-  int cur = 0;                               // kt % NST
-  for (int kt = 0; kt < nfull; kt++) {
-    const int knext = min(kt + NST, nfull - 1);
-    multiply(lds + cur * L::STAGE, [&](int i) {
-      if (i < DPW) copy(knext, cur, i);
-      if (i + 16 < DPW) copy(knext, cur, i + 16);   // two 8-bit operands: 18 copies
-    });
-    gemm::stage_barrier<(NST - 1) * DPW>();  // tile kt + 1 has landed
-    cur = cur + 1 == NST ? 0 : cur + 1;
+    for (int j = 0; j < 4; j++) {
+      slice(0, j, 0);
+      slice(0, j, 1);
+    }
+    slice(1, 0, 0);
+    slice(1, 0, 1);
+#pragma unroll
+    for (int i = 0; i < NST; i++)
+#pragma unroll
+      for (int d = 0; d < DD; d++) copy(min(i, nfull - 1), i, d);
+    gemm::stage_barrier<(NST - 1) * DD>();   // the scales and tile 0 have landed
+    read_scales_ring(lds + L::RING, 0, wa, lane, sa);
+    read_scales_ring(lds + L::RING + 4096, 0, wb, lane, sb);
+    read_frags<CA, CB, AMN, BMN, 0>(lds, lds + PA::TILE, wa, wb, lane, fa0, fb0);
+    int cur = 0;                             // kt % NST
+    for (int kt = 0; kt < nfull; kt++) {
+      const uint8_t* st = lds + cur * L::STAGE;
+      const int nxt = cur + 1 == NST ? 0 : cur + 1;
+      const uint8_t* nst = lds + nxt * L::STAGE;
+      const int knext = min(kt + NST, nfull - 1);
+      mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, [&](int i) {
+        if (i < 8) {
+          if (i & 1) fb1[i >> 1] = read_frag<CB, BMN>(st + PA::TILE, wb, i >> 1, 1, lane);
+          else fa1[i >> 1] = read_frag<CA, AMN>(st, wa, i >> 1, 1, lane);
+        }
+      });
+      mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [&](int i) {
+        if (i == 0) {
+          // only the data copies of the batches after tile kt + 1's (tiles kt + 2 ..
+          // kt + NST - 1) may still fly: every scale quarter issued so far has landed
+          gemm::stage_barrier<(NST - 2) * DD>();
+          const uint8_t* ring = lds + L::RING + (((kt + 1) >> 2) & 1) * L::RING_BUF;
+          read_scales_ring(ring, kt + 1, wa, lane, na);
+          read_scales_ring(ring + 4096, kt + 1, wb, lane, nb);
+        }
+        if (i < 8) {
+          if (i & 1) fb0[i >> 1] = read_frag<CB, BMN>(nst + PA::TILE, wb, i >> 1, 0, lane);
+          else fa0[i >> 1] = read_frag<CA, AMN>(nst, wa, i >> 1, 0, lane);
+        }
+        if (i < DPW) batch_copy(kt, knext, cur, i);
+        if (i + 16 < DPW) batch_copy(kt, knext, cur, i + 16);   // two 8-bit operands: 18 copies
+      });
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        sa[t] = na[t];
+        sb[t] = nb[t];
+      }
+      cur = nxt;
+    }
   }
   gemm::wait_dma();                          // the repeated copies too, before LDS is reused
   __syncthreads();
@@ -405,10 +482,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     const uint32_t wsb = mask_scale_word(load_scale_word(a.SFB, a.ld_sfb, n0, a.N, q, nfull), nfull, nblk);
     store_chunks<CA, AMN>(st, q, va);
     store_chunks<CB, BMN>(st + PA::TILE, q, vb);
-    *(BSM_LDS uint32_t*)(st + L::SCALES + 4 * q) = wsa;
-    *(BSM_LDS uint32_t*)(st + L::SCALES + 1024 + 4 * q) = wsb;
+    uint8_t* scales = lds + L::RING;          // one word per row: A's 256, then B's
+    *(BSM_LDS uint32_t*)(scales + 4 * q) = wsa;
+    *(BSM_LDS uint32_t*)(scales + 1024 + 4 * q) = wsb;
     __syncthreads();
-    multiply(st, [](int) {});
+    multiply(st, scales);
     __syncthreads();
   }
   gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, a.accum != 0,

@@ -151,3 +151,22 @@ def test_mx_any_full_size_sampled(O, a_fmt, b_fmt):
     nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, pm, pn)
     assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e2m3", "e2m3"), ("e4m3", "e2m3"), ("e2m1", "e3m2")])
+def test_mx_any_scale_groups(O, a_fmt, b_fmt):
+    """K tile counts around the scale ring's four-tile groups (5, 6, 7, 9 and 13 whole tiles,
+    with and without a partial last tile): groups the last tile leaves partly unused, a last
+    tile that ends its group, and both pipeline depths (three stages for 6-bit x 6-bit, two
+    for 8-bit x 6-bit)."""
+    for i, K in enumerate([640, 768, 896, 1184, 1664, 1696]):
+        M, N = 300, 260
+        accum = i & 1
+        g = case(a_fmt, b_fmt, 130 + i, M, N, K, ld_pad=64 if i % 2 else 0)
+        d0 = np.random.default_rng(40 + i).standard_normal((M, N)).astype(np.float32)
+        say("mx any scale groups", a_fmt, b_fmt, M, N, K, accum)
+        D = run(g, M, N, K, a_fmt, b_fmt, d0 if accum else None, 0, 0, accum)
+        ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
+                                        g["ldb"], g["SFB"], g["ld_sfb"], d0, N, 0, 0, accum)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        assert nb == 0, (K, worst)

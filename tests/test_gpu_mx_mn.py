@@ -87,6 +87,22 @@ def test_mx_mn_vs_oracle(O, a_fmt, b_fmt, amaj, bmaj):
         assert np.isnan(D[:, N:]).all()
 
 
+@pytest.mark.parametrize("a_fmt,b_fmt,amaj,bmaj", [("e4m3", "e4m3", "m", "n"), ("e2m1", "e4m3", "k", "n"),
+                                                   ("e2m1", "e2m1", "m", "k")])
+def test_mx_mn_scale_groups(O, a_fmt, b_fmt, amaj, bmaj):
+    """MN-major storage at K tile counts around the scale ring's four-tile groups (5, 7 and 13
+    whole tiles, one with a partial last tile), both pipeline depths (two stages for two
+    8-bit MN-major operands, three otherwise)."""
+    for i, K in enumerate([640, 896, 1696]):
+        M, N = 260, 300
+        g = case(a_fmt, b_fmt, amaj, bmaj, 150 + i, M, N, K)
+        say("mx mn scale groups", a_fmt, b_fmt, amaj, bmaj, M, N, K)
+        D = run(g, M, N, K, a_fmt, b_fmt, amaj, bmaj)
+        ref, bound = oracle(O, g, M, N, K, a_fmt, b_fmt, amaj, bmaj)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        assert nb == 0, (K, worst)
+
+
 @pytest.mark.parametrize("a_fmt,b_fmt,amaj,bmaj", [("e2m3", "e4m3", "k", "n"), ("e4m3", "e3m2", "m", "k"),
                                                    ("e2m1", "e2m3", "m", "k"), ("e3m2", "e2m1", "k", "n")])
 def test_mx_mn_with_6bit_kmajor_operand(O, a_fmt, b_fmt, amaj, bmaj):

@@ -275,6 +275,40 @@ def test_box_steps_vs_oracle(O, dtype, swz):
     assert np.array_equal(host(dd, NPDT[dtype], mem.shape), want)
 
 
+@pytest.mark.parametrize("dtype,swz,rank", [("bf16", 3, 3), ("u8", 0, 3), ("f32", 1, 2), ("e4m3", 2, 3),
+                                            ("bf16", 3, 1)])
+def test_box_load_steps_adjacent_runs(O, dtype, swz, rank):
+    """Repeat axes whose last axis steps by exactly the box width along the innermost
+    dimension (boxes side by side, loaded in runs of up to eight per workgroup): 11 boxes per
+    repeat row (a partial run), the first and last boxes partly out of range, element
+    stride 2 on an outer axis; images against the oracle."""
+    rng = np.random.default_rng([13, bsm.DTYPE[dtype], swz, rank])
+    esz = bsm.ESIZE[dtype]
+    inner = {0: 48 // esz, 1: 32 // esz, 2: 64 // esz, 3: 128 // esz}[swz]
+    full = (5, 21, 10 * inner + 7)[3 - rank:]
+    pitch = (full[-1] * esz + 15) // 16 * 16 // esz + 16 // esz
+    mem = rng.integers(0, 1 << (8 * esz), full[:-1] + (pitch,), dtype=np.uint64).astype(NPDT[dtype])
+    strides = tuple(mem.strides[:-1]) + (esz,)
+    box, estr = ((2, 6, inner)[3 - rank:], (1, 2, 1)[3 - rank:])
+    coords = (-1, 4, -(inner // 2))[3 - rank:]
+    reps = (3, 11)[max(0, 2 - rank):] if rank > 1 else (11,)
+    steps = ([(2, 0, 0), (0, 0, inner)] if rank == 3 else [(5, 0), (0, inner)]) if rank > 1 else [(inner,)]
+    fill = 1 if dtype in ("bf16", "f32", "e4m3") else 0
+    stride = O.image_stride(dtype, box, estr, swz)
+    n = int(np.prod(reps))
+    say("box_load_steps adjacent", dtype, swz, full, box, reps)
+    dimg = dev_like(n * stride, 0xA5)
+    bsm.bsm_tile_box_load_steps(bsm.tensor_desc(dev(mem), dtype, full, strides), bsm.box_desc(box, estr, swz, fill),
+                                coords, reps, steps, dimg)
+    got = host(dimg, np.uint8).reshape(n, stride)
+    exp = O.box_load_steps(mem, dtype, full, strides, box, estr, coords, reps, steps, swz, fill).reshape(n, stride)
+    nbytes = int(np.prod(O.image_extents(box, estr))) * esz
+    written = np.zeros(stride, bool)
+    written[[O.swizzle(o, swz) for o in range(nbytes)]] = True
+    assert np.array_equal(got[:, written], exp[:, written])
+    assert (got[:, ~written] == 0xA5).all()
+
+
 def test_box_store_steps_reduce_add(O):
     """Add-reduction with repeat axes onto disjoint boxes (a 3 x 2 grid of (16, 32) bf16 boxes)."""
     rng = np.random.default_rng(12)

@@ -62,8 +62,8 @@ KERNEL_SOURCES = {
     "gather4": ["k_tile.hip", "bsm_device.hpp"],
     "scatter4": ["k_tile.hip", "bsm_device.hpp"],
     "box_load_rank3": ["k_tile.hip", "bsm_device.hpp"],
-    "gemm_e4m3_e2m1": ["k_gemm_mx_any.hip", "gemm_common.hpp", "bsm_device.hpp"],
-    "gemm_e2m3_e2m3": ["k_gemm_mx_any.hip", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_e4m3_e2m1": ["k_gemm_mx_any.hip", "gemm_mx_any.hpp", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_e2m3_e2m3": ["k_gemm_mx_any.hip", "gemm_mx_any.hpp", "gemm_common.hpp", "bsm_device.hpp"],
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_busy_bench_step.md")

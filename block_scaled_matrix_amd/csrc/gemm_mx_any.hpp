@@ -103,15 +103,20 @@ struct Lay {
 };
 
 // Scale ring: word q (K tile 4g + q) of row R of a group buffer sits at physical word
-// q ^ ((R >> 4) & 3), so the 32 consecutive rows one read instruction touches fall in 32
-// distinct banks.
-__device__ __forceinline__ uint32_t ring_word_offset(int R, int q) { return (uint32_t)(16 * R + 4 * (q ^ ((R >> 4) & 3))); }
+// q ^ ((R >> 4) & 3) in A's half and q ^ ((R >> 4) & 3) ^ 2 in B's, so the 32 consecutive
+// rows one read instruction touches fall in 32 distinct banks, and the A and B words of
+// one row (4 KiB apart, which the compiler fetches with one two-address read) in
+// different ones.
+__device__ __forceinline__ uint32_t ring_word_offset(int op, int R, int q) {
+  return (uint32_t)(16 * R + 4 * (q ^ ((R >> 4) & 3) ^ (op ? 2 : 0)));
+}
 
 // This lane's scale words of K tile kt for its four rows (base + 32t + l%32) from the ring
-// buffer of kt's group (A's or B's half).
-__device__ __forceinline__ void read_scales_ring(const uint8_t* half, int kt, int base, int lane, uint32_t (&s)[4]) {
+// buffer of kt's group (operand op's half).
+__device__ __forceinline__ void read_scales_ring(const uint8_t* half, int op, int kt, int base, int lane,
+                                                 uint32_t (&s)[4]) {
 #pragma unroll
-  for (int t = 0; t < 4; t++) s[t] = *(const BSM_LDS uint32_t*)(half + ring_word_offset(base + 32 * t + (lane & 31), kt & 3));
+  for (int t = 0; t < 4; t++) s[t] = *(const BSM_LDS uint32_t*)(half + ring_word_offset(op, base + 32 * t + (lane & 31), kt & 3));
 }
 
 __device__ __forceinline__ uint2 lds_read_b64(const void* p) {
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   // tile re-read the last one, and rows past the operand its last row (unused values).
   auto slice = [&](int g, int j, int c) {
     const int k = 2 * w + c, op = k >> 2, R = 64 * j + 16 * (k & 3) + (lane >> 2);
-    const int qw = (lane & 3) ^ ((R >> 4) & 3);
+    const int qw = (lane & 3) ^ ((R >> 4) & 3) ^ (op ? 2 : 0);
     const int64_t rows = op ? rows_b : rows_a;
     const uint32_t off = (uint32_t)(min((int64_t)R, rows - 1) * (op ? a.ld_sfb : a.ld_sfa)) +
                          4u * (uint32_t)min(4 * g + qw, nfull - 1);
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
 #pragma unroll
       for (int d = 0; d < DD; d++) copy(min(i, nfull - 1), i, d);
     gemm::stage_barrier<(NST - 1) * DD>();   // the scales and tile 0 have landed
-    read_scales_ring(lds + L::RING, 0, wa, lane, sa);
-    read_scales_ring(lds + L::RING + 4096, 0, wb, lane, sb);
+    read_scales_ring(lds + L::RING, 0, 0, wa, lane, sa);
+    read_scales_ring(lds + L::RING + 4096, 1, 0, wb, lane, sb);
     read_frags<CA, CB, AMN, BMN, 0>(lds, lds + PA::TILE, wa, wb, lane, fa0, fb0);
     int cur = 0;                             // kt % NST
     for (int kt = 0; kt < nfull; kt++) {
@@ -440,8 +445,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
           // kt + NST - 1) may still fly: every scale quarter issued so far has landed
           gemm::stage_barrier<(NST - 2) * DD>();
           const uint8_t* ring = lds + L::RING + (((kt + 1) >> 2) & 1) * L::RING_BUF;
-          read_scales_ring(ring, kt + 1, wa, lane, na);
-          read_scales_ring(ring + 4096, kt + 1, wb, lane, nb);
+          read_scales_ring(ring, 0, kt + 1, wa, lane, na);
+          read_scales_ring(ring + 4096, 1, kt + 1, wb, lane, nb);
         }
         if (i < 8) {
           if (i & 1) fb0[i >> 1] = read_frag<CB, BMN>(nst + PA::TILE, wb, i >> 1, 0, lane);

@@ -103,12 +103,12 @@ struct Lay {
 };
 
 // Scale ring: word q (K tile 4g + q) of row R of a group buffer sits at physical word
-// q ^ ((R >> 4) & 3) in A's half and q ^ ((R >> 4) & 3) ^ 2 in B's, so the 32 consecutive
-// rows one read instruction touches fall in 32 distinct banks, and the A and B words of
-// one row (4 KiB apart, which the compiler fetches with one two-address read) in
-// different ones.
+// q ^ ((R >> 4) & 3) ^ ((R >> 6) & 1), XOR 2 in B's half: the 32 consecutive rows one read
+// instruction touches fall in 32 distinct banks, and so do the words of rows 32, 64 or 96
+// apart (blocks t and t + 1 .. 3, multiples of 512 bytes apart), which the compiler may
+// fetch with one two-address read.
 __device__ __forceinline__ uint32_t ring_word_offset(int op, int R, int q) {
-  return (uint32_t)(16 * R + 4 * (q ^ ((R >> 4) & 3) ^ (op ? 2 : 0)));
+  return (uint32_t)(16 * R + 4 * (q ^ ((R >> 4) & 3) ^ ((R >> 6) & 1) ^ (op ? 2 : 0)));
 }
 
 // This lane's scale words of K tile kt for its four rows (base + 32t + l%32) from the ring
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   // tile re-read the last one, and rows past the operand its last row (unused values).
   auto slice = [&](int g, int j, int c) {
     const int k = 2 * w + c, op = k >> 2, R = 64 * j + 16 * (k & 3) + (lane >> 2);
-    const int qw = (lane & 3) ^ ((R >> 4) & 3) ^ (op ? 2 : 0);
+    const int qw = (lane & 3) ^ ((R >> 4) & 3) ^ ((R >> 6) & 1) ^ (op ? 2 : 0);
     const int64_t rows = op ? rows_b : rows_a;
     const uint32_t off = (uint32_t)(min((int64_t)R, rows - 1) * (op ? a.ld_sfb : a.ld_sfa)) +
                          4u * (uint32_t)min(4 * g + qw, nfull - 1);

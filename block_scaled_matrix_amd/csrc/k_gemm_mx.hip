@@ -78,9 +78,9 @@ __device__ __forceinline__ void issue_data(const Ops& o, const uint8_t* ga, cons
 
 // Scale ring. Row R of an operand's group buffer holds the 8 scale words of K tiles
 // G g .. G g + G - 1 (SFW words per tile), logical word q at physical word
-// q ^ ((R >> 3) & 7) (A) or q ^ ((R >> 3) & 7) ^ 4 (B), so the 32 rows one wave reads per
-// block land in 32 distinct banks, and the A and B words of one row (8 KiB apart, which
-// the compiler fetches with one two-address read) in different ones.
+// q ^ sw(R), sw(R) = ((R >> 3) & 7) ^ 4 ((R >> 6) & 1): the 32 rows one wave reads per
+// block land in 32 distinct banks, and so do the words of rows 64 apart (blocks t and
+// t + 2, 2 KiB apart), which the compiler fetches with one two-address read.
 // Group g lives in buffer g & 1 and is copied in G slices of SLICE_ROWS rows per
 // operand, one slice per K tile while group g - 1 is in use. Copy c of this wave for
 // slice j of group g: 8 rows, lane l -> row 8 (l / 8) + ..., physical word l % 8.
@@ -91,7 +91,7 @@ __device__ __forceinline__ void issue_slice(const Ops& o, int g, int j, int c, u
   const int k = w * F::SLICE_COPIES + c;
   const int op = k / PER_OP, ii = k % PER_OP;
   const int R = j * F::SLICE_ROWS + 8 * ii + (lane >> 3);
-  const int q = (lane & 7) ^ ((R >> 3) & 7) ^ (op ? 4 : 0);
+  const int q = (lane & 7) ^ ((R >> 3) & 7) ^ (((R >> 6) & 1) << 2);
   const uint32_t word = (uint32_t)min(8 * g + q, o.ldw - 1);
   const uint8_t* base = op ? o.SFB : o.SFA;
   const uint32_t off = (uint32_t)min(R, op ? o.lim_b : o.lim_a) * (op ? o.ld_sfb : o.ld_sfa) + 4 * word;
@@ -110,10 +110,11 @@ __device__ __forceinline__ void read_scales(const uint8_t* lds, int kt, int wa, 
   for (int q = 0; q < F::SFW; q++)
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-      const int sw = (4 * t + (r >> 3)) & 7;  // (row >> 3) & 7 for rows wave base + 32t + r
-      const uint32_t o = 32 * (32 * t + r);
-      sa[t][q] = *(const BSM_LDS uint32_t*)(buf + 32 * wa + o + 4 * ((w0 + q) ^ sw));
-      sb[t][q] = *(const BSM_LDS uint32_t*)(buf + RING_OP + 32 * wb + o + 4 * ((w0 + q) ^ sw ^ 4));
+      // sw(R) for rows R = wave base (0 or 128) + 32t + r
+      const int sw = ((4 * t + (r >> 3)) & 7) ^ (((t >> 1) & 1) << 2);
+      const uint32_t o = 32 * (32 * t + r) + 4 * ((w0 + q) ^ sw);
+      sa[t][q] = *(const BSM_LDS uint32_t*)(buf + 32 * wa + o);
+      sb[t][q] = *(const BSM_LDS uint32_t*)(buf + RING_OP + 32 * wb + o);
     }
 }
 

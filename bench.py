@@ -31,6 +31,9 @@ reported under `widened` (not part of `value`):
 (the mixed pair runs at the 8-bit MFMA rate, peak 5033.2 TFLOP/s; FP6 pairs at the 4-bit
 rate, peak 10066.3 TFLOP/s)
 
+`context` holds one reference point that is not part of the path: torch.mm (hipBLASLt) on the
+bf16 workload's shape with a fresh bf16 output, timed the same way after the step.
+
 --epilogue silu_affine fuses the scalar epilogue f(x) = x / (1 + exp(-x)) * 2 + 1 (the example call
 of "Explicit CUDA tile patterns", Scalar compositions) into the three GEMMs' stores (bsm_gemm_ewise, bsm_gemm_block_scale_ewise); the
 rest of the step is unchanged, and config.epilogue names it.
@@ -396,6 +399,18 @@ def main():
         if mf is not None:
             wide[name]["mfma_busy"], wide[name]["clock_ghz"] = mf
         log(f"{name} (widened): {ms:.4f} ms  {wide[name]['achieved']:.1f} {unit}")
+    # context, not part of the path: the vendor library (torch.mm -> hipBLASLt) on the bf16
+    # workload's shape, fresh output, B as stored (K, N); timed the same way after the step
+    g = inp["bf16"]
+    A16 = g["A"].view(torch.bfloat16).reshape(g["M"], g["K"])
+    B16 = g["B"].view(torch.bfloat16).reshape(g["K"], g["N"])
+    mm = [("torch_mm_bf16", lambda: torch.mm(A16, B16), 2.0 * g["M"] * g["N"] * g["K"], "TFLOP/s", PEAK["bf16_TFs"])]
+    mm[0][1]()
+    torch.cuda.synchronize()
+    context = {"torch_mm_bf16": rate_entry(time_launches(mm, args.steps, stream)[0], *mm[0][2:])}
+    context["torch_mm_bf16"]["note"] = ("hipBLASLt through torch.mm, bf16 8192^3, fresh bf16 output, no accumulation: "
+                                        "a vendor-library reference point, not part of the step")
+    log(f"torch_mm_bf16 (context): {context['torch_mm_bf16']['ms']:.4f} ms  {context['torch_mm_bf16']['achieved']:.1f} TFLOP/s")
     dom = max((n for n in per if n != "add_one"), key=lambda n: per[n]["ms"])
     d = per[dom]
     gemm_flops = sum(k[2] for k in ks if k[0].startswith("gemm"))
@@ -419,6 +434,7 @@ def main():
                    f"{args.epilogue}(scale {EPILOGUE_ARGS[0]:g}, bias {EPILOGUE_ARGS[1]:g})"},
         "per_kernel": per,
         "widened": wide,
+        "context": context,
         "roofline": {"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
                      "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dom)},
         "cpu_baseline": cpu,

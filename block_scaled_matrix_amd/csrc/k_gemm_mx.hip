@@ -77,13 +77,12 @@ __device__ __forceinline__ void issue_data(const Ops& o, const uint8_t* ga, cons
 }
 
 // Scale ring. Row R of an operand's group buffer holds the 8 scale words of K tiles
-// G g .. G g + G - 1 (SFW words per tile). One word per tile (8-bit operands): logical word
-// q at physical word q ^ sw(R), sw(R) = ((R >> 3) & 7) ^ 4 ((R >> 6) & 1). Two words per
-// tile (E2M1): the tile's pair P (words 2P, 2P + 1, read with one 64-bit read) at physical
-// pair P ^ s2(R), s2(R) = ((R >> 3) & 3) ^ 2 ((R >> 6) & 1). Either way the 32 rows one
-// wave reads per block land in distinct banks, and so do the words of rows 64 apart
-// (blocks t and t + 2, 2 KiB apart), which the compiler may fetch with one two-address read.
-__device__ __forceinline__ int ring_sw(int R) { return ((R >> 3) & 7) ^ (((R >> 6) & 1) << 2); }
+// G g .. G g + G - 1 (SFW words per tile) as four 8-byte pairs, read with one 64-bit read
+// each: pair P (words 2P, 2P + 1: an E2M1 tile's two words, or the words of two
+// consecutive 8-bit tiles) at physical pair P ^ s2(R), s2(R) = ((R >> 3) & 3) ^ 2 ((R >> 6)
+// & 1), so the 32 rows one wave reads per block land in distinct bank pairs, and so do the
+// pairs of rows 64 apart (blocks t and t + 2, 2 KiB apart), which the compiler may fetch
+// with one two-address read.
 __device__ __forceinline__ int ring_s2(int R) { return ((R >> 3) & 3) ^ (((R >> 6) & 1) << 1); }
 // Group g lives in buffer g & 1 and is copied in G slices of SLICE_ROWS rows per
 // operand, one slice per K tile while group g - 1 is in use. Copy c of this wave for
@@ -96,42 +95,33 @@ __device__ __forceinline__ void issue_slice(const Ops& o, int g, int j, int c, u
   const int op = k / PER_OP, ii = k % PER_OP;
   const int R = j * F::SLICE_ROWS + 8 * ii + (lane >> 3);
   const int p = lane & 7;  // physical word
-  const int q = FMT == 4 ? 2 * ((p >> 1) ^ ring_s2(R)) + (p & 1) : p ^ ring_sw(R);
+  const int q = 2 * ((p >> 1) ^ ring_s2(R)) + (p & 1);
   const uint32_t word = (uint32_t)min(8 * g + q, o.ldw - 1);
   const uint8_t* base = op ? o.SFB : o.SFA;
   const uint32_t off = (uint32_t)min(R, op ? o.lim_b : o.lim_a) * (op ? o.ld_sfb : o.ld_sfa) + 4 * word;
   gemm::dma4s(base, off, ring + (g & 1) * RING_GROUP + op * RING_OP + 32 * (j * F::SLICE_ROWS + 8 * ii));
 }
 
-// Raw scale words of K tile kt for this lane's rows (wave base + 32t + l%32).
+// Raw scale words for this lane's rows (wave base + 32t + l%32): the pair holding K tile kt's
+// words, [t][0] and [t][1]: for E2M1 the tile's two words, for 8-bit operands (kt even) the
+// words of tiles kt and kt + 1.
 template <int FMT>
 __device__ __forceinline__ void read_scales(const uint8_t* lds, int kt, int wa, int wb, int lane, uint32_t (&sa)[4][2],
                                             uint32_t (&sb)[4][2]) {
   typedef Fmt<FMT> F;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   const uint8_t* buf = lds + RING + ((kt / F::G) & 1) * RING_GROUP;
   const int r = lane & 31;
-  if constexpr (FMT == 4) {
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const int P = FMT == 4 ? kt % F::G : (kt % F::G) >> 1;
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      // s2(R) for rows R = wave base (0 or 128) + 32t + r
-      const int s2 = ((r >> 3) & 3) ^ (((t >> 1) & 1) << 1);
-      const uint32_t o = 32 * (32 * t + r) + 8 * ((kt % F::G) ^ s2);
-      const u32x2 x = *(const BSM_LDS u32x2*)(buf + 32 * wa + o);
-      const u32x2 y = *(const BSM_LDS u32x2*)(buf + RING_OP + 32 * wb + o);
-      sa[t][0] = x[0]; sa[t][1] = x[1];
-      sb[t][0] = y[0]; sb[t][1] = y[1];
-    }
-  } else {
-    const int w0 = kt % F::G;
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      // sw(R) for rows R = wave base (0 or 128) + 32t + r
-      const int sw = ((4 * t + (r >> 3)) & 7) ^ (((t >> 1) & 1) << 2);
-      const uint32_t o = 32 * (32 * t + r) + 4 * (w0 ^ sw);
-      sa[t][0] = *(const BSM_LDS uint32_t*)(buf + 32 * wa + o);
-      sb[t][0] = *(const BSM_LDS uint32_t*)(buf + RING_OP + 32 * wb + o);
-    }
+  for (int t = 0; t < 4; t++) {
+    // s2(R) for rows R = wave base (0 or 128) + 32t + r
+    const int s2 = ((r >> 3) & 3) ^ (((t >> 1) & 1) << 1);
+    const uint32_t o = 32 * (32 * t + r) + 8 * (P ^ s2);
+    const u32x2 x = *(const BSM_LDS u32x2*)(buf + 32 * wa + o);
+    const u32x2 y = *(const BSM_LDS u32x2*)(buf + RING_OP + 32 * wb + o);
+    sa[t][0] = x[0]; sa[t][1] = x[1];
+    sb[t][0] = y[0]; sb[t][1] = y[1];
   }
 }
 
@@ -373,7 +363,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
       mfma_step_il<0, CA, CB, 1>(f1, sa, sb, acc, [&](int i) {
         if (i == 4) gemm::stage_barrier<10>();
         if (i < 12) copy(6 + i);
-        if (i == 4) read_scales<0>(lds, kt + 1, wa, wb, lane, ra, rb);
+        // tile kt + 1's words: one pair read serves tiles kt + 1 (even) and kt + 2
+        if (i == 4) {
+          if (((kt + 1) & 1) == 0) {
+            read_scales<0>(lds, kt + 1, wa, wb, lane, ra, rb);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+              ra[t][0] = ra[t][1];
+              rb[t][0] = rb[t][1];
+            }
+          }
+        }
         if (i >= 4 && i < 12) {
           read_frag<0>(nst, 0, 2 * (i - 4), wa, wb, lane, f0);
           read_frag<0>(nst, 0, 2 * (i - 4) + 1, wa, wb, lane, f0);

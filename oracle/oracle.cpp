@@ -665,6 +665,7 @@ int64_t oracle_check_gemm(const float* D, int64_t rows, int64_t cols, int64_t ld
       double d = (double)D[r * ldd + c], e = ref[r * cols + c], b = bound[r * cols + c];
       bool ok;
       if (std::isnan(e) || std::isnan(d)) ok = std::isnan(e) && std::isnan(d);
+      else if (std::isinf(e) || std::isinf(d)) ok = d == e;   // an infinity matches only itself
       else {
         double err = std::fabs(d - e);
         ok = err <= tol * b + std::ldexp(std::fabs(e), -24);

@@ -260,6 +260,21 @@ def test_check_gemm_flags_planted_errors(O):
     assert O.check_gemm(np.array([[0, -0.0], [1e-30, 0]], np.float32), z, z, 2e-3)[0] == 1  # exact where bound 0
 
 
+def test_check_gemm_infinities(O):
+    """An infinite reference (an E5M2 infinity times a nonzero finite value) matches exactly the
+    same infinity: +inf = +inf and -inf = -inf pass; the other sign, a finite value or NaN fail."""
+    inf = np.inf
+    ref = np.array([[inf, -inf, inf, -inf, inf, 1.0]])
+    bound = np.array([[inf, inf, inf, inf, inf, 1.0]])
+    D = np.array([[inf, -inf, inf, -inf, inf, 1.0]], np.float32)
+    assert O.check_gemm(D, ref, bound, 1e-5)[0] == 0
+    for j, wrong in [(0, -inf), (1, inf), (2, 3.0e38), (3, np.nan), (5, inf)]:
+        D2 = D.copy()
+        D2[0, j] = wrong
+        nb, first, _ = O.check_gemm(D2, ref, bound, 1e-5)
+        assert nb == 1 and first == j, (j, wrong)
+
+
 PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e5m2"), ("e2m3", "e4m3"), ("e2m1", "e3m2"),
          ("e3m2", "e2m3")]
 

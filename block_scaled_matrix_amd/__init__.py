@@ -24,7 +24,7 @@ EWISE = {"none": 0, "silu_affine": 1}
 EXPORTS = ("bsm_image_stride", "bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy",
            "bsm_tile_box_load_steps", "bsm_tile_box_store_steps", "bsm_tile_gather4", "bsm_tile_scatter4", "bsm_gemm",
            "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise", "bsm_gemm_block_scale_major",
-           "bsm_tile_add_scalar_f32", "bsm_debug_fragments", "bsm_debug_fragment_shape", "bsm_last_error")
+           "bsm_gemm_block_scale_fastacc", "bsm_tile_add_scalar_f32", "bsm_debug_fragments", "bsm_debug_fragment_shape", "bsm_last_error")
 
 
 class BsmError(RuntimeError):
@@ -79,6 +79,7 @@ def lib():
         L.bsm_gemm_block_scale_ewise.argtypes = L.bsm_gemm_block_scale.argtypes[:-1] + [C.POINTER(bsm_ewise), P]
         L.bsm_gemm_block_scale_major.argtypes = [I64, I64, I64, I32, P, I64, C.c_char, P, I64, I32, P, I64, C.c_char,
                                                  P, I64, P, I64, C.c_int, C.c_int, C.c_int, C.POINTER(bsm_ewise), P]
+        L.bsm_gemm_block_scale_fastacc.argtypes = L.bsm_gemm_block_scale_ewise.argtypes
         L.bsm_tile_add_scalar_f32.argtypes = [P, P, I64, C.c_float, P]
         L.bsm_debug_fragments.argtypes = [P, I64, I64, C.c_char, P, P]
         L.bsm_debug_fragment_shape.restype = None
@@ -87,7 +88,8 @@ def lib():
                       "bsm_tile_box_store_steps", "bsm_tile_gather4",
                       "bsm_tile_scatter4", "bsm_gemm",
                       "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise",
-                      "bsm_gemm_block_scale_major", "bsm_tile_add_scalar_f32", "bsm_debug_fragments"):
+                      "bsm_gemm_block_scale_major", "bsm_gemm_block_scale_fastacc", "bsm_tile_add_scalar_f32",
+                      "bsm_debug_fragments"):
             getattr(L, rc_fn).restype = C.c_int
         _lib = L
     return _lib
@@ -241,6 +243,13 @@ def bsm_gemm_block_scale_major(M, N, K, a_fmt: str, A, lda, a_major: str, SFA, l
                                             DTYPE[b_fmt], _ptr(B), ldb, b_major.encode(), _ptr(SFB), ld_sfb, _ptr(D),
                                             ldd, neg_a, neg_b, accum, C.byref(ew) if ew is not None else None,
                                             _stream(stream)))
+
+
+def bsm_gemm_block_scale_fastacc(M, N, K, a_fmt: str, A, lda, SFA, ld_sfa, b_fmt: str, B, ldb, SFB, ld_sfb, D, ldd,
+                                 neg_a=0, neg_b=0, accum=0, ew: bsm_ewise | None = None, stream=None):
+    _check(lib().bsm_gemm_block_scale_fastacc(M, N, K, DTYPE[a_fmt], _ptr(A), lda, _ptr(SFA), ld_sfa, DTYPE[b_fmt],
+                                              _ptr(B), ldb, _ptr(SFB), ld_sfb, _ptr(D), ldd, neg_a, neg_b, accum,
+                                              C.byref(ew) if ew is not None else None, _stream(stream)))
 
 
 def bsm_tile_add_scalar_f32(src, dst, n: int, s: float, stream=None):

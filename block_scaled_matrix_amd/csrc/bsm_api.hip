@@ -418,7 +418,8 @@ int bsm_gemm_ewise(int64_t M, int64_t N, int64_t K, int32_t ab, const void* A, i
 static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
                             char a_major, const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B,
                             int64_t ldb, char b_major, const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd,
-                            int neg_a, int neg_b, int accum, const bsm_ewise& ew, void* stream, const char* name) {
+                            int neg_a, int neg_b, int accum, const bsm_ewise& ew, void* stream, const char* name,
+                            int window = 0) {
   int rc;
   if ((rc = check_flag(neg_a, "neg_a")) || (rc = check_flag(neg_b, "neg_b")) || (rc = check_flag(accum, "accum")))
     return rc;
@@ -469,6 +470,7 @@ static int gemm_block_scale(int64_t M, int64_t N, int64_t K, int32_t a_fmt, cons
   g.SFA = SFA; g.ld_sfa = ld_sfa; g.SFB = SFB; g.ld_sfb = ld_sfb;
   g.D = D; g.ldd = ldd; g.negate = neg_a ^ neg_b; g.accum = accum;
   g.ew_op = ew.op; g.ew_scale = ew.scale; g.ew_bias = ew.bias;
+  g.mx_window = window;
   hipError_t e = bsm::launch_gemm_mx(g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, name);
   return ok();
@@ -501,6 +503,17 @@ int bsm_gemm_block_scale_major(int64_t M, int64_t N, int64_t K, int32_t a_fmt, c
   return gemm_block_scale(M, N, K, a_fmt, A, lda, a_major, SFA, ld_sfa, b_fmt, B, ldb, b_major, SFB, ld_sfb, D, ldd,
                           neg_a, neg_b, accum, ew ? *ew : bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream,
                           "bsm_gemm_block_scale_major");
+}
+
+int bsm_gemm_block_scale_fastacc(int64_t M, int64_t N, int64_t K, int32_t a_fmt, const void* A, int64_t lda,
+                                 const uint8_t* SFA, int64_t ld_sfa, int32_t b_fmt, const void* B, int64_t ldb,
+                                 const uint8_t* SFB, int64_t ld_sfb, float* D, int64_t ldd, int neg_a, int neg_b,
+                                 int accum, const bsm_ewise* ew, void* stream) {
+  int rc;
+  if (ew && (rc = check_ewise(ew))) return rc;
+  return gemm_block_scale(M, N, K, a_fmt, A, lda, 'k', SFA, ld_sfa, b_fmt, B, ldb, 'k', SFB, ld_sfb, D, ldd, neg_a,
+                          neg_b, accum, ew ? *ew : bsm_ewise{BSM_EW_NONE, 1.0f, 0.0f}, stream,
+                          "bsm_gemm_block_scale_fastacc", 1);
 }
 
 int bsm_tile_add_scalar_f32(const float* src, float* dst, int64_t n, float s, void* stream) {

@@ -71,11 +71,14 @@ struct GemmArgs {
   int32_t accum;
   int32_t ew_op;        // bsm_ewise_op applied to each output before its store (0: none)
   float ew_scale, ew_bias;
+  int32_t mx_window;    // block scaled: 1 = every pairing on the scaled f8f6f4 MFMA (its 2^-13 block
+                        // window), 0 = exact products (bf16 MFMA) for the pairings that need them
 };
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
-// Any pairing of E4M3, E5M2, E2M3, E3M2, E2M1 except 8-bit x 8-bit and E2M1 x E2M1 (K > 0).
+// Any pairing of E4M3, E5M2, E2M3, E3M2, E2M1 except E2M1 x E2M1, and except 8-bit x 8-bit
+// when mx_window is set (K > 0).
 hipError_t launch_gemm_mx_any(const GemmArgs& a, hipStream_t st);
 // One or both operands MN-major (A only, B only, both); an MN-major operand is E4M3, E5M2 or
 // E2M1 (K > 0).

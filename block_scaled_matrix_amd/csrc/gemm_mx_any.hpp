@@ -34,6 +34,21 @@
 // fragments between step 1's, so no K tile starts by waiting for the LDS. A partial last
 // K tile goes through registers with zero elements and unit scales past K.
 //
+// Two ways to multiply a step's fragments (template parameter BF):
+//  - the scaled f8f6f4 MFMA (BF false). It sums the products of one 32-K scale block on a grid
+//    of 2^-13 times the block's largest |product| (measured on the device), which is exact only
+//    when every product of the pair's formats is a multiple of that grid (E2M1 x E2M1, E2M3 x
+//    E2M3, E2M1 x E2M3, E2M1 x E3M2);
+//  - exact products (BF true), for every pairing with a wider product range: each operand
+//    element times its block scale is converted to bf16 in registers (exact: 2 to 4 significant
+//    bits and an exponent inside bf16's range), and the products are summed by the bf16
+//    32x32x16 MFMA, which keeps every product bit down to about 2^-24 of the largest term of
+//    each instruction (measured on the device). The conversion reads the scale as E8M0 from the
+//    exponent field of a float (code << 23; code 255 gives NaN), so it applies the scale exactly.
+//    Every format is then read so that lane half h holds the contiguous k in [32h, +32) of the
+//    64-K step, element 8j + e feeding the bf16 MFMA j of the step at k 8h + e, for both
+//    operands alike; one step is four bf16 MFMAs per accumulator, at half the 8-bit MFMA rate.
+//
 // MN-major operands (K rows with M or N contiguous; 8-bit and E2M1 elements): the tile is
 // 128 k-rows of the workgroup's 256 M/N elements, copied as they are, and the fragments
 // come from gfx950's transposing LDS reads (probed on the device): within a 16-lane group
@@ -55,6 +70,13 @@ namespace mxany {
 constexpr int BM = 256, BN = 256, KT = 128;
 
 __host__ __device__ constexpr int fmt_bits(int c) { return c <= 1 ? 8 : (c <= 3 ? 6 : 4); }
+
+// True when some product of the two formats is not a multiple of 2^-13 times the largest
+// product the formats can form, so the scaled MFMA's block sum may drop bits: any 8-bit
+// operand, and E3M2 with E3M2 or E2M3 (E3M2 values are multiples of 2^-4 up to 28).
+__host__ __device__ constexpr bool wide_products(int ca, int cb) {
+  return fmt_bits(ca) == 8 || fmt_bits(cb) == 8 || (ca == 3 && cb != 4) || (cb == 3 && ca != 4);
+}
 
 // bsm_dtype -> MFMA format code
 inline int mfma_code(int32_t dt) {
@@ -216,8 +238,10 @@ __device__ __forceinline__ void read_scales(const uint8_t* area, int base, int l
   for (int t = 0; t < 4; t++) s[t] = *(const BSM_LDS uint32_t*)(area + 4 * (base + 32 * t + (lane & 31)));
 }
 
-// Operand registers of 64-K step s for the lane's row of 32-row block t.
-template <int C, bool MN>
+// Operand registers of 64-K step s for the lane's row of 32-row block t. With BF (the exact-
+// products route) an 8-bit operand is read with the contiguous k in [32h, +32) of the step in
+// lane half h, the order of the 6- and 4-bit formats.
+template <int C, bool MN, bool BF = false>
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t, int s, int lane) {
   typedef Op<C, MN> P;
   const int h = lane >> 5;
@@ -230,7 +254,7 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t,
     if (P::BITS == 8) {
 #pragma unroll
       for (int r = 0; r < 4; r++) {   // k 16h + 8r' (r' = r & 1) and 32 + ..., eight k-rows each
-        const int kb = 64 * s + 16 * h + 8 * (r & 1) + 32 * (r >> 1);
+        const int kb = BF ? 64 * s + 32 * h + 8 * r : 64 * s + 16 * h + 8 * (r & 1) + 32 * (r >> 1);
         const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((BSM_LDS v2i*)at(kb + (i >> 1), m0 + 8 * (i & 1)));
         v[2 * r] = x[0];
         v[2 * r + 1] = x[1];
@@ -252,7 +276,8 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t,
   // logical byte offset o of the row -> its place in the permuted row
   auto at = [&](int o) { return row + 16 * P::phys(o >> 4, r) + (o & 15); };
   if (P::BITS == 8) {
-    const uint4 x = lds_read_b128(at(64 * s + 16 * h)), y = lds_read_b128(at(64 * s + 32 + 16 * h));
+    const int o0 = BF ? 64 * s + 32 * h : 64 * s + 16 * h, o1 = BF ? o0 + 16 : o0 + 32;
+    const uint4 x = lds_read_b128(at(o0)), y = lds_read_b128(at(o1));
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
   } else if (P::BITS == 6) {
@@ -270,14 +295,175 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int base, int t,
 
 // Operand registers of 64-K step S for the wave: A blocks t = 0..3 (rows wa + 32t + l%32),
 // B blocks (rows wb + ...).
-template <int CA, int CB, bool AMN, bool BMN, int S>
+template <int CA, int CB, bool AMN, bool BMN, bool BF, int S>
 __device__ __forceinline__ void read_frags(const uint8_t* ta, const uint8_t* tb, int wa, int wb, int lane,
                                            i32x8 (&fa)[4], i32x8 (&fb)[4]) {
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    fa[t] = read_frag<CA, AMN>(ta, wa, t, S, lane);
-    fb[t] = read_frag<CB, BMN>(tb, wb, t, S, lane);
+    fa[t] = read_frag<CA, AMN, BF>(ta, wa, t, S, lane);
+    fb[t] = read_frag<CB, BMN, BF>(tb, wb, t, S, lane);
   }
+}
+
+// ---- exact-products route: operand elements times their scale as bf16 ----------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x6_t __attribute__((ext_vector_type(6)));
+typedef unsigned u32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t bits2(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Elements 8j .. 8j + 7 of the lane's 32 (8-bit: dwords 2j, 2j + 1; 4-bit: dword j, low
+// nibble first) times 2^(code - 127), as 8 bf16 (the operand of bf16 MFMA j). `sbits` is
+// code << 23: the conversions take the scale from a float's exponent field.
+template <int C, int J>
+__device__ __forceinline__ uint4 cvt_part(const i32x8& v, uint32_t sbits) {
+  const float s = __uint_as_float(sbits);
+  if constexpr (C == 0) {
+    const uint32_t w0 = (uint32_t)v[2 * J], w1 = (uint32_t)v[2 * J + 1];
+    return make_uint4(bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true)));
+  } else if constexpr (C == 1) {
+    const uint32_t w0 = (uint32_t)v[2 * J], w1 = (uint32_t)v[2 * J + 1];
+    return make_uint4(bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, false)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, true)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, false)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, true)));
+  } else {
+    static_assert(C == 4, "6-bit operands convert all 32 elements at once (cvt_all6)");
+    const uint32_t w = (uint32_t)v[J];
+    return make_uint4(bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                      bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3)));
+  }
+}
+
+// All 32 elements of a 6-bit operand (dwords 0..5, element i at bits 6i..6i+5) times
+// 2^(code - 127) as bf16, o[j] = elements 8j .. 8j + 7. Written as inline assembly with an
+// early-clobber 16-register result: the compiler's builtin for these conversions let the
+// result overlap live registers.
+template <int C>
+__device__ __forceinline__ void cvt_all6(const i32x8& v, uint32_t sbits, uint4 (&o)[4]) {
+  const u32x6_t in = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3], (uint32_t)v[4], (uint32_t)v[5]};
+  const float s = __uint_as_float(sbits);
+  u32x16_t r;
+  if constexpr (C == 2) asm volatile("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(r) : "v"(in), "v"(s));
+  else asm volatile("v_cvt_scalef32_pk32_bf16_bf6 %0, %1, %2" : "=&v"(r) : "v"(in), "v"(s));
+#pragma unroll
+  for (int j = 0; j < 4; j++) o[j] = make_uint4(r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]);
+}
+
+// One operand's converted fragments for the bf16 MFMAs. 8- and 4-bit operands convert one
+// part j (elements 8j .. 8j + 7 of every block) at a time into buffer j & 1, ahead of its MFMAs,
+// and part 0 of the next step during part 3 of the current one (PREFETCH); 6-bit operands
+// convert whole blocks (all four parts) at the start of the step. The dwords a conversion
+// reads are pinned in place first (an empty asm that claims to rewrite them), so it issues
+// where it is written, between two MFMAs, rather than in a burst ahead of the step.
+template <int C>
+struct Conv {
+  static constexpr bool WHOLE = fmt_bits(C) == 6;
+  static constexpr bool PREFETCH = !WHOLE;
+  uint4 p[WHOLE ? 4 : 2][WHOLE ? 4 : 1][4];   // WHOLE: [t][0][j]; else [j & 1][0][t]
+  template <int J>
+  __device__ __forceinline__ void prepare(i32x8 (&f)[4], const uint32_t (&sb)[4], int t) {
+    if constexpr (WHOLE) {
+      if (J == 0) cvt_all6<C>(f[t], sb[t], p[t][0]);
+    } else {
+      constexpr int D = C == 4 ? J : 2 * J;
+      asm volatile("" : "+v"(f[t][D])::"memory");
+      if constexpr (C != 4) asm volatile("" : "+v"(f[t][D + 1])::"memory");
+      p[J & 1][0][t] = cvt_part<C, J>(f[t], sb[t]);
+      gemm::pin_frag(p[J & 1][0][t]);
+    }
+  }
+  template <int J>
+  __device__ __forceinline__ const uint4& get(int t) const {
+    if constexpr (WHOLE) return p[t][0][J];
+    else return p[J & 1][0][t];
+  }
+};
+
+// Scale bits (code << 23) of this lane's 32-K block in step S: byte 2S + h of the tile's word.
+template <int S>
+__device__ __forceinline__ void scale_bits(const uint32_t (&s)[4], int sh, uint32_t (&o)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) o[t] = ((s[t] >> (sh + 16 * S)) & 0xFFu) << 23;
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const uint4& b, const uint4& a, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a), c, 0, 0,
+                                                 0);
+}
+
+// Part 0 of a step for both operands (the prefetching formats), from raw fragments and the
+// scale words of the step's tile.
+template <int CA, int CB, int S>
+__device__ __forceinline__ void prepare_first(Conv<CA>& ca, Conv<CB>& cb, i32x8 (&fa)[4], i32x8 (&fb)[4],
+                                              const uint32_t (&sa)[4], const uint32_t (&sb)[4], int sh) {
+  uint32_t xa[4], xb[4];
+  scale_bits<S>(sa, sh, xa);
+  scale_bits<S>(sb, sh, xb);
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    if constexpr (Conv<CA>::PREFETCH) ca.template prepare<0>(fa, xa, t);
+    if constexpr (Conv<CB>::PREFETCH) cb.template prepare<0>(fb, xb, t);
+  }
+}
+
+// The 64 bf16 MFMAs of 64-K step S (MFMA j of each accumulator covers elements 8j..8j+7 of
+// the lanes' 32), j-major so that the conversions of part j + 1 go out between part j's
+// MFMAs. Part 0 of this step is ready in ca / cb (prefetching formats); with NEXT, part 0 of
+// the next step (raw fragments nfa / nfb, step index SN of the tile whose scale words are
+// nsa / nsb) is converted between part 3's MFMAs. nfa, nfb, nsa and nsb are read only then,
+// so side work of this step may still be filling them. side(i) (i = 0..15) runs after every
+// fourth MFMA, as mfma16 runs it after every one.
+template <int CA, int CB, int S, bool NEXT, int SN, typename Side>
+__device__ __forceinline__ void mfma64_bf(Conv<CA>& ca, Conv<CB>& cb, i32x8 (&fa)[4], i32x8 (&fb)[4],
+                                          const uint32_t (&sa)[4], const uint32_t (&sb)[4], i32x8 (&nfa)[4],
+                                          i32x8 (&nfb)[4], const uint32_t (&nsa)[4], const uint32_t (&nsb)[4], int sh,
+                                          f32x16 (&acc)[4][4], Side side) {
+  uint32_t xa[4], xb[4];
+  scale_bits<S>(sa, sh, xa);
+  scale_bits<S>(sb, sh, xb);
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    if constexpr (!Conv<CA>::PREFETCH) ca.template prepare<0>(fa, xa, t);
+    if constexpr (!Conv<CB>::PREFETCH) cb.template prepare<0>(fb, xb, t);
+  }
+  uint32_t nxa[4], nxb[4];
+  auto part = [&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    if constexpr (J == 3 && NEXT) {
+      scale_bits<SN>(nsa, sh, nxa);
+      scale_bits<SN>(nsb, sh, nxb);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int mt = i >> 2, nt = i & 3;
+      asm volatile("" : "+a"(acc[mt][nt])::"memory");
+      acc[mt][nt] = mfma_bf16(cb.template get<J>(nt), ca.template get<J>(mt), acc[mt][nt]);
+      asm volatile("" : "+a"(acc[mt][nt])::"memory");
+      if (i < 8) {
+        if constexpr (J < 3) {
+          if (i & 1) cb.template prepare<J + 1>(fb, xb, i >> 1);
+          else ca.template prepare<J + 1>(fa, xa, i >> 1);
+        } else if constexpr (NEXT) {
+          if (i & 1) {
+            if constexpr (Conv<CB>::PREFETCH) cb.template prepare<0>(nfb, nxb, i >> 1);
+          } else {
+            if constexpr (Conv<CA>::PREFETCH) ca.template prepare<0>(nfa, nxa, i >> 1);
+          }
+        }
+      }
+      if ((i & 3) == 3) side(4 * J + (i >> 2));
+    }
+  };
+  part(std::integral_constant<int, 0>{});
+  part(std::integral_constant<int, 1>{});
+  part(std::integral_constant<int, 2>{});
+  part(std::integral_constant<int, 3>{});
 }
 
 // The 16 MFMAs of 64-K step S (accumulator rows mt-major). The MFMA takes B first (its
@@ -300,7 +486,7 @@ __device__ __forceinline__ void mfma16(const i32x8 (&fa)[4], const i32x8 (&fb)[4
   }
 }
 
-template <int CA, int CB, bool AMN, bool BMN>
+template <int CA, int CB, bool AMN, bool BMN, bool BF>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m, int tiles_n) {
   typedef Op<CA, AMN> PA;
   typedef Op<CB, BMN> PB;
@@ -383,20 +569,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   static_assert(DPW <= 32, "at most two copies per MFMA slot of step 1");
   // Multiply the partial last K tile, held in stage st with its scale words (one per row,
   // A's then B's) at `scales`: step 1's fragment reads go out between step 0's MFMAs.
+  // Converted fragments of the exact-products route (unused on the other route).
+  Conv<CA> cva;
+  Conv<CB> cvb;
   auto multiply = [&](const uint8_t* st, const uint8_t* scales) {
     uint32_t sa[4], sb[4];
     i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
     read_scales(scales, wa, lane, sa);
     read_scales(scales + 1024, wb, lane, sb);
-    read_frags<CA, CB, AMN, BMN, 0>(st, st + PA::TILE, wa, wb, lane, fa0, fb0);
-    mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, [&](int i) {
+    read_frags<CA, CB, AMN, BMN, BF, 0>(st, st + PA::TILE, wa, wb, lane, fa0, fb0);
+    auto reads1 = [&](int i) {
       if (i < 8) {
-        if (i & 1) fb1[i >> 1] = read_frag<CB, BMN>(st + PA::TILE, wb, i >> 1, 1, lane);
-        else fa1[i >> 1] = read_frag<CA, AMN>(st, wa, i >> 1, 1, lane);
+        if (i & 1) fb1[i >> 1] = read_frag<CB, BMN, BF>(st + PA::TILE, wb, i >> 1, 1, lane);
+        else fa1[i >> 1] = read_frag<CA, AMN, BF>(st, wa, i >> 1, 1, lane);
       }
-    });
-    gemm::lds_barrier();
-    mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [](int) {});
+    };
+    if constexpr (BF) {
+      prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh);
+      mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, sa, sb, fa1, fb1, sa, sb, sh, acc, reads1);
+      gemm::lds_barrier();
+      mfma64_bf<CA, CB, 1, false, 0>(cva, cvb, fa1, fb1, sa, sb, fa0, fb0, sa, sb, sh, acc, [](int) {});
+    } else {
+      mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, reads1);
+      gemm::lds_barrier();
+      mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [](int) {});
+    }
   };
 
   // Whole K tiles; tile kt lives in stage kt % NST. One barrier per tile, at the start of
@@ -426,20 +623,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     gemm::stage_barrier<(NST - 1) * DD>();   // the scales and tile 0 have landed
     read_scales_ring(lds + L::RING, 0, 0, wa, lane, sa);
     read_scales_ring(lds + L::RING + 4096, 1, 0, wb, lane, sb);
-    read_frags<CA, CB, AMN, BMN, 0>(lds, lds + PA::TILE, wa, wb, lane, fa0, fb0);
+    read_frags<CA, CB, AMN, BMN, BF, 0>(lds, lds + PA::TILE, wa, wb, lane, fa0, fb0);
+    if constexpr (BF) prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh);
     int cur = 0;                             // kt % NST
     for (int kt = 0; kt < nfull; kt++) {
       const uint8_t* st = lds + cur * L::STAGE;
       const int nxt = cur + 1 == NST ? 0 : cur + 1;
       const uint8_t* nst = lds + nxt * L::STAGE;
       const int knext = min(kt + NST, nfull - 1);
-      mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, [&](int i) {
+      auto side0 = [&](int i) {
         if (i < 8) {
-          if (i & 1) fb1[i >> 1] = read_frag<CB, BMN>(st + PA::TILE, wb, i >> 1, 1, lane);
-          else fa1[i >> 1] = read_frag<CA, AMN>(st, wa, i >> 1, 1, lane);
+          if (i & 1) fb1[i >> 1] = read_frag<CB, BMN, BF>(st + PA::TILE, wb, i >> 1, 1, lane);
+          else fa1[i >> 1] = read_frag<CA, AMN, BF>(st, wa, i >> 1, 1, lane);
         }
-      });
-      mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [&](int i) {
+      };
+      auto side1 = [&](int i) {
         if (i == 0) {
           // only the data copies of the batches after tile kt + 1's (tiles kt + 2 ..
           // kt + NST - 1) may still fly: every scale quarter issued so far has landed
@@ -449,12 +647,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
           read_scales_ring(ring + 4096, 1, kt + 1, wb, lane, nb);
         }
         if (i < 8) {
-          if (i & 1) fb0[i >> 1] = read_frag<CB, BMN>(nst + PA::TILE, wb, i >> 1, 0, lane);
-          else fa0[i >> 1] = read_frag<CA, AMN>(nst, wa, i >> 1, 0, lane);
+          if (i & 1) fb0[i >> 1] = read_frag<CB, BMN, BF>(nst + PA::TILE, wb, i >> 1, 0, lane);
+          else fa0[i >> 1] = read_frag<CA, AMN, BF>(nst, wa, i >> 1, 0, lane);
         }
         if (i < DPW) batch_copy(kt, knext, cur, i);
         if (i + 16 < DPW) batch_copy(kt, knext, cur, i + 16);   // two 8-bit operands: 18 copies
-      });
+      };
+      if constexpr (BF) {
+        // step 0 converts step 1's first part from fa1 / fb1 (read by side0), step 1 the next
+        // tile's from fa0 / fb0 and its scale words na / nb (read by side1)
+        mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, sa, sb, fa1, fb1, sa, sb, sh, acc, side0);
+        mfma64_bf<CA, CB, 1, true, 0>(cva, cvb, fa1, fb1, sa, sb, fa0, fb0, na, nb, sh, acc, side1);
+      } else {
+        mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, side0);
+        mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, side1);
+      }
 #pragma unroll
       for (int t = 0; t < 4; t++) {
         sa[t] = na[t];
@@ -498,19 +705,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
                          a.ew_op, a.ew_scale, a.ew_bias);
 }
 
-// Launch of one (A format, B format, major orders) instance. Instances the tuned kernel of
-// k_gemm_mx.hip covers (K-major 8-bit x 8-bit, K-major E2M1 x E2M1) and 6-bit MN-major
-// operands are never compiled here: they report an invalid launch.
-template <int CA, int CB, bool AMN, bool BMN>
-hipError_t launch_pair(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t st) {
-  constexpr bool tuned = !AMN && !BMN && ((fmt_bits(CA) == 8 && fmt_bits(CB) == 8) || (CA == 4 && CB == 4));
+// Launch of one (A format, B format, major orders) instance on the route the call asks for:
+// exact products where the pairing needs them (wide_products), or the scaled MFMA when the
+// call takes its accumulation window (a.mx_window, K-major operands only). Instances the tuned
+// kernels of k_gemm_mx.hip cover (K-major E2M1 x E2M1, and K-major 8-bit x 8-bit on the
+// scaled MFMA) and 6-bit MN-major operands are never compiled here: they report an invalid
+// launch.
+template <int CA, int CB, bool AMN, bool BMN, bool BF>
+hipError_t launch_route(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t st) {
+  constexpr bool tuned = !AMN && !BMN && ((CA == 4 && CB == 4) || (!BF && fmt_bits(CA) == 8 && fmt_bits(CB) == 8));
   constexpr bool fp6_mn = (AMN && fmt_bits(CA) == 6) || (BMN && fmt_bits(CB) == 6);
   if constexpr (tuned || fp6_mn) {
     return hipErrorInvalidValue;
   } else {
-    hipLaunchKernelGGL((k_gemm_mx_any<CA, CB, AMN, BMN>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m,
+    hipLaunchKernelGGL((k_gemm_mx_any<CA, CB, AMN, BMN, BF>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_m,
                        tiles_n);
     return hipGetLastError();
+  }
+}
+
+template <int CA, int CB, bool AMN, bool BMN>
+hipError_t launch_pair(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t st) {
+  constexpr bool wide = wide_products(CA, CB);
+  if constexpr (!wide || AMN || BMN) {
+    // one route: the scaled MFMA is exact for these formats, or the operands are MN-major
+    // (the window route takes K-major operands only)
+    if (a.mx_window && (AMN || BMN)) return hipErrorInvalidValue;
+    return launch_route<CA, CB, AMN, BMN, wide>(a, tiles_m, tiles_n, st);
+  } else {
+    if (a.mx_window) return launch_route<CA, CB, AMN, BMN, false>(a, tiles_m, tiles_n, st);
+    return launch_route<CA, CB, AMN, BMN, true>(a, tiles_m, tiles_n, st);
   }
 }
 

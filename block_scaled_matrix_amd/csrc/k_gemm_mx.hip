@@ -441,6 +441,9 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
   if (!a.a_kmajor) return launch_gemm_mx_mn_a(a, st);
   if (!a.b_kmajor) return launch_gemm_mx_mn_b(a, st);
   if (!(byte_a && byte_b) && !(a.dtype == BSM_E2M1 && a.dtype_b == BSM_E2M1)) return launch_gemm_mx_any(a, st);
+  // 8-bit pairs sum exactly only through the general kernel's bf16 route; this kernel's
+  // scaled fp8 MFMA serves calls that take its accumulation window
+  if (byte_a && byte_b && !a.mx_window) return launch_gemm_mx_any(a, st);
   const int64_t tm64 = (a.M + BM - 1) / BM, tn64 = (a.N + BN - 1) / BN;
   if (tm64 * tn64 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = (int)tm64, tiles_n = (int)tn64;

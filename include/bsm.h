@@ -223,12 +223,17 @@ int bsm_gemm(int64_t M, int64_t N, int64_t K, int32_t ab,
  *   K a multiple of 32; ld_sfa >= K/32, ld_sfb >= K/32, both multiples of 4, SFA and
  *   SFB 4-byte aligned (scale rows are read as 32-bit words); every buffer spans whole
  *   rows (rows * ld); D as for bsm_gemm. A, B, SFA, SFB must not overlap D.
- * Precision: products of decoded values are exact and blocks are accumulated in
- * float32. The gfx950 scaled MFMA sums the 32 products of one scale block on a fixed
- * grid of 2^-13 times the block's largest |product| (products below it are truncated),
- * so each block may lose up to sum_k min(|p_k|, grid) beyond float32 rounding; blocks
- * whose products span fewer than 13 binades (E2M1 x E2M1, E2M3 x E2M3, E2M1 x E2M3) sum
- * exactly. */
+ * Precision: every product of decoded, scaled values is formed exactly and the sums
+ * keep |D - ref| within 1e-5 * sum_k |A(m,k) B(n,k)| (plus half an ulp of the float32
+ * result): pairings whose products are all multiples of 2^-13 times the largest product
+ * the two formats can form (E2M1 x E2M1, E2M3 x E2M3, E2M1 x E2M3, E2M1 x E3M2, in either
+ * order) run the scaled f8f6f4 MFMA, whose block sums are then exact; every other pairing
+ * (any 8-bit operand, E3M2 with E3M2 or E2M3) converts each element times its scale to
+ * bf16 in registers (exact) and sums the products with the bf16 MFMA, which keeps every
+ * product bit down to about 2^-24 of the largest term of each 16-product instruction,
+ * at half the 8-bit MFMA rate. Scaled values must lie inside bf16's range on that route
+ * (2^-133 up to about 3.4e38, i.e. scale codes that keep |element| * 2^(code - 127)
+ * there); beyond it they round to bf16 subnormals, zero or infinity. */
 int bsm_gemm_block_scale(int64_t M, int64_t N, int64_t K,
                          int32_t a_fmt, const void* A, int64_t lda, const uint8_t* SFA, int64_t ld_sfa,
                          int32_t b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
@@ -294,6 +299,22 @@ int bsm_gemm_block_scale_major(int64_t M, int64_t N, int64_t K,
                                const uint8_t* SFB, int64_t ld_sfb,
                                float* D, int64_t ldd, int neg_a, int neg_b, int accum,
                                const bsm_ewise* ew, void* stream);
+
+/* bsm_gemm_block_scale_ewise with every pairing on gfx950's scaled f8f6f4 MFMA: the
+ * fast-accumulation form, at the full 8-bit (and 4/6-bit) MFMA rate, for callers that
+ * accept its block sums. Same arguments, layouts and errors (K-major operands only; ew may
+ * be NULL for no epilogue). Precision: products are exact, but the instruction sums the 32
+ * products of one scale block on a fixed grid of 2^-13 times the block's largest |product|
+ * (measured on the device: a product 2^-13 below the block maximum is kept, one 2^-14
+ * below is dropped), so each block may lose up to sum_k min(|p_k|, grid) beyond float32
+ * rounding; the block sums are then accumulated in float32. For pairings whose products
+ * all lie on that grid (see bsm_gemm_block_scale) the result equals bsm_gemm_block_scale's
+ * bound; for wide-range 8-bit operands it does not meet 1e-5 * sum|ab|. */
+int bsm_gemm_block_scale_fastacc(int64_t M, int64_t N, int64_t K,
+                                 int32_t a_fmt, const void* A, int64_t lda, const uint8_t* SFA, int64_t ld_sfa,
+                                 int32_t b_fmt, const void* B, int64_t ldb, const uint8_t* SFB, int64_t ld_sfb,
+                                 float* D, int64_t ldd, int neg_a, int neg_b, int accum,
+                                 const bsm_ewise* ew, void* stream);
 
 /* Element-wise scalar add on float32 ([TOE] "A Load, Compute, and Store Example"
  * adds one to a (2,32,3,4) tile; [TP] "Scalar compositions"): dst[i] = src[i] + s,

@@ -192,6 +192,16 @@ def test_gemm_contract_violations(L):
     # an MN-major A spans K = 128 rows of lda = 64 bytes (8 KiB, where M rows of it would span 4 KiB)
     expect("BSM_E_ALIAS", sm, 64, 64, 128, "e4m3", A, 64, "m", SA, 4, "e4m3", B, 128, "k", SB, 4, A + 4096, 64)
     bsm.bsm_gemm_block_scale_major(64, 0, 64, "e4m3", 0, 0, "m", 0, 0, "e4m3", 0, 0, "n", 0, 0, 0, 0, stream=0)
+    # the fast-accumulation call keeps every rule of the plain call; ew may be NULL
+    sf = lambda *a, ew=None: bsm.bsm_gemm_block_scale_fastacc(*a, ew=ew, stream=0)
+    expect("BSM_E_SHAPE", sf, 64, 64, 48, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_DTYPE", sf, 64, 64, 64, "e4m3", A, 64, SA, 4, "bf16", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ALIGN", sf, 64, 64, 64, "e4m3", A, 72, SA, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ALIAS", sf, 64, 64, 64, "e4m3", A, 64, D + 64, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_NULL", sf, 64, 64, 64, "e4m3", A, 64, 0, 4, "e4m3", B, 64, SB, 4, D, 64)
+    expect("BSM_E_ARG", lambda: sf(64, 64, 64, "e4m3", A, 64, SA, 4, "e4m3", B, 64, SB, 4, D, 64,
+                                   ew=bsm.ewise_desc(9)))
+    bsm.bsm_gemm_block_scale_fastacc(0, 64, 64, "e4m3", 0, 0, 0, 0, "e4m3", 0, 0, 0, 0, 0, 0, stream=0)
     a = lambda *x: bsm.bsm_tile_add_scalar_f32(*x, stream=0)
     expect("BSM_E_SHAPE", a, A, B, -1, 1.0)
     expect("BSM_E_ALIGN", a, A + 4, B, 8, 1.0)

@@ -2,8 +2,10 @@
 
 Tolerances (the stated bound of the method, written out):
   dense:        |D - ref| <= 2e-3 * sum_k |a_mk b_nk|  (+ half an ulp of the float32 result)
-  block scaled: |D - ref| <= 1e-5 * sum_k |a_mk b_nk|  (+ half an ulp)
-Inputs whose every partial sum is exact in float32 must match bit for bit.
+  block scaled: |D - ref| <= 1e-5 * sum_k |a_mk b_nk|  (+ half an ulp; mx_check.check_strict)
+Inputs whose every partial sum is exact in float32 must match bit for bit. Only the
+fast-accumulation call (bsm_gemm_block_scale_fastacc) is checked with the scaled MFMA's
+block-window allowance (mx_check.check_window).
 """
 import numpy as np
 import pytest
@@ -12,47 +14,11 @@ import torch
 import block_scaled_matrix_amd as bsm
 from block_scaled_matrix_amd import workloads as W
 from gpu_util import dev, dev_f32, host, say
+from mx_check import TOL_MX, check_strict, check_window, note, pad_cols, pad_scales, pair_case
 
 pytestmark = pytest.mark.gpu
 
-TOL_DENSE, TOL_MX = 2e-3, 1e-5
-WINDOW_BITS = 13
-
-
-def fp8_window_slack(O, g, pm, pn):
-    """Extra error allowance for 8-bit operands (E4M3, E5M2; measured with E4M3, applied to every
-    8-bit pairing since they go through the same instruction): gfx950's fp8 MFMA sums the 32 products of
-    each scale block on a grid of 2^(E-13), E the exponent of the block's largest
-    |product| (measured on the device: a product 2^-13 below the block maximum is kept,
-    2^-14 below is dropped; sums across blocks and with the accumulator are float32).
-    Each product can lose at most min(|p|, grid). Returns that bound per point."""
-    K = g["K"]
-    af, bf = g.get("fmt", "e4m3"), g.get("b_fmt", g.get("fmt", "e4m3"))
-    A = O.decode(af, g["A"]).reshape(-1, g["lda"])[:, :K] * np.repeat(np.exp2(g["SFA"][:, :K // 32] - 127.0), 32, 1)
-    B = O.decode(bf, g["B"]).reshape(-1, g["ldb"])[:, :K] * np.repeat(np.exp2(g["SFB"][:, :K // 32] - 127.0), 32, 1)
-    out = np.empty(len(pm))
-    for c in range(0, len(pm), 256):
-        p = np.abs(A[pm[c:c + 256]] * B[pn[c:c + 256]]).reshape(-1, K // 32, 32)
-        mx = p.max(axis=2, keepdims=True)
-        grid = np.where(mx > 0, np.exp2(np.floor(np.log2(np.where(mx > 0, mx, 1.0))) - WINDOW_BITS), 0.0)
-        out[c:c + 256] = np.minimum(p, grid).sum(axis=(1, 2))
-    return out
-
-
-def check_mx(O, fmt, g, D, ref, bound, pm=None, pn=None):
-    """1e-5 * sum|ab| (+ half an ulp), plus for E4M3 the fp8 dot-product window slack."""
-    if pm is None:
-        M, N = ref.shape
-        pm, pn = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
-        d, r, b = D[:M, :N].reshape(-1), ref.reshape(-1), bound.reshape(-1)
-    else:
-        d, r, b = D[pm, pn], ref, bound
-    tol = TOL_MX * b + np.ldexp(np.abs(r), -24)
-    if fmt in ("e4m3", "e5m2"):
-        tol = tol + fp8_window_slack(O, g, pm, pn)
-    err = np.abs(d.astype(np.float64) - r)
-    bad = ~(err <= tol) & ~(np.isnan(d) & np.isnan(r))
-    return int(bad.sum()), float(np.max(err / np.maximum(b, 1e-300)))
+TOL_DENSE = 2e-3
 
 
 def run_dense(M, N, K, dt, A, lda, amaj, B, ldb, bmaj, D0=None, neg_a=0, neg_b=0, accum=0, ldd=None):
@@ -63,12 +29,6 @@ def run_dense(M, N, K, dt, A, lda, amaj, B, ldb, bmaj, D0=None, neg_a=0, neg_b=0
     dD = dev_f32(d)
     bsm.bsm_gemm(M, N, K, dt, dev(A), lda, amaj, dev(B), ldb, bmaj, dD, ldd, neg_a, neg_b, accum)
     return dD.cpu().numpy()
-
-
-def pad_cols(a, ld):
-    out = np.zeros((a.shape[0], ld), a.dtype)
-    out[:, :a.shape[1]] = a
-    return out
 
 
 def dense_case(rng, M, N, K, dt, amaj, bmaj, exact=False):
@@ -241,13 +201,6 @@ def run_mx(M, N, K, fmt, g, D0=None, neg_a=0, neg_b=0, accum=0, b_fmt=None):
     return dD.cpu().numpy()
 
 
-def pad_scales(sf, ld):
-    """Scale rows padded to ld bytes with NaN codes (0xFF): the kernel must never use them."""
-    out = np.full((sf.shape[0], ld), 255, np.uint8)
-    out[:, :sf.shape[1]] = sf
-    return out
-
-
 def mx_case(fmt, seed, M, N, K, exp_range=4, ld_pad=0, b_fmt=None):
     if fmt == "e2m1":
         g = W.mxfp4(seed=seed, M=M, N=N, K=K, exp_range=exp_range)
@@ -280,11 +233,8 @@ def test_block_scale_vs_oracle(O, fmt):
         D = run_mx(M, N, K, fmt, g, d0 if accum else None, neg_a, neg_b, accum)
         ref, bound = O.gemm_block_scale(M, N, K, fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], fmt, g["B"], g["ldb"],
                                         g["SFB"], g["ld_sfb"], d0, N, neg_a, neg_b, accum)
-        g["K"] = K
-        nb, worst = check_mx(O, fmt, g, D, ref, bound)
+        nb, worst = check_strict(O, D, ref, bound, name=f"{fmt} x {fmt} shapes")
         assert nb == 0, (M, N, K, worst)
-        if fmt == "e2m1":   # E2M1 products span < 2^13 per block: the plain bound holds
-            assert O.check_gemm(D, ref, bound, TOL_MX)[0] == 0
         assert np.isnan(D[:, N:]).all()
 
 
@@ -293,7 +243,7 @@ def test_block_scale_vs_oracle(O, fmt):
 LARGE_SHAPE = (8448, 2304, 2112)
 
 
-@pytest.mark.parametrize("fmt,neg_a,accum", [("e4m3", 0, 1), ("e2m1", 1, 0), ("e2m1", 0, 1)])
+@pytest.mark.parametrize("fmt,neg_a,accum", [("e4m3", 0, 1), ("e2m1", 1, 0), ("e2m1", 0, 1), ("e5m2", 1, 1)])
 def test_block_scale_large_grid_vs_oracle(O, fmt, neg_a, accum):
     M, N, K = LARGE_SHAPE
     g = mx_case(fmt, 77, M, N, K)
@@ -302,14 +252,8 @@ def test_block_scale_large_grid_vs_oracle(O, fmt, neg_a, accum):
     D = run_mx(M, N, K, fmt, g, d0 if accum else None, neg_a, 0, accum)
     ref, bound = O.gemm_block_scale(M, N, K, fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], fmt, g["B"], g["ldb"],
                                     g["SFB"], g["ld_sfb"], d0, N, neg_a, 0, accum, 256, 512)
-    g["K"] = K
-    if fmt == "e2m1":
-        assert O.check_gemm(D[256:512, :N], ref, bound, TOL_MX)[0] == 0
-    else:   # the fp8 window slack is costly to evaluate: 8192 points of those rows
-        rng = np.random.default_rng(6)
-        pm, pn = 256 + rng.integers(0, 256, 8192), rng.integers(0, N, 8192)
-        nb, worst = check_mx(O, fmt, g, D, ref[pm - 256, pn], bound[pm - 256, pn], pm, pn)
-        assert nb == 0, worst
+    nb, worst = check_strict(O, D[256:512], ref, bound, name=f"{fmt} x {fmt} 8448x2304x2112 rows 256..511")
+    assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()
 
 
@@ -324,8 +268,7 @@ def test_block_scale_e5m2_vs_oracle(O, a_fmt, b_fmt):
         D = run_mx(M, N, K, a_fmt, g, d0 if accum else None, neg_a, neg_b, accum, b_fmt=b_fmt)
         ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
                                         g["ldb"], g["SFB"], g["ld_sfb"], d0, N, neg_a, neg_b, accum)
-        g["K"] = K
-        nb, worst = check_mx(O, a_fmt, g, D, ref, bound)
+        nb, worst = check_strict(O, D, ref, bound, name=f"{a_fmt} x {b_fmt} shapes")
         assert nb == 0, (M, N, K, worst)
         assert np.isnan(D[:, N:]).all()
 
@@ -376,6 +319,9 @@ def test_block_scale_nan_scale_poisons_row(O, fmt):
 
 
 def test_mxfp8_full_size_sampled(O):
+    """The MXFP8 workload (8192 x 8192 x 16384, E4M3 codes uniform over the finite values,
+    scales 127 +- 4): 1000 sampled outputs within the stated bound, with no allowance for the
+    scaled fp8 MFMA's block window (the call sums exact products with the bf16 MFMA)."""
     g = W.mxfp8()
     M, N, K = g["M"], g["N"], g["K"]
     say("mxfp8 full", M, N, K)
@@ -383,7 +329,7 @@ def test_mxfp8_full_size_sampled(O):
     pm, pn = W.sample_points(M, N, 1000)
     ref, bound = O.gemm_block_scale_points(M, N, K, "e4m3", g["A"], K, g["SFA"], K // 32, "e4m3", g["B"], K,
                                            g["SFB"], K // 32, None, 0, 0, 0, 0, pm, pn)
-    nb, worst = check_mx(O, "e4m3", g, D, ref, bound, pm, pn)
+    nb, worst = check_strict(O, D, ref, bound, pm, pn, name="mxfp8 8192x8192x16384 (1000 points)")
     assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()
 
@@ -396,27 +342,116 @@ def test_mxfp4_full_size_sampled(O):
     pm, pn = W.sample_points(M, N, 1000)
     ref, bound = O.gemm_block_scale_points(M, N, K, "e2m1", g["A"], K, g["SFA"], K // 32, "e2m1", g["B"], K,
                                            g["SFB"], K // 32, None, 0, 1, 0, 0, pm, pn)
-    nb, first, worst = O.check_gemm(D[pm, pn].reshape(1, -1), ref.reshape(1, -1), bound.reshape(1, -1), TOL_MX)
-    assert nb == 0, (first, worst)
+    nb, worst = check_strict(O, D, ref, bound, pm, pn, name="mxfp4 16384x8192x8192 (1000 points)")
+    assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()
 
 
+def _window_pair(O, run, small_a, small_b):
+    """One 32-element block with products 256 * 256 = 2^16 and small_a * small_b (E4M3 codes)."""
+    A = np.zeros((1, 32), np.uint8)
+    B = np.zeros((1, 32), np.uint8)
+    A[0, 0] = B[0, 0] = 0x78          # 256 * 256 = 2^16
+    A[0, 1], B[0, 1] = small_a, small_b
+    sf = np.full((1, 4), 127, np.uint8)
+    g = {"A": A, "B": B, "SFA": sf, "SFB": sf, "lda": 32, "ldb": 32, "ld_sfa": 4, "ld_sfb": 4}
+    D = run(1, 1, 32, "e4m3", g)
+    ref, _ = O.gemm_block_scale(1, 1, 32, "e4m3", A, 32, sf, 4, "e4m3", B, 32, sf, 4)
+    return float(D[0, 0]), float(ref[0, 0])
+
+
 def test_e4m3_block_window_characterization(O):
-    """The device fact the E4M3 tolerance rests on: inside one 32-element scale block the
-    scaled fp8 MFMA keeps a product 2^-13 below the block's largest product and drops one
-    2^-14 below (2^16 + 2^3 is exact, 2^16 + 2^2 returns 2^16)."""
-    def run_pair(small_a, small_b):
-        A = np.zeros((1, 32), np.uint8)
-        B = np.zeros((1, 32), np.uint8)
-        A[0, 0] = B[0, 0] = 0x78          # 256 * 256 = 2^16
-        A[0, 1], B[0, 1] = small_a, small_b
-        sf = np.full((1, 4), 127, np.uint8)
-        g = {"A": A, "B": B, "SFA": sf, "SFB": sf, "lda": 32, "ldb": 32, "ld_sfa": 4, "ld_sfb": 4}
-        D = run_mx(1, 1, 32, "e4m3", g)
-        ref, _ = O.gemm_block_scale(1, 1, 32, "e4m3", A, 32, sf, 4, "e4m3", B, 32, sf, 4)
-        return float(D[0, 0]), float(ref[0, 0])
+    """The device fact behind the two routes: inside one 32-element scale block the scaled fp8
+    MFMA (the fast-accumulation call) keeps a product 2^-13 below the block's largest product
+    and drops one 2^-14 below (2^16 + 2^3 is exact, 2^16 + 2^2 returns 2^16); the plain call
+    keeps products down to 2^-24 of the largest (2^16 + 2^2 and 2^16 + 2^-2 exact), smaller
+    ones costing at most that much."""
     say("e4m3 window")
-    got, ref = run_pair(0x48, 0x40)       # 4 * 2 = 2^3 -> kept
+    got, ref = _window_pair(O, run_mx_fast, 0x48, 0x40)     # 4 * 2 = 2^3 -> kept
     assert got == ref == 65536.0 + 8.0
-    got, ref = run_pair(0x40, 0x40)       # 2 * 2 = 2^2 -> dropped
+    got, ref = _window_pair(O, run_mx_fast, 0x40, 0x40)     # 2 * 2 = 2^2 -> dropped
     assert ref == 65536.0 + 4.0 and got == 65536.0
+    for small in (0x40, 0x30):                               # 2^2, 2^-2 (0.5^2): kept exactly
+        got, ref = _window_pair(O, run_mx, small, small)
+        assert got == ref, (small, got, ref)
+    for small in (0x08, 0x01):                               # 2^-12, 2^-18: below the bf16 MFMA's
+        got, ref = _window_pair(O, run_mx, small, small)     # 2^-24 window, within the bound
+        assert abs(got - ref) <= np.ldexp(65536.0, -24), (small, got, ref)
+
+
+def test_bf16_mfma_accumulation_characterization(O):
+    """The device fact the exact-products route rests on, through the dense bf16 GEMM: one
+    32x32x16 bf16 MFMA keeps product bits down to 2^-24 of its largest term (1 + 2^-20 and
+    1 + 2^-12 + ... + 2^-16 are exact) and drops terms far below it (2^30 + 1 - 2^30 gives 0);
+    products below the window therefore cost at most about 2^-24 of the instruction's
+    largest term each."""
+    def one(vals):
+        a = np.zeros((1, 16), np.float32)
+        a[0, :len(vals)] = vals
+        A = W.to_half_bits(a, "bf16")
+        B = W.to_half_bits(np.ones((1, 16), np.float32), "bf16")
+        return float(run_dense(1, 1, 16, "bf16", A, 16, "k", B, 16, "k")[0, 0])
+    say("bf16 mfma window")
+    assert one([1.0, 2.0 ** -20]) == 1.0 + 2.0 ** -20
+    assert one([1.0, 2.0 ** -12, 2.0 ** -13, 2.0 ** -14, 2.0 ** -15, 2.0 ** -16]) == \
+        1.0 + 2.0 ** -12 + 2.0 ** -13 + 2.0 ** -14 + 2.0 ** -15 + 2.0 ** -16
+    assert one([2.0 ** 16, 2.0 ** 2]) == 65540.0
+    assert one([2.0 ** 30, 1.0, -2.0 ** 30]) == 0.0
+
+
+def run_mx_fast(M, N, K, fmt, g, D0=None, neg_a=0, neg_b=0, accum=0, b_fmt=None, ew=None):
+    ldd = (N + 3) // 4 * 4
+    d = np.full((M, ldd), np.nan, np.float32)
+    if D0 is not None:
+        d[:, :N] = D0
+    dD = dev_f32(d)
+    bsm.bsm_gemm_block_scale_fastacc(M, N, K, fmt, dev(g["A"]), g["lda"], dev(g["SFA"]), g["ld_sfa"], b_fmt or fmt,
+                                     dev(g["B"]), g["ldb"], dev(g["SFB"]), g["ld_sfb"], dD, ldd, neg_a, neg_b, accum,
+                                     ew=ew)
+    return dD.cpu().numpy()
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e2m1"), ("e3m2", "e3m2")])
+def test_fastacc_within_window(O, a_fmt, b_fmt):
+    """The fast-accumulation call on pairings with wide product ranges: within the stated
+    bound plus the scaled MFMA's block-window allowance, over ragged shapes, negation and
+    accumulation."""
+    for i, (M, N, K) in enumerate([(9, 17, 64), (300, 260, 288), (130, 513, 512), (256, 256, 1056)]):
+        neg_a, accum = i & 1, (i >> 1) & 1
+        g = pair_case(a_fmt, b_fmt, 90 + i, M, N, K, ld_pad=64 if i == 2 else 0)
+        d0 = np.random.default_rng(i).standard_normal((M, N)).astype(np.float32)
+        say("mx fastacc", a_fmt, b_fmt, M, N, K, neg_a, accum)
+        D = run_mx_fast(M, N, K, a_fmt, g, d0 if accum else None, neg_a, 0, accum, b_fmt=b_fmt)
+        ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
+                                        g["ldb"], g["SFB"], g["ld_sfb"], d0, N, neg_a, 0, accum)
+        nb, worst = check_window(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        assert nb == 0, (M, N, K, worst)
+        assert np.isnan(D[:, N:]).all()
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e2m1", "e2m1"), ("e2m3", "e2m3"), ("e2m1", "e3m2")])
+def test_fastacc_equals_plain_call_for_exact_pairs(O, a_fmt, b_fmt):
+    """For pairings whose products lie on the scaled MFMA's grid both calls run the same kernel:
+    bit-identical results."""
+    M, N, K = 300, 260, 1056
+    g = pair_case(a_fmt, b_fmt, 95, M, N, K)
+    say("mx fastacc vs plain", a_fmt, b_fmt)
+    D1 = run_mx_fast(M, N, K, a_fmt, g, b_fmt=b_fmt)
+    D2 = run_mx(M, N, K, a_fmt, g, b_fmt=b_fmt)
+    assert np.array_equal(D1.view(np.uint32), D2.view(np.uint32))
+
+
+def test_mxfp8_fastacc_full_size_margin(O):
+    """The MXFP8 workload through the fast-accumulation call: within the window allowance; the
+    measured margin against the stated bound is recorded (it exceeds 1e-5 on this data, which
+    is why the plain call takes the exact-products route)."""
+    g = W.mxfp8()
+    M, N, K = g["M"], g["N"], g["K"]
+    say("mxfp8 fastacc full", M, N, K)
+    D = run_mx_fast(M, N, K, "e4m3", g)
+    pm, pn = W.sample_points(M, N, 300)
+    ref, bound = O.gemm_block_scale_points(M, N, K, "e4m3", g["A"], K, g["SFA"], K // 32, "e4m3", g["B"], K,
+                                           g["SFB"], K // 32, None, 0, 0, 0, 0, pm, pn)
+    nb, worst = check_window(O, g, "e4m3", "e4m3", K, D, ref, bound, pm, pn)
+    note("mxfp8 8192x8192x16384 fast accumulation (300 points)", worst)
+    assert nb == 0, worst

@@ -1,10 +1,10 @@
 """GPU parity: block-scaled GEMM over the other pairings of the f8f6f4 formats (the 6-bit
 E2M3 / E3M2 and operands of different widths, run by the general kernel) against the oracle.
 
-Tolerance as for the 8-bit pairs: 1e-5 * sum|ab| + half an ulp of the float32 result, plus
-the accumulation-window slack of the scaled MFMA (each 32-K block sums on a grid of 2^-13
-times its largest |product|; a format pair whose products span fewer than 13 binades sums
-exactly, which the exact-sum cases check bit for bit).
+Tolerance: the stated bound, 1e-5 * sum|ab| + half an ulp of the float32 result
+(mx_check.check_strict), for every pairing. Pairings whose products all lie on the scaled
+MFMA's grid sum exactly there (checked bit for bit by the exact-sum cases); the others run the
+exact-products route.
 """
 import numpy as np
 import pytest
@@ -13,29 +13,14 @@ import torch
 import block_scaled_matrix_amd as bsm
 from block_scaled_matrix_amd import workloads as W
 from gpu_util import dev, dev_f32, say
-from test_gpu_gemm import TOL_MX, WINDOW_BITS, pad_cols, pad_scales
+from mx_check import TOL_MX, check_strict, pair_case
 
 pytestmark = pytest.mark.gpu
 
 BITS = W.BITS
 PAIRS = [("e4m3", "e2m1"), ("e2m1", "e4m3"), ("e5m2", "e2m1"), ("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"),
          ("e2m3", "e4m3"), ("e3m2", "e2m1"), ("e2m1", "e2m3"), ("e5m2", "e3m2")]
-
-
-def case(a_fmt, b_fmt, seed, M, N, K, exp_range=4, ld_pad=0):
-    """W.mx_pair operands in rows of ld = K + ld_pad elements rounded up to a multiple of 64
-    (16-byte aligned rows for every width, 6-bit ones included); scale rows padded to a
-    multiple of 4 bytes with NaN codes the kernel must never use."""
-    g = W.mx_pair(seed, M, N, K, a_fmt, b_fmt, exp_range)
-    ld = (K + ld_pad + 63) // 64 * 64
-    if ld != K:
-        g["A"] = pad_cols(g["A"], ld * BITS[a_fmt] // 8)
-        g["B"] = pad_cols(g["B"], ld * BITS[b_fmt] // 8)
-    g["lda"] = g["ldb"] = ld
-    ld_sf = (K // 32 + 3) // 4 * 4 + (4 if ld_pad else 0)
-    g["SFA"], g["SFB"] = pad_scales(g["SFA"], ld_sf), pad_scales(g["SFB"], ld_sf)
-    g["ld_sfa"] = g["ld_sfb"] = ld_sf
-    return g
+case = pair_case
 
 
 def run(g, M, N, K, a_fmt, b_fmt, D0=None, neg_a=0, neg_b=0, accum=0, ew=None):
@@ -53,32 +38,8 @@ def run(g, M, N, K, a_fmt, b_fmt, D0=None, neg_a=0, neg_b=0, accum=0, ew=None):
     return dD.cpu().numpy()
 
 
-def window_slack(O, g, a_fmt, b_fmt, K, pm, pn):
-    """Per point: sum over the 32-K blocks of sum_k min(|p_k|, 2^(E - 13)), E the exponent of
-    the block's largest |product| (the scaled MFMA's accumulation grid)."""
-    A = O.decode(a_fmt, g["A"]).reshape(-1, g["lda"])[:, :K] * np.repeat(np.exp2(g["SFA"][:, :K // 32] - 127.0), 32, 1)
-    B = O.decode(b_fmt, g["B"]).reshape(-1, g["ldb"])[:, :K] * np.repeat(np.exp2(g["SFB"][:, :K // 32] - 127.0), 32, 1)
-    out = np.empty(len(pm))
-    for c in range(0, len(pm), 256):
-        p = np.abs(A[pm[c:c + 256]] * B[pn[c:c + 256]]).reshape(-1, K // 32, 32)
-        mx = p.max(axis=2, keepdims=True)
-        grid = np.where(mx > 0, np.exp2(np.floor(np.log2(np.where(mx > 0, mx, 1.0))) - WINDOW_BITS), 0.0)
-        out[c:c + 256] = np.minimum(p, grid).sum(axis=(1, 2))
-    return out
-
-
-def check(O, g, a_fmt, b_fmt, K, D, ref, bound, pm=None, pn=None):
-    if pm is None:
-        M, N = ref.shape
-        pm, pn = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
-        r, b = ref.reshape(-1), bound.reshape(-1)
-    else:
-        r, b = ref, bound
-    d = D[pm, pn].astype(np.float64)
-    tol = TOL_MX * b + np.ldexp(np.abs(r), -24) + window_slack(O, g, a_fmt, b_fmt, K, pm, pn)
-    err = np.abs(d - r)
-    bad = ~(err <= tol) & ~(np.isnan(d) & np.isnan(r))
-    return int(bad.sum()), float(np.max(err / np.maximum(b, 1e-300)))
+def check(O, g, a_fmt, b_fmt, K, D, ref, bound, pm=None, pn=None, name=None):
+    return check_strict(O, D, ref, bound, pm, pn, name=name)
 
 
 SHAPES = [(1, 1, 32), (9, 17, 64), (300, 260, 288), (130, 513, 512), (256, 256, 128), (64, 96, 1056), (33, 40, 96)]
@@ -94,16 +55,17 @@ def test_mx_any_pair_vs_oracle(O, a_fmt, b_fmt):
         D = run(g, M, N, K, a_fmt, b_fmt, d0 if accum else None, neg_a, neg_b, accum)
         ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
                                         g["ldb"], g["SFB"], g["ld_sfb"], d0, N, neg_a, neg_b, accum)
-        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, name=f"{a_fmt} x {b_fmt} shapes")
         assert nb == 0, (M, N, K, worst)
         assert np.isnan(D[:, N:]).all()
 
 
-@pytest.mark.parametrize("a_fmt,b_fmt", [("e2m3", "e2m3"), ("e2m1", "e2m3"), ("e2m3", "e2m1")])
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e2m3", "e2m3"), ("e2m1", "e2m3"), ("e2m3", "e2m1"), ("e2m1", "e3m2")])
 def test_mx_any_exact_pairs_bit_exact(O, a_fmt, b_fmt):
-    """Products of these pairs span fewer than 13 binades per block and unit-range scales
-    keep every partial sum exact in float32: the result must equal the oracle's bit for bit."""
-    for M, N, K in [(256, 256, 128), (300, 200, 352)]:
+    """Products of these pairs all lie on the scaled MFMA's grid and unit-range scales keep
+    every partial sum exact in float32: the result must equal the oracle's bit for bit, also
+    over K of several scale-ring groups (K = 1408: eleven K tiles, three groups)."""
+    for M, N, K in [(256, 256, 128), (300, 200, 352), (264, 136, 1408)]:
         g = case(a_fmt, b_fmt, 5, M, N, K, exp_range=1)
         say("mx any exact", a_fmt, b_fmt, M, N, K)
         D = run(g, M, N, K, a_fmt, b_fmt)
@@ -130,8 +92,7 @@ def test_mx_any_with_epilogue(O):
     D = run(g, M, N, K, "e4m3", "e2m1", ew=bsm.ewise_desc("silu_affine", 2.0, 1.0))
     ref, bound = O.gemm_block_scale(M, N, K, "e4m3", g["A"], g["lda"], g["SFA"], g["ld_sfa"], "e2m1", g["B"],
                                     g["ldb"], g["SFB"], g["ld_sfb"])
-    pm, pn = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
-    t_x = (TOL_MX * bound + np.ldexp(np.abs(ref), -24)).reshape(-1) + window_slack(O, g, "e4m3", "e2m1", K, pm, pn)
+    t_x = (TOL_MX * bound + np.ldexp(np.abs(ref), -24)).reshape(-1)
     f = O.ewise_silu_affine(ref, 2.0, 1.0).reshape(-1)
     silu = O.ewise_silu_affine(ref, 1.0, 0.0).reshape(-1)
     tol = 1.1 * 2.0 * t_x + np.ldexp(2.0 * np.abs(silu), -20) + np.ldexp(np.abs(f), -23) + np.ldexp(3.0, -112)
@@ -148,7 +109,7 @@ def test_mx_any_full_size_sampled(O, a_fmt, b_fmt):
     pm, pn = W.sample_points(M, N, 600)
     ref, bound = O.gemm_block_scale_points(M, N, K, a_fmt, g["A"], K, g["SFA"], K // 32, b_fmt, g["B"], K, g["SFB"],
                                            K // 32, None, 0, 0, 0, 0, pm, pn)
-    nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, pm, pn)
+    nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, pm, pn, name=f"{a_fmt} x {b_fmt} 8192x8192x16384 (600 points)")
     assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()
 
@@ -168,5 +129,5 @@ def test_mx_any_scale_groups(O, a_fmt, b_fmt):
         D = run(g, M, N, K, a_fmt, b_fmt, d0 if accum else None, 0, 0, accum)
         ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
                                         g["ldb"], g["SFB"], g["ld_sfb"], d0, N, 0, 0, accum)
-        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, name=f"{a_fmt} x {b_fmt} scale groups")
         assert nb == 0, (K, worst)

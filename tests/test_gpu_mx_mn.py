@@ -1,10 +1,10 @@
 """GPU parity: block-scaled GEMM with MN-major operands (K rows, M or N contiguous;
 bsm_gemm_block_scale_major) against the oracle on the same MN-major storage.
 
-Tolerance as for the K-major pairs (test_gpu_mx_any): 1e-5 * sum|ab| + half an ulp of the
-float32 result + the scaled MFMA's accumulation-window slack. MN-major and K-major operands
-of a pair the general kernel runs in both orders go through the same MFMA sequence, so those
-results must also agree bit for bit.
+Tolerance as for the K-major pairs (test_gpu_mx_any): the stated bound, 1e-5 * sum|ab| +
+half an ulp of the float32 result. MN-major and K-major operands of a pair the general kernel
+runs in both orders go through the same MFMA sequence, so those results must also agree bit
+for bit.
 """
 import numpy as np
 import pytest
@@ -13,7 +13,7 @@ import block_scaled_matrix_amd as bsm
 from block_scaled_matrix_amd import workloads as W
 from gpu_util import dev, dev_f32, say
 from test_gpu_gemm import pad_cols, pad_scales
-from test_gpu_mx_any import check, window_slack
+from test_gpu_mx_any import check
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +82,7 @@ def test_mx_mn_vs_oracle(O, a_fmt, b_fmt, amaj, bmaj):
         say("mx mn", a_fmt, b_fmt, amaj, bmaj, M, N, K, neg_a, neg_b, accum)
         D = run(g, M, N, K, a_fmt, b_fmt, amaj, bmaj, d0 if accum else None, neg_a, neg_b, accum)
         ref, bound = oracle(O, g, M, N, K, a_fmt, b_fmt, amaj, bmaj, d0, neg_a, neg_b, accum)
-        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, name=f"{a_fmt} x {b_fmt} {amaj}{bmaj}-major shapes")
         assert nb == 0, (M, N, K, worst)
         assert np.isnan(D[:, N:]).all()
 
@@ -99,7 +99,7 @@ def test_mx_mn_scale_groups(O, a_fmt, b_fmt, amaj, bmaj):
         say("mx mn scale groups", a_fmt, b_fmt, amaj, bmaj, M, N, K)
         D = run(g, M, N, K, a_fmt, b_fmt, amaj, bmaj)
         ref, bound = oracle(O, g, M, N, K, a_fmt, b_fmt, amaj, bmaj)
-        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, name=f"{a_fmt} x {b_fmt} {amaj}{bmaj}-major scale groups")
         assert nb == 0, (K, worst)
 
 
@@ -112,7 +112,7 @@ def test_mx_mn_with_6bit_kmajor_operand(O, a_fmt, b_fmt, amaj, bmaj):
         say("mx mn 6-bit partner", a_fmt, b_fmt, amaj, bmaj, M, N, K)
         D = run(g, M, N, K, a_fmt, b_fmt, amaj, bmaj)
         ref, bound = oracle(O, g, M, N, K, a_fmt, b_fmt, amaj, bmaj)
-        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound)
+        nb, worst = check(O, g, a_fmt, b_fmt, K, D, ref, bound, name=f"{a_fmt} x {b_fmt} {amaj}{bmaj}-major 6-bit partner")
         assert nb == 0, (M, N, K, worst)
 
 
@@ -154,7 +154,7 @@ def test_mx_mn_nan_scale_and_epilogue(O):
     D = run(g, M, N, K, "e4m3", "e2m1", "m", "n", ew=bsm.ewise_desc("silu_affine", 2.0, 1.0))
     ref, bound = oracle(O, g, M, N, K, "e4m3", "e2m1", "m", "n")
     pm, pn = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
-    t_x = (1e-5 * bound + np.ldexp(np.abs(ref), -24)).reshape(-1) + window_slack(O, g, "e4m3", "e2m1", K, pm, pn)
+    t_x = (1e-5 * bound + np.ldexp(np.abs(ref), -24)).reshape(-1)
     f = O.ewise_silu_affine(ref, 2.0, 1.0).reshape(-1)
     silu = O.ewise_silu_affine(ref, 1.0, 0.0).reshape(-1)
     tol = 1.1 * 2.0 * t_x + np.ldexp(2.0 * np.abs(silu), -20) + np.ldexp(np.abs(f), -23) + np.ldexp(3.0, -112)
@@ -175,6 +175,7 @@ def test_mx_mn_full_size_sampled(O, a_fmt, b_fmt, amaj, bmaj):
     pm, pn = W.sample_points(M, N, 600)
     ref, bound = O.gemm_block_scale_points(M, N, K, a_fmt, As, lda, g["SFA"], K // 32, b_fmt, Bs, ldb, g["SFB"],
                                            K // 32, None, 0, 0, 0, 0, pm, pn, a_major=amaj, b_major=bmaj)
-    nb, worst = check(O, gs, a_fmt, b_fmt, K, D, ref, bound, pm, pn)
+    nb, worst = check(O, gs, a_fmt, b_fmt, K, D, ref, bound, pm, pn,
+                      name=f"{a_fmt} x {b_fmt} {amaj}{bmaj}-major 8192x8192x16384 (600 points)")
     assert nb == 0, worst
     assert np.isfinite(D[:, :N]).all()

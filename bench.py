@@ -53,13 +53,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"hbm_GBs": 8000.0, "bf16_TFs": 2516.6, "fp8_TFs": 5033.2, "fp4_TFs": 10066.3}
+# The MFMA each GEMM row executes, and that instruction's dense peak. Block-scaled pairings
+# with wide product ranges (any 8-bit operand) sum exact products with the bf16 MFMA, so
+# their rate is bounded by the bf16 peak; `frac` stays against the format's own MFMA peak.
+INSTRUCTION = {
+    "gemm_bf16": ("v_mfma_f32_32x32x16_bf16", "bf16_TFs"),
+    "gemm_mxfp8": ("v_mfma_f32_32x32x16_bf16 (exact products)", "bf16_TFs"),
+    "gemm_mxfp4": ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", "fp4_TFs"),
+    "gemm_mxfp8_fastacc": ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", "fp8_TFs"),
+    "gemm_e4m3_e2m1": ("v_mfma_f32_32x32x16_bf16 (exact products)", "bf16_TFs"),
+    "gemm_e2m3_e2m3": ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp6)", "fp4_TFs"),
+}
 
 # Source files each kernel is built from (their hash ties a counter summary to the code).
 _CSRC = os.path.join("block_scaled_matrix_amd", "csrc")
 KERNEL_SOURCES = {
     "box_copy": ["k_tile.hip", "bsm_device.hpp"],
     "gemm_bf16": ["k_gemm_dense.hip", "gemm_common.hpp", "bsm_device.hpp"],
-    "gemm_mxfp8": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_mxfp8": ["k_gemm_mx_any.hip", "gemm_mx_any.hpp", "gemm_common.hpp", "bsm_device.hpp"],
+    "gemm_mxfp8_fastacc": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
     "gemm_mxfp4": ["k_gemm_mx.hip", "gemm_common.hpp", "bsm_device.hpp"],
     "add_one": ["k_tile.hip", "bsm_device.hpp"],
     "gather4": ["k_tile.hip", "bsm_device.hpp"],
@@ -112,7 +124,15 @@ def measured_mfma(kernel):
     return None
 
 
+CALIB_K = 1 << 20   # the LDS-DMA calibration: one 256 x 256 output tile over K = 2^20 bf16
+
+
 def copy_calibration():
+    """Kernels of known HBM traffic for calibrating the byte counters: the float32 add-scalar copy
+    (coalesced 16-byte loads and stores; 1 GiB read + 1 GiB written per launch, three launches),
+    and a one-workgroup dense GEMM M = N = 256, K = 2^20 whose operands arrive only through the
+    GEMMs' direct HBM->LDS copies (global_load_lds): A and B are read exactly once (512 MiB each,
+    1 GiB in all) and 256 KiB of D is written."""
     import torch
 
     import block_scaled_matrix_amd as bsm
@@ -124,8 +144,15 @@ def copy_calibration():
     for _ in range(3):
         bsm.bsm_tile_add_scalar_f32(src, dst, n, 1.0)
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "add_scalar_f32", "bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
-                      "launches": 3}), flush=True)
+    del src, dst
+    A = torch.zeros(256 * CALIB_K, dtype=torch.int16, device="cuda")
+    B = torch.zeros_like(A)
+    D = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    bsm.bsm_gemm(256, 256, CALIB_K, "bf16", A, CALIB_K, "k", B, CALIB_K, "k", D, 256, 0, 0, 0)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": ["add_scalar_f32", "gemm_bf16 256x256x2^20 (global_load_lds)"],
+                      "bytes_read": [CALIB_BYTES, 2 * 256 * CALIB_K * 2], "bytes_written": [CALIB_BYTES, 256 * 256 * 4],
+                      "launches": [3, 1]}), flush=True)
 
 
 def log(*a):
@@ -235,11 +262,10 @@ def widened(inp):
     dst = bsm.tensor_desc(g["dst"], "bf16", (rows, cols), (cols * 2, 2))
     nbytes = 2 * rows * cols * 2                 # every table byte read once and written once (as image bytes)
 
-    def mx(key):
+    def mx(key, call=bsm.bsm_gemm_block_scale):
         x = inp[key]
-        return lambda: bsm.bsm_gemm_block_scale(x["M"], x["N"], x["K"], x["fmt"], x["A"], x["lda"], x["SFA"],
-                                                x["ld_sfa"], x["b_fmt"], x["B"], x["ldb"], x["SFB"], x["ld_sfb"],
-                                                x["D"], x["N"], 0, 0, 0)
+        return lambda: call(x["M"], x["N"], x["K"], x["fmt"], x["A"], x["lda"], x["SFA"], x["ld_sfa"], x["b_fmt"],
+                            x["B"], x["ldb"], x["SFB"], x["ld_sfb"], x["D"], x["N"], 0, 0, 0)
     flops = 2.0 * 8192 * 8192 * 16384
     b3 = inp["b3"]
     d3 = b3["dims"]
@@ -255,7 +281,48 @@ def widened(inp):
          PEAK["hbm_GBs"]),
         ("gemm_e4m3_e2m1", mx("mix"), flops, "TFLOP/s", PEAK["fp8_TFs"]),
         ("gemm_e2m3_e2m3", mx("fp6"), flops, "TFLOP/s", PEAK["fp4_TFs"]),
+        # the MXFP8 workload through the fast-accumulation call (scaled fp8 MFMA, its 2^-13
+        # block window: outside the stated bound on these operands)
+        ("gemm_mxfp8_fastacc", mx("fp8", bsm.bsm_gemm_block_scale_fastacc), 2.0 * 8192 * 8192 * 16384, "TFLOP/s",
+         PEAK["fp8_TFs"]),
     ]
+
+
+MFMA_LOOP = {"bf16": (800, 32768), "e4m3": (400, 131072), "e2m1": (800, 131072)}   # iters, FLOP per MFMA
+LOOP_WGS = 1024
+UNRAGGED_ROWS = 16256      # 127 box rows of 128: no ragged edge along either axis
+
+
+def ceilings(inp):
+    """(name, launch, work, unit, peak, note) of the diagnostic rows in `context`."""
+    import torch
+
+    import block_scaled_matrix_amd as bsm
+
+    b = inp["box"]
+    rows, cols, pitch = b["rows"], b["cols"], b["pitch"]
+    n = rows * pitch                                   # every element of the three buffers, padding included
+    st = (pitch * 2, 2)
+    td = lambda t: bsm.tensor_desc(t, "bf16", (UNRAGGED_ROWS, pitch), st)
+    box = bsm.box_desc(b["box"], (1, 1), 3, 0)
+    out = inp.setdefault("loop_out", torch.empty(LOOP_WGS * 256, dtype=torch.float32, device="cuda"))
+    rows_ = [
+        ("stream_mix_bf16", lambda: bsm.bsm_debug_stream_mix_bf16(b["src"], b["dst"], b["dst_add"], n), 4 * 2 * n,
+         "GB/s", PEAK["hbm_GBs"], "the box copy's traffic mix (read src, write dst, read and write dst_add) on the "
+         "three flat 16381 x 8192 bf16 buffers, 16-byte non-temporal accesses, no boxes: the stream ceiling of the mix"),
+        ("box_copy_unragged", lambda: bsm.bsm_tile_box_copy(td(b["src"]), td(b["dst"]), td(b["dst_add"]), box),
+         4 * UNRAGGED_ROWS * pitch * 2, "GB/s", PEAK["hbm_GBs"],
+         "bsm_tile_box_copy on a 16256 x 8192 view of the same buffers ((128, 64) boxes, 128-byte swizzle): "
+         "the workload's kernel with no ragged box row or column"),
+    ]
+    for kind, peak in (("bf16", PEAK["bf16_TFs"]), ("e4m3", PEAK["fp8_TFs"]), ("e2m1", PEAK["fp4_TFs"])):
+        iters, fl = MFMA_LOOP[kind]
+        rows_.append((f"mfma_loop_{kind}", (lambda k=kind, it=iters: bsm.bsm_debug_mfma_loop(k, LOOP_WGS, it, out)),
+                      float(LOOP_WGS * 4 * iters * 16 * fl), "TFLOP/s", peak,
+                      f"back-to-back {kind} MFMAs on random register operands, 16 accumulators per wave, "
+                      f"{LOOP_WGS} workgroups x {iters} iterations, no memory traffic: the matrix-pipe ceiling "
+                      "under the clock the device holds for that load"))
+    return rows_
 
 
 def time_launches(ks, steps, stream):
@@ -273,54 +340,301 @@ def time_launches(ks, steps, stream):
     return [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps for i in range(len(ks))]
 
 
-def rate_entry(ms, work, unit, peak):
+def rate_entry(ms, work, unit, peak, name=None):
     rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-    return {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
-            "frac": round(rate / peak, 4), "work_per_launch": work}
+    e = {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
+         "frac": round(rate / peak, 4), "work_per_launch": work}
+    if name in INSTRUCTION:
+        ins, key = INSTRUCTION[name]
+        e["instruction"], e["instruction_peak"] = ins, PEAK[key]
+        e["instruction_frac"] = round(rate / PEAK[key], 4)
+    return e
 
 
-def cpu_baseline():
-    """The oracle, as it stands, on a bounded sample of the same workloads."""
+def cpu_baseline(inp):
+    """The oracle, as it stands, on a bounded sample of the same workloads. Its rows also give
+    the GPU's parity on that sample: each call is launched once more on fresh outputs (the timed
+    steps accumulate into the bf16 D and the reduce-add target) and compared element by element
+    with the oracle, under the bound each row states (bf16: 2e-3 * sum|ab|, block scaled:
+    1e-5 * sum|ab|, both plus half an ulp of the float32 result; box copy: bit for bit)."""
     import numpy as np
+    import torch
 
+    import block_scaled_matrix_amd as bsm
     from block_scaled_matrix_amd import workloads as W
     from oracle import oracle as O
 
     O.lib()
     flops = 0.0
     t_gemm = 0.0
+    parity = {}
+
+    def gemm_parity(name, D, ref, bound, tol, sample):
+        nb, _, worst = O.check_gemm(np.ascontiguousarray(D, np.float32), ref, bound, tol)
+        parity[name] = {"sample": sample, "tol_sum_abs_ab": tol, "n_bad": nb, "worst_err_over_sum_abs_ab": worst}
+
     g = W.gemm_bf16()
     rows = 16
     t0 = time.perf_counter()
-    O.gemm(g["M"], g["N"], g["K"], "bf16", g["A"], g["K"], "k", g["B"], g["N"], "n", g["D0"], g["N"], 0, 0, 1, 0, rows)
+    ref, bound = O.gemm(g["M"], g["N"], g["K"], "bf16", g["A"], g["K"], "k", g["B"], g["N"], "n", g["D0"], g["N"], 0,
+                        0, 1, 0, rows)
     t_gemm += time.perf_counter() - t0
     flops += 2.0 * rows * g["N"] * g["K"]
+    x = inp["bf16"]
+    D = torch.from_numpy(g["D0"][:rows].copy()).cuda()   # the first rows of D0, accumulated once
+    bsm.bsm_gemm(rows, x["N"], x["K"], "bf16", x["A"], x["K"], "k", x["B"], x["N"], "n", D, x["N"], 0, 0, 1)
+    gemm_parity("gemm_bf16", D.cpu().numpy(), ref, bound, 2e-3, f"rows 0..{rows - 1}, all columns")
     del g
     g = W.mxfp8()
+    rows = 4
     t0 = time.perf_counter()
-    O.gemm_block_scale(g["M"], g["N"], g["K"], "e4m3", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e4m3", g["B"], g["K"],
-                       g["SFB"], g["ld_sfb"], None, 0, 0, 0, 0, 0, 4)
+    ref, bound = O.gemm_block_scale(g["M"], g["N"], g["K"], "e4m3", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e4m3",
+                                    g["B"], g["K"], g["SFB"], g["ld_sfb"], None, 0, 0, 0, 0, 0, rows)
     t_gemm += time.perf_counter() - t0
-    flops += 2.0 * 4 * g["N"] * g["K"]
+    flops += 2.0 * rows * g["N"] * g["K"]
+    x = inp["fp8"]
+    x["D"].fill_(float("nan"))
+    bsm.bsm_gemm_block_scale(x["M"], x["N"], x["K"], "e4m3", x["A"], x["lda"], x["SFA"], x["ld_sfa"], "e4m3", x["B"],
+                             x["ldb"], x["SFB"], x["ld_sfb"], x["D"], x["N"], 0, 0, 0)
+    gemm_parity("gemm_mxfp8", x["D"][:rows].cpu().numpy(), ref, bound, 1e-5, f"rows 0..{rows - 1}, all columns")
+    x["D"].fill_(float("nan"))
+    bsm.bsm_gemm_block_scale_fastacc(x["M"], x["N"], x["K"], "e4m3", x["A"], x["lda"], x["SFA"], x["ld_sfa"], "e4m3",
+                                     x["B"], x["ldb"], x["SFB"], x["ld_sfb"], x["D"], x["N"], 0, 0, 0)
+    gemm_parity("gemm_mxfp8_fastacc", x["D"][:rows].cpu().numpy(), ref, bound, 1e-5,
+                f"rows 0..{rows - 1}, all columns (fast accumulation: not expected within the bound)")
     del g
     g = W.mxfp4()
+    rows = 8
     t0 = time.perf_counter()
-    O.gemm_block_scale(g["M"], g["N"], g["K"], "e2m1", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e2m1", g["B"], g["K"],
-                       g["SFB"], g["ld_sfb"], None, 0, 1, 0, 0, 0, 8)
+    ref, bound = O.gemm_block_scale(g["M"], g["N"], g["K"], "e2m1", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e2m1",
+                                    g["B"], g["K"], g["SFB"], g["ld_sfb"], None, 0, 1, 0, 0, 0, rows)
     t_gemm += time.perf_counter() - t0
-    flops += 2.0 * 8 * g["N"] * g["K"]
+    flops += 2.0 * rows * g["N"] * g["K"]
+    x = inp["fp4"]
+    x["D"].fill_(float("nan"))
+    bsm.bsm_gemm_block_scale(x["M"], x["N"], x["K"], "e2m1", x["A"], x["lda"], x["SFA"], x["ld_sfa"], "e2m1", x["B"],
+                             x["ldb"], x["SFB"], x["ld_sfb"], x["D"], x["N"], 1, 0, 0)
+    gemm_parity("gemm_mxfp4", x["D"][:rows].cpu().numpy(), ref, bound, 1e-5, f"rows 0..{rows - 1}, all columns")
     del g
     # box round trip on a 1024-row band of the copy workload (128 boxes wide)
     b = W.box_copy_bf16(rows=1024)
+    st = (b["pitch"] * 2, 2)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ds, dd, da = dev(b["src"]), dev(b["dst"]), dev(b["dst_add"])
+    td = lambda t: bsm.tensor_desc(t, "bf16", (1024, b["cols"]), st)
+    bsm.bsm_tile_box_copy(td(ds), td(dd), td(da), bsm.box_desc(b["box"], (1, 1), 3, 0))
     t0 = time.perf_counter()
-    O.box_copy_grid(b["src"], b["dst"], b["dst_add"], "bf16", (1024, b["cols"]), (b["pitch"] * 2, 2), b["box"], (1, 1),
-                    3, 0)
+    O.box_copy_grid(b["src"], b["dst"], b["dst_add"], "bf16", (1024, b["cols"]), st, b["box"], (1, 1), 3, 0)
     t_box = time.perf_counter() - t0
     box_gbs = 4 * 1024 * b["cols"] * 2 / t_box / 1e9
-    return {"value": flops / t_gemm / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+    same = (np.array_equal(dd.cpu().numpy(), b["dst"]), np.array_equal(da.cpu().numpy(), b["dst_add"]))
+    parity["box_copy"] = {"sample": "a 1024x8190 band (128 boxes wide), store and reduce-add, padding included",
+                          "bit_exact": bool(all(same))}
+    base = {"value": flops / t_gemm / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"GEMM rows: bf16 16 of 8192, mxfp8 4 of 8192, mxfp4 8 of 16384 (full N and K), "
                       f"{t_gemm:.1f} s; box copy on a 1024x8190 band: {box_gbs:.3f} GB/s in {t_box:.1f} s",
             "box_copy_GBs": box_gbs}
+    return base, parity
+
+
+# rocprofv3 kernel names -> bench row names (first match wins). Two k_box_copy2d groups are
+# told apart by their grid: the workload's (16381 rows) has more workgroups than the
+# unragged 16256-row view.
+NAME_RULES = [
+    (r"k_gemm_dense<4, true, false, true>", "gemm_bf16"),
+    (r"k_gemm_mx_any<0, 0, false, false, true>", "gemm_mxfp8"),
+    (r"k_gemm_mx<0, 0, 0, false>", "gemm_mxfp8_fastacc"),
+    (r"k_gemm_mx<4, 4, 4, false>", "gemm_mxfp4"),
+    (r"k_gemm_mx_any<0, 4, false, false, true>", "gemm_e4m3_e2m1"),
+    (r"k_gemm_mx_any<2, 2, false, false, false>", "gemm_e2m3_e2m3"),
+    (r"k_row4<false>", "gather4"),
+    (r"k_row4<true>", "scatter4"),
+    (r"k_box_load\(", "box_load_rank3"),
+    (r"k_add_scalar_f32", "add_one"),
+    (r"k_stream_mix_bf16", "stream_mix_bf16"),
+    (r"k_mfma_loop<4>", "mfma_loop_bf16"),
+    (r"k_mfma_loop<6>", "mfma_loop_e4m3"),
+    (r"k_mfma_loop<7>", "mfma_loop_e2m1"),
+    (r"k_box_copy2d", "box_copy*"),
+]
+# Algorithmic HBM bytes per launch of the GEMMs: operands once, D written (and read when
+# accumulating), scales once.
+ALG_BYTES = {
+    "gemm_bf16": 2 * 8192 * 8192 * 2 + 2 * 8192 * 8192 * 4,
+    "gemm_mxfp8": 2 * 8192 * 16384 + 2 * 8192 * 512 + 8192 * 8192 * 4,
+    "gemm_mxfp8_fastacc": 2 * 8192 * 16384 + 2 * 8192 * 512 + 8192 * 8192 * 4,
+    "gemm_mxfp4": 16384 * 4096 + 8192 * 4096 + 16384 * 256 + 8192 * 256 + 16384 * 8192 * 4,
+    "gemm_e4m3_e2m1": 8192 * 16384 + 8192 * 8192 + 2 * 8192 * 512 + 8192 * 8192 * 4,
+    "gemm_e2m3_e2m3": 2 * 8192 * 12288 + 2 * 8192 * 512 + 8192 * 8192 * 4,
+}
+# Work per launch (FLOP or algorithmic bytes), the same figures the timed run uses.
+STATIC_WORK = {
+    "box_copy": (4 * 16381 * 8190 * 2, "GB/s", PEAK["hbm_GBs"]),
+    "box_copy_unragged": (4 * UNRAGGED_ROWS * 8192 * 2, "GB/s", PEAK["hbm_GBs"]),
+    "stream_mix_bf16": (4 * 2 * 16381 * 8192, "GB/s", PEAK["hbm_GBs"]),
+    "gemm_bf16": (2.0 * 8192 ** 3, "TFLOP/s", PEAK["bf16_TFs"]),
+    "gemm_mxfp8": (2.0 * 8192 * 8192 * 16384, "TFLOP/s", PEAK["fp8_TFs"]),
+    "gemm_mxfp8_fastacc": (2.0 * 8192 * 8192 * 16384, "TFLOP/s", PEAK["fp8_TFs"]),
+    "gemm_mxfp4": (2.0 * 16384 * 8192 * 8192, "TFLOP/s", PEAK["fp4_TFs"]),
+    "gemm_e4m3_e2m1": (2.0 * 8192 * 8192 * 16384, "TFLOP/s", PEAK["fp8_TFs"]),
+    "gemm_e2m3_e2m3": (2.0 * 8192 * 8192 * 16384, "TFLOP/s", PEAK["fp4_TFs"]),
+    "gather4": (2 * 65536 * 4096 * 2, "GB/s", PEAK["hbm_GBs"]),
+    "scatter4": (2 * 65536 * 4096 * 2, "GB/s", PEAK["hbm_GBs"]),
+    "box_load_rank3": (2 * (64 * 2048 // 2 * 2048 * 2), "GB/s", PEAK["hbm_GBs"]),
+    "add_one": (2 * 768 * 4, "GB/s", PEAK["hbm_GBs"]),
+}
+for _k, (_it, _fl) in MFMA_LOOP.items():
+    STATIC_WORK[f"mfma_loop_{_k}"] = (float(LOOP_WGS * 4 * _it * 16 * _fl), "TFLOP/s",
+                                      PEAK[{"bf16": "bf16_TFs", "e4m3": "fp8_TFs", "e2m1": "fp4_TFs"}[_k]])
+
+
+def _profile_groups(rows, steps):
+    """rows: (kernel name, grid, start, end, extra) per dispatch. Groups them by (bench name, grid),
+    keeps each group's last `steps` dispatches (the timed launches: the bench issues every row's
+    untimed launches first) and returns {bench name: [(start, end, extra), ...]}, plus a log."""
+    import re
+    groups = {}
+    for name, grid, t0, t1, extra in rows:
+        bench = None
+        for rx, bn in NAME_RULES:
+            if re.search(rx, name):
+                bench = bn
+                break
+        if bench is None:
+            continue
+        groups.setdefault((bench, grid), []).append((t0, t1, extra, name))
+    boxes = sorted((g for g in groups if g[0] == "box_copy*"), key=lambda g: -g[1])
+    out, names = {}, {}
+    for key, lst in groups.items():
+        bench = key[0]
+        if bench == "box_copy*":
+            bench = "box_copy" if key == boxes[0] else "box_copy_unragged"
+        lst.sort()
+        kept = lst[-steps:] if steps else lst
+        out[bench] = [(a, b, e) for a, b, e, _ in kept]
+        names[bench] = (lst[0][3], key[1], len(lst), len(kept))
+    return out, names
+
+
+def summarize(dirs, steps, calib=None):
+    """Markdown summaries of rocprofv3 CSV output (kernel trace and/or counter collection)
+    under `dirs`, over each row's timed launches only (its last `steps` dispatches)."""
+    import csv
+    import glob
+
+    def rd(pattern):
+        fs = []
+        for d in dirs:
+            fs += glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        out = []
+        for f in fs:
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    trace = rd("*kernel_trace.csv")
+    if trace:
+        rows = [(r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+                 int(r["Start_Timestamp"]), int(r["End_Timestamp"]), None) for r in trace]
+        g, names = _profile_groups(rows, steps)
+        print("| bench name | kernel | workgroups | launches (kept / all) | mean us | min us | max us | achieved | frac |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for bench in sorted(g, key=lambda b: -sum(e - s for s, e, _ in g[b])):
+            d = [(e - s) / 1e3 for s, e, _ in g[bench]]
+            mean = sum(d) / len(d)
+            kname, grid, nall, nkept = names[bench]
+            work, unit, peak = STATIC_WORK.get(bench, (None, "", None))
+            ach = f"{work / (mean * 1e-6) / (1e12 if unit == 'TFLOP/s' else 1e9):.1f} {unit}" if work else ""
+            frac = f"{work / (mean * 1e-6) / (1e12 if unit == 'TFLOP/s' else 1e9) / peak:.4f}" if work else ""
+            print(f"| {bench} | `{kname[:60]}` | {grid // 256} | {nkept} / {nall} | {mean:.1f} | {min(d):.1f} | "
+                  f"{max(d):.1f} | {ach} | {frac} |")
+    # counters: one rocprofv3 pass per directory (each pass its own process); per row, the mean
+    # of each counter over its timed dispatches, merged over the passes
+    means, durs, kept = {}, {}, {}
+    for d in dirs:
+        cc = rd_dir(d)
+        if not cc:
+            continue
+        per = {}
+        for r in cc:
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+            per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        g, _ = _profile_groups([(k[0], k[1], k[2], k[3], v) for k, v in per.items()], steps)
+        for bench, lst in g.items():
+            for c in {c for x in lst for c in x[2]}:
+                means.setdefault(bench, {})[c] = sum(x[2].get(c, 0.0) for x in lst) / len(lst)
+            durs.setdefault(bench, []).append(sum(e - s for s, e, _ in lst) / len(lst))
+            kept[bench] = len(lst)
+    if means:
+        cal = {"FETCH_SIZE": 1.0, "WRITE_SIZE": 1.0}
+        if calib:
+            # true KiB per dispatch of each calibration kernel, per counter
+            truth = {"FETCH_SIZE": {"k_add_scalar_f32": CALIB_BYTES / 1024, "k_gemm_dense": 2 * 256 * CALIB_K * 2 / 1024},
+                     "WRITE_SIZE": {"k_add_scalar_f32": CALIB_BYTES / 1024, "k_gemm_dense": 256 * 256 * 4 / 1024}}
+            print("| counter | calibration kernel | dispatches | counter KiB (mean) | true KiB | true / counter |")
+            print("|---|---|---|---|---|---|")
+            for c, dirc in calib.items():
+                for kern, true_kib in truth[c].items():
+                    vals = [float(r["Counter_Value"]) for r in rd_dir(dirc)
+                            if r["Counter_Name"] == c and kern in r["Kernel_Name"]]
+                    if not vals:
+                        continue
+                    f = true_kib / (sum(vals) / len(vals))
+                    if kern == "k_add_scalar_f32":
+                        cal[c] = f
+                    print(f"| {c} | {kern} | {len(vals)} | {sum(vals) / len(vals):.0f} | {true_kib:.0f} | {f:.4f} |")
+            print("\nfactors applied below (the plain copy's): " + ", ".join(f"{c} {v:.4f}" for c, v in cal.items()) +
+                  "\n")
+        counters = sorted({c for v in means.values() for c in v})
+        print("| bench name | launches kept | mean us | " + " | ".join(counters) + " | derived |")
+        print("|---|---|---|" + "---|" * len(counters) + "---|")
+        machine = []
+        for bench in sorted(means):
+            mean = means[bench]
+            dur = sum(durs[bench]) / len(durs[bench])   # ns
+            der = []
+            if mean.get("GRBM_GUI_ACTIVE", 0) > 0:
+                cyc = mean["GRBM_GUI_ACTIVE"] / 8
+                clock = cyc / dur
+                der.append(f"clock {clock:.2f} GHz")
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                    busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc)
+                    der.append(f"MFMA busy {busy:.3f}")
+                    if bench in KERNEL_SOURCES and busy > 0:
+                        machine.append(f"mfma: {bench} {busy:.4f} {clock:.4f} {source_hash(bench)}")
+            if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
+                act, con = mean["SQ_LDS_IDX_ACTIVE"], mean["SQ_LDS_BANK_CONFLICT"]
+                der.append(f"conflict ratio {con / max(act - con, 1):.3f}")
+            if "SQ_WAIT_INST_LDS" in mean and mean.get("SQ_WAVE_CYCLES", 0) > 0:
+                der.append(f"LDS-issue wait {4 * mean['SQ_WAIT_INST_LDS'] / mean['SQ_WAVE_CYCLES']:.3f}")
+            if "FETCH_SIZE" in mean and "WRITE_SIZE" in mean:
+                b = int(round((mean["FETCH_SIZE"] * cal["FETCH_SIZE"] + mean["WRITE_SIZE"] * cal["WRITE_SIZE"]) * 1024))
+                alg = STATIC_WORK.get(bench)
+                if alg and alg[1] == "GB/s":
+                    der.append(f"HBM bytes {b} ({b / alg[0]:.2f}x algorithmic)")
+                elif bench in ALG_BYTES:
+                    der.append(f"HBM bytes {b} ({b / ALG_BYTES[bench]:.2f}x algorithmic {ALG_BYTES[bench]})")
+                else:
+                    der.append(f"HBM bytes {b}")
+                if bench in KERNEL_SOURCES:
+                    machine.append(f"traffic: {bench} {b} {source_hash(bench)}")
+            print(f"| {bench} | {kept[bench]} | {dur / 1e3:.1f} | " + " | ".join(f"{mean.get(c, 0.0):.4g}" for c in counters) +
+                  " | " + "; ".join(der) + " |")
+        if machine:
+            print("\nMachine-readable rows for bench.py (mfma: kernel, MFMA busy, clock GHz, source hash; traffic: "
+                  "kernel, HBM bytes per launch, source hash):\n\n```")
+            print("\n".join(machine))
+            print("```")
+
+
+def rd_dir(d):
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            out += list(csv.DictReader(fh))
+    return out
 
 
 def main():
@@ -333,7 +647,20 @@ def main():
                     help="scalar epilogue fused into the GEMMs' stores")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the plain copy of known size used to calibrate the HBM byte counters")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print markdown summaries of rocprofv3 CSV output under DIR (kernel trace, counters) over "
+                         "each row's timed launches (the last --steps dispatches of each kernel); no GPU needed")
+    ap.add_argument("--calib-fetch", metavar="DIR", help="with --summarize: FETCH_SIZE run of --copy-calibration")
+    ap.add_argument("--calib-write", metavar="DIR", help="with --summarize: WRITE_SIZE run of --copy-calibration")
     args = ap.parse_args()
+    if args.summarize:
+        calib = {}
+        if args.calib_fetch:
+            calib["FETCH_SIZE"] = args.calib_fetch
+        if args.calib_write:
+            calib["WRITE_SIZE"] = args.calib_write
+        summarize(args.summarize, args.steps, calib or None)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); every workload here fits one MI355X and "
               "no multi-GPU path is part of this library.", file=sys.stderr)
@@ -381,8 +708,8 @@ def main():
     for i, (name, _, work, unit, peak) in enumerate(ks):
         ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
         rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-        per[name] = {"ms": round(ms, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
-                     "frac": round(rate / peak, 4), "work_per_launch": work, "traffic": measured_traffic(name)}
+        per[name] = rate_entry(ms, work, unit, peak, name)
+        per[name]["traffic"] = measured_traffic(name)
         mf = measured_mfma(name)
         if mf is not None:   # counter figures of the same kernel sources (profiles/mfma_busy_bench_step.md)
             per[name]["mfma_busy"], per[name]["clock_ghz"] = mf
@@ -393,7 +720,7 @@ def main():
     torch.cuda.synchronize()
     wide = {}
     for (name, _, work, unit, peak), ms in zip(wk, time_launches(wk, args.steps, stream)):
-        wide[name] = rate_entry(ms, work, unit, peak)
+        wide[name] = rate_entry(ms, work, unit, peak, name)
         wide[name]["traffic"] = measured_traffic(name)
         mf = measured_mfma(name)
         if mf is not None:
@@ -411,16 +738,31 @@ def main():
     context["torch_mm_bf16"]["note"] = ("hipBLASLt through torch.mm, bf16 8192^3, fresh bf16 output, no accumulation: "
                                         "a vendor-library reference point, not part of the step")
     log(f"torch_mm_bf16 (context): {context['torch_mm_bf16']['ms']:.4f} ms  {context['torch_mm_bf16']['achieved']:.1f} TFLOP/s")
+    # the ceilings the rows run against, measured with the library's diagnostic kernels on the
+    # same device in the same run (not part of the step)
+    ck = ceilings(inp)
+    for _, fn, *_ in ck:
+        fn()
+    torch.cuda.synchronize()
+    for (name, _, work, unit, peak, note), ms in zip(ck, time_launches(ck, args.steps, stream)):
+        context[name] = rate_entry(ms, work, unit, peak)
+        context[name]["note"] = note
+        context[name]["traffic"] = measured_traffic(name)
+        mf = measured_mfma(name)
+        if mf is not None:
+            context[name]["mfma_busy"], context[name]["clock_ghz"] = mf
+        log(f"{name} (context): {ms:.4f} ms  {context[name]['achieved']:.1f} {unit}")
     dom = max((n for n in per if n != "add_one"), key=lambda n: per[n]["ms"])
     d = per[dom]
     gemm_flops = sum(k[2] for k in ks if k[0].startswith("gemm"))
     value = gemm_flops / (ms_step * 1e-3) / 1e12
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline()
+        log("cpu baseline (oracle) and parity on its sample ...")
+        cpu, parity = cpu_baseline(inp)
         log(f"cpu baseline: {cpu}")
+        log(f"parity: {parity}")
 
     out = {
         "metric": "GEMM TFLOP/s (% MFMA peak) bf16/MXFP8/MXFP4; box-copy GB/s (% HBM)",
@@ -435,9 +777,11 @@ def main():
         "per_kernel": per,
         "widened": wide,
         "context": context,
-        "roofline": {"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
-                     "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dom)},
+        "roofline": dict({"kernel": dom, "bound": "hbm" if d["unit"] == "GB/s" else "mfma", "achieved": d["achieved"],
+                          "peak": d["peak"], "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dom)},
+                         **{k: d[k] for k in ("instruction", "instruction_peak", "instruction_frac") if k in d}),
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(out), flush=True)
 

@@ -24,7 +24,7 @@ EWISE = {"none": 0, "silu_affine": 1}
 EXPORTS = ("bsm_image_stride", "bsm_tile_box_load", "bsm_tile_box_store", "bsm_tile_box_copy",
            "bsm_tile_box_load_steps", "bsm_tile_box_store_steps", "bsm_tile_gather4", "bsm_tile_scatter4", "bsm_gemm",
            "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise", "bsm_gemm_block_scale_major",
-           "bsm_gemm_block_scale_fastacc", "bsm_tile_add_scalar_f32", "bsm_debug_fragments", "bsm_debug_fragment_shape", "bsm_last_error")
+           "bsm_gemm_block_scale_fastacc", "bsm_debug_stream_mix_bf16", "bsm_debug_mfma_loop", "bsm_tile_add_scalar_f32", "bsm_debug_fragments", "bsm_debug_fragment_shape", "bsm_last_error")
 
 
 class BsmError(RuntimeError):
@@ -81,6 +81,8 @@ def lib():
                                                  P, I64, P, I64, C.c_int, C.c_int, C.c_int, C.POINTER(bsm_ewise), P]
         L.bsm_gemm_block_scale_fastacc.argtypes = L.bsm_gemm_block_scale_ewise.argtypes
         L.bsm_tile_add_scalar_f32.argtypes = [P, P, I64, C.c_float, P]
+        L.bsm_debug_stream_mix_bf16.argtypes = [P, P, P, I64, P]
+        L.bsm_debug_mfma_loop.argtypes = [I32, I64, I32, P, P]
         L.bsm_debug_fragments.argtypes = [P, I64, I64, C.c_char, P, P]
         L.bsm_debug_fragment_shape.restype = None
         L.bsm_debug_fragment_shape.argtypes = [C.POINTER(I64), C.POINTER(I64)]
@@ -89,7 +91,7 @@ def lib():
                       "bsm_tile_scatter4", "bsm_gemm",
                       "bsm_gemm_block_scale", "bsm_gemm_ewise", "bsm_gemm_block_scale_ewise",
                       "bsm_gemm_block_scale_major", "bsm_gemm_block_scale_fastacc", "bsm_tile_add_scalar_f32",
-                      "bsm_debug_fragments"):
+                      "bsm_debug_fragments", "bsm_debug_stream_mix_bf16", "bsm_debug_mfma_loop"):
             getattr(L, rc_fn).restype = C.c_int
         _lib = L
     return _lib
@@ -264,3 +266,11 @@ def bsm_debug_fragment_shape():
 
 def bsm_debug_fragments(src, rows: int, kdim: int, major: str, dump, stream=None):
     _check(lib().bsm_debug_fragments(_ptr(src), rows, kdim, major.encode(), _ptr(dump), _stream(stream)))
+
+
+def bsm_debug_stream_mix_bf16(src, dst, add, n: int, stream=None):
+    _check(lib().bsm_debug_stream_mix_bf16(_ptr(src), _ptr(dst), _ptr(add), n, _stream(stream)))
+
+
+def bsm_debug_mfma_loop(kind: str, workgroups: int, iters: int, out, stream=None):
+    _check(lib().bsm_debug_mfma_loop(DTYPE[kind], workgroups, iters, _ptr(out), _stream(stream)))

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsm.so")
 SOURCES = ["bsm_api.hip", "k_tile.hip", "k_gemm_dense.hip", "k_gemm_mx.hip", "k_gemm_mx_any.hip",
-           "k_gemm_mx_mn_a.hip", "k_gemm_mx_mn_b.hip", "k_gemm_mx_mn_ab.hip"]
+           "k_gemm_mx_mn_a.hip", "k_gemm_mx_mn_b.hip", "k_gemm_mx_mn_ab.hip", "k_diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: never emit packed fp32 arithmetic (v_pk_*_f32).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

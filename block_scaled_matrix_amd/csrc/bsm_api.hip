@@ -528,6 +528,33 @@ int bsm_tile_add_scalar_f32(const float* src, float* dst, int64_t n, float s, vo
   return ok();
 }
 
+int bsm_debug_stream_mix_bf16(const void* src, void* dst, void* add, int64_t n, void* stream) {
+  if (n < 0 || n % 8) return fail(BSM_E_SHAPE, "n = %lld must be a non-negative multiple of 8", (long long)n);
+  if (n == 0) return ok();
+  if (!src || !dst || !add) return fail(BSM_E_NULL, "src, dst or add is NULL");
+  if ((uintptr_t)src % 16 || (uintptr_t)dst % 16 || (uintptr_t)add % 16)
+    return fail(BSM_E_ALIGN, "src, dst and add must be 16-byte aligned");
+  const uintptr_t nb = (uintptr_t)n * 2;
+  const Range a{(uintptr_t)src, (uintptr_t)src + nb}, b{(uintptr_t)dst, (uintptr_t)dst + nb},
+      c{(uintptr_t)add, (uintptr_t)add + nb};
+  if (overlap(a, b) || overlap(a, c) || overlap(b, c)) return fail(BSM_E_ALIAS, "src, dst and add must not overlap");
+  hipError_t e = bsm::launch_stream_mix_bf16(src, dst, add, n, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsm_debug_stream_mix_bf16");
+  return ok();
+}
+
+int bsm_debug_mfma_loop(int32_t kind, int64_t workgroups, int32_t iters, float* out, void* stream) {
+  if (kind != BSM_BF16 && kind != BSM_E4M3 && kind != BSM_E2M1)
+    return fail(BSM_E_DTYPE, "kind %d: the MFMA loop takes BSM_BF16, BSM_E4M3 or BSM_E2M1", kind);
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return fail(BSM_E_SHAPE, "workgroups = %lld and iters = %d must lie in 1 .. 2^20", (long long)workgroups, iters);
+  if (!out) return fail(BSM_E_NULL, "out is NULL");
+  if ((uintptr_t)out % 4) return fail(BSM_E_ALIGN, "out must be 4-byte aligned");
+  hipError_t e = bsm::launch_mfma_loop(kind, workgroups, iters, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsm_debug_mfma_loop");
+  return ok();
+}
+
 void bsm_debug_fragment_shape(int64_t* rows, int64_t* kdim) {
   if (rows) *rows = bsm::kDenseTileRows;
   if (kdim) *kdim = bsm::kDenseTileK;

@@ -86,6 +86,12 @@ hipError_t launch_gemm_mx_mn_a(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mx_mn_b(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mx_mn_ab(const GemmArgs& a, hipStream_t st);
 
+// Diagnostics (k_diag.hip): the box copy's traffic mix on flat bf16 buffers of n elements
+// (n a multiple of 8, 16-byte aligned), and workgroups x 256 lanes of back-to-back MFMAs of
+// `kind` (BSM_BF16, BSM_E4M3, BSM_E2M1), iters x 16 per wave, one float per lane to out.
+hipError_t launch_stream_mix_bf16(const void* src, void* dst, void* add, int64_t n, hipStream_t st);
+hipError_t launch_mfma_loop(int kind, int64_t workgroups, int iters, float* out, hipStream_t st);
+
 // Operand-tile geometry of the dense GEMM (rows x K elements per LDS stage).
 constexpr int kDenseTileRows = 256;
 constexpr int kDenseTileK = 64;

@@ -337,6 +337,24 @@ int bsm_debug_fragments(const uint16_t* src, int64_t rows, int64_t kdim, char ma
                         uint16_t* dump, void* stream);
 void bsm_debug_fragment_shape(int64_t* rows, int64_t* kdim);
 
+/* Diagnostic: the box copy's HBM traffic mix on flat buffers, with no boxes and no edges:
+ * dst[i] = src[i] and add[i] = RNE_bf16(add[i] + src[i]) for i < n bf16 elements (4 * 2 * n
+ * bytes moved, as bsm_tile_box_copy moves per element), 16-byte non-temporal accesses. It
+ * measures the stream rate this read/write mix sustains on the device, the ceiling of the
+ * box copy ([TMA] "Stores, reductions, and completion"). n a multiple of 8 (n == 0: no-op);
+ * src, dst, add 16-byte aligned and pairwise non-overlapping. */
+int bsm_debug_stream_mix_bf16(const void* src, void* dst, void* add, int64_t n, void* stream);
+
+/* Diagnostic: workgroups x 256 lanes of back-to-back MFMAs on random register operands,
+ * 16 independent 32x32 accumulators per wave (the GEMMs' layout), iters x 16 MFMAs per wave,
+ * no memory or LDS traffic: the matrix-pipe rate the device holds under that load ([MMA]
+ * "Example: four K16 issues": the MMA issue stream alone). kind: BSM_BF16 (v_mfma_f32_32x32x16_bf16,
+ * 32768 FLOP each), BSM_E4M3 or BSM_E2M1 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales,
+ * 131072 FLOP each); so 4 * 16 * iters * workgroups MFMAs per launch. out receives one float
+ * per lane (workgroups * 256, the lane's accumulator sum, so that no MFMA is dead code);
+ * 4-byte aligned. workgroups and iters in 1 .. 2^20. */
+int bsm_debug_mfma_loop(int32_t kind, int64_t workgroups, int32_t iters, float* out, void* stream);
+
 /* Message describing the last nonzero status returned on this thread. */
 const char* bsm_last_error(void);
 

@@ -207,6 +207,19 @@ def test_gemm_contract_violations(L):
     expect("BSM_E_ALIGN", a, A + 4, B, 8, 1.0)
     expect("BSM_E_ALIAS", a, A, A + 16, 8, 1.0)
     expect("BSM_E_NULL", a, 0, B, 8, 1.0)
+    mix = lambda *x: bsm.bsm_debug_stream_mix_bf16(*x, stream=0)
+    expect("BSM_E_SHAPE", mix, A, B, D, 12)                      # not a multiple of 8
+    expect("BSM_E_SHAPE", mix, A, B, D, -8)
+    expect("BSM_E_NULL", mix, A, 0, D, 8)
+    expect("BSM_E_ALIGN", mix, A + 8, B, D, 8)
+    expect("BSM_E_ALIAS", mix, A, A + 16, D, 64)
+    bsm.bsm_debug_stream_mix_bf16(0, 0, 0, 0, stream=0)           # n == 0: no-op
+    loop = lambda *x: bsm.bsm_debug_mfma_loop(*x, stream=0)
+    expect("BSM_E_DTYPE", loop, "f16", 4, 4, D)
+    expect("BSM_E_SHAPE", loop, "bf16", 0, 4, D)
+    expect("BSM_E_SHAPE", loop, "e4m3", 4, (1 << 20) + 1, D)
+    expect("BSM_E_NULL", loop, "e2m1", 4, 4, 0)
+    expect("BSM_E_ALIGN", loop, "bf16", 4, 4, D + 2)
     rows, kdim = bsm.bsm_debug_fragment_shape()
     expect("BSM_E_SHAPE", bsm.bsm_debug_fragments, A, rows, kdim + 16, "k", B, 0)
     expect("BSM_E_MAJOR", bsm.bsm_debug_fragments, A, rows, kdim, "n", B, 0)

@@ -52,6 +52,16 @@ def gemm_f16_128(seed: int = 0, M: int = 128, N: int = 128, K: int = 64):
             "a_major": "k", "b_major": "k", "accum": 0, "neg_a": 0, "neg_b": 0, "dtype": "f16"}
 
 
+def quarter_grid_f16(seed: int = 0, shapes=((128, 64), (64, 64))):
+    """fp16 bit arrays, one per shape in order from one generator, of values on the grid
+    {-1, -3/4, ..., 3/4, 1} drawn uniformly (the operands of the 128x64x64 example GEMM that
+    "tcgen05.mma", Example: four K16 issues, runs with seed 0). Every product is a multiple of
+    1/16 and every K-sum of 64 of them is below 2^6, so each is exact in float32."""
+    rng = np.random.default_rng(seed)
+    quarter = np.float16(0.25)
+    return [(rng.integers(low=-4, high=5, size=sh).astype(np.float16) * quarter).view(np.uint16) for sh in shapes]
+
+
 def add_one_tile():
     return np.arange(768, dtype=np.float32).reshape(2, 32, 3, 4)
 

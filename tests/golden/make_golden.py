@@ -11,21 +11,40 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
+def fragment_words(mats, trans):
+    """The register image of one ldmatrix issue over n 8x8 b16 matrices ("ldmatrix / stmatrix",
+    Address providers and result owners; Transpose and stores): lane 4j + w owns word w of row
+    j of each matrix, i.e. halves (2w, 2w + 1) of row j, taken from the matrix or, with .trans,
+    from its transpose. Returns (32 lanes, n) uint32 words, low half first."""
+    n = mats.shape[0]
+    out = np.zeros((32, n), np.uint64)
+    for i in range(n):
+        src = mats[i].T if trans else mats[i]
+        for lane in range(32):
+            row, word = divmod(lane, 4)
+            out[lane, i] = int(src[row, 2 * word]) | (int(src[row, 2 * word + 1]) << 16)
+    return out
+
+
 def ldmatrix_x2():
-    # "ldmatrix / stmatrix", Examples (interleaved shared rows and register slots
-    # 0, 2, 8, 10): x = arange(128) as (16,4,2) uint32; every slot holds the sentinel
-    # 4294966519 except slot 8k+2m of lane l, which holds x[2(l//4)+m, l%4, k].
-    x = np.arange(128, dtype=np.uint64).reshape(16, 4, 2)
-    exp = np.full((32, 12), 4294966519, dtype=np.uint64)
-    for lane in range(32):
-        for k in range(2):
-            for m in range(2):
-                exp[lane, 8 * k + 2 * m] = x[2 * (lane // 4) + m, lane % 4, k]
+    # "ldmatrix / stmatrix", Examples (interleaved shared rows and register slots 0, 2, 8, 10):
+    # the data are 128 consecutive uint32 values in a (16, 4, 2) shared tensor; issue k reads the
+    # two matrices m = 0, 1 whose eight rows are the 16-byte rows (2r + m, :, k), and the
+    # register layout (2, 2, 8, 4):(8, 2, 4@lane, 1@lane) places matrix m of issue k in slot
+    # 8k + 2m. Every other slot keeps the sentinel 4294966519 (int32 -777).
+    x = np.arange(128, dtype=np.uint32).reshape(16, 4, 2)
+    halves = x.view(np.uint16).reshape(16, 4, 2, 2)           # [row, word, issue, half]
+    slots = np.full((32, 12), 4294966519, dtype=np.uint64)
+    for k in range(2):
+        mats = np.stack([np.stack([halves[2 * r + m, :, k, :].reshape(8) for r in range(8)]) for m in range(2)])
+        words = fragment_words(mats, trans=False)
+        for m in range(2):
+            slots[:, 8 * k + 2 * m] = words[:, m]
     hdr = ("ldmatrix / stmatrix -- Examples: interleaved shared rows and register slots 0, 2, 8, 10.\n"
            "Input x = arange(128, uint32).reshape(16,4,2) in shared layout (16,4,2):(8,1,128);\n"
            "two ldmatrix.x2 issues. Rows: lanes 0..31; columns: the 12 register slots.\n"
            "Sentinel 4294966519 (int32 -777) marks slots the instruction must not touch.")
-    np.savetxt(os.path.join(HERE, "ldmatrix_x2_expected.txt"), exp, fmt="%d", header=hdr)
+    np.savetxt(os.path.join(HERE, "ldmatrix_x2_expected.txt"), slots, fmt="%d", header=hdr)
 
 
 def tma_two_box():

@@ -24,11 +24,11 @@ def half_vals(bits, dt):
 
 
 def test_pages_tcgen05_example_exact(O):
-    """tcgen05.mma, Example: 128x64x64, inputs integers(-4,5)/4 fp16, D = a @ b.T."""
-    rng = np.random.default_rng(0)
-    a = (rng.integers(-4, 5, (128, 64)) / 4).astype(np.float16)
-    b = (rng.integers(-4, 5, (64, 64)) / 4).astype(np.float16)
-    ref, bound = O.gemm(128, 64, 64, "f16", a.view(np.uint16), 64, "k", b.view(np.uint16), 64, "k")
+    """The example GEMM of "tcgen05.mma" (Example: four K16 issues): M = 128, N = K = 64, fp16
+    operands on the quarter grid from seed 0, D = A B^T; against numpy float64."""
+    ab, bb = W.quarter_grid_f16(0)
+    a, b = ab.view(np.float16), bb.view(np.float16)
+    ref, bound = O.gemm(128, 64, 64, "f16", ab, 64, "k", bb, 64, "k")
     exp = a.astype(np.float64) @ b.astype(np.float64).T
     assert np.array_equal(ref, exp)
     assert np.array_equal(bound, np.abs(a.astype(np.float64)) @ np.abs(b.astype(np.float64)).T)

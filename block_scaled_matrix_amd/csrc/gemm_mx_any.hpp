@@ -385,11 +385,18 @@ struct Conv {
   }
 };
 
-// Scale bits (code << 23) of this lane's 32-K block in step S: byte 2S + h of the tile's word.
-template <int S>
+// Scale operand of this lane's 32-K block in step S: byte 2S + h of the tile's word rotated into
+// bits 23..30, a float's exponent field (rotate right by 8 (2S + h) + 9 = 16S + sh + 9, mod 32).
+// The 2-element conversions read only that field (probed: sign and mantissa bits are ignored),
+// so one rotate is the whole operand; the 32-element 6-bit conversions get the field alone.
+template <int C, int S>
 __device__ __forceinline__ void scale_bits(const uint32_t (&s)[4], int sh, uint32_t (&o)[4]) {
+  const uint32_t r = (uint32_t)(16 * S + 9 + sh) & 31u;
 #pragma unroll
-  for (int t = 0; t < 4; t++) o[t] = ((s[t] >> (sh + 16 * S)) & 0xFFu) << 23;
+  for (int t = 0; t < 4; t++) {
+    const uint32_t x = __builtin_amdgcn_alignbit(s[t], s[t], r);
+    o[t] = fmt_bits(C) == 6 ? (x & 0x7F800000u) : x;
+  }
 }
 
 __device__ __forceinline__ f32x16 mfma_bf16(const uint4& b, const uint4& a, f32x16 c) {
@@ -397,14 +404,14 @@ __device__ __forceinline__ f32x16 mfma_bf16(const uint4& b, const uint4& a, f32x
                                                  0);
 }
 
-// Part 0 of a step for both operands (the prefetching formats), from raw fragments and the
-// scale words of the step's tile.
+// The scale operands of a step (xa, xb) and part 0 of its fragments for both operands (the
+// prefetching formats), from raw fragments and the scale words of the step's tile.
 template <int CA, int CB, int S>
 __device__ __forceinline__ void prepare_first(Conv<CA>& ca, Conv<CB>& cb, i32x8 (&fa)[4], i32x8 (&fb)[4],
-                                              const uint32_t (&sa)[4], const uint32_t (&sb)[4], int sh) {
-  uint32_t xa[4], xb[4];
-  scale_bits<S>(sa, sh, xa);
-  scale_bits<S>(sb, sh, xb);
+                                              const uint32_t (&sa)[4], const uint32_t (&sb)[4], int sh,
+                                              uint32_t (&xa)[4], uint32_t (&xb)[4]) {
+  scale_bits<CA, S>(sa, sh, xa);
+  scale_bits<CB, S>(sb, sh, xb);
 #pragma unroll
   for (int t = 0; t < 4; t++) {
     if constexpr (Conv<CA>::PREFETCH) ca.template prepare<0>(fa, xa, t);
@@ -414,30 +421,27 @@ __device__ __forceinline__ void prepare_first(Conv<CA>& ca, Conv<CB>& cb, i32x8 
 
 // The 64 bf16 MFMAs of 64-K step S (MFMA j of each accumulator covers elements 8j..8j+7 of
 // the lanes' 32), j-major so that the conversions of part j + 1 go out between part j's
-// MFMAs. Part 0 of this step is ready in ca / cb (prefetching formats); with NEXT, part 0 of
-// the next step (raw fragments nfa / nfb, step index SN of the tile whose scale words are
-// nsa / nsb) is converted between part 3's MFMAs. nfa, nfb, nsa and nsb are read only then,
-// so side work of this step may still be filling them. side(i) (i = 0..15) runs after every
-// fourth MFMA, as mfma16 runs it after every one.
+// MFMAs. The step's scale operands are in xa / xb and part 0 of its fragments in ca / cb
+// (prefetching formats). With NEXT, part 3 replaces xa / xb with the next step's (step index
+// SN of the tile whose scale words are nsa / nsb) and converts that step's part 0 (raw
+// fragments nfa / nfb) between its MFMAs; nfa, nfb, nsa and nsb are read only then, so side
+// work of this step may still be filling them. side(i) (i = 0..15) runs after every fourth
+// MFMA, as mfma16 runs it after every one.
 template <int CA, int CB, int S, bool NEXT, int SN, typename Side>
 __device__ __forceinline__ void mfma64_bf(Conv<CA>& ca, Conv<CB>& cb, i32x8 (&fa)[4], i32x8 (&fb)[4],
-                                          const uint32_t (&sa)[4], const uint32_t (&sb)[4], i32x8 (&nfa)[4],
-                                          i32x8 (&nfb)[4], const uint32_t (&nsa)[4], const uint32_t (&nsb)[4], int sh,
+                                          uint32_t (&xa)[4], uint32_t (&xb)[4], i32x8 (&nfa)[4], i32x8 (&nfb)[4],
+                                          const uint32_t (&nsa)[4], const uint32_t (&nsb)[4], int sh,
                                           f32x16 (&acc)[4][4], Side side) {
-  uint32_t xa[4], xb[4];
-  scale_bits<S>(sa, sh, xa);
-  scale_bits<S>(sb, sh, xb);
 #pragma unroll
   for (int t = 0; t < 4; t++) {
     if constexpr (!Conv<CA>::PREFETCH) ca.template prepare<0>(fa, xa, t);
     if constexpr (!Conv<CB>::PREFETCH) cb.template prepare<0>(fb, xb, t);
   }
-  uint32_t nxa[4], nxb[4];
   auto part = [&](auto jc) {
     constexpr int J = decltype(jc)::value;
     if constexpr (J == 3 && NEXT) {
-      scale_bits<SN>(nsa, sh, nxa);
-      scale_bits<SN>(nsb, sh, nxb);
+      scale_bits<CA, SN>(nsa, sh, xa);
+      scale_bits<CB, SN>(nsb, sh, xb);
     }
 #pragma unroll
     for (int i = 0; i < 16; i++) {
@@ -451,9 +455,9 @@ __device__ __forceinline__ void mfma64_bf(Conv<CA>& ca, Conv<CB>& cb, i32x8 (&fa
           else ca.template prepare<J + 1>(fa, xa, i >> 1);
         } else if constexpr (NEXT) {
           if (i & 1) {
-            if constexpr (Conv<CB>::PREFETCH) cb.template prepare<0>(nfb, nxb, i >> 1);
+            if constexpr (Conv<CB>::PREFETCH) cb.template prepare<0>(nfb, xb, i >> 1);
           } else {
-            if constexpr (Conv<CA>::PREFETCH) ca.template prepare<0>(nfa, nxa, i >> 1);
+            if constexpr (Conv<CA>::PREFETCH) ca.template prepare<0>(nfa, xa, i >> 1);
           }
         }
       }
@@ -569,9 +573,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   static_assert(DPW <= 32, "at most two copies per MFMA slot of step 1");
   // Multiply the partial last K tile, held in stage st with its scale words (one per row,
   // A's then B's) at `scales`: step 1's fragment reads go out between step 0's MFMAs.
-  // Converted fragments of the exact-products route (unused on the other route).
+  // Converted fragments and scale operands of the exact-products route (unused on the other).
   Conv<CA> cva;
   Conv<CB> cvb;
+  uint32_t xsa[4], xsb[4];
   auto multiply = [&](const uint8_t* st, const uint8_t* scales) {
     uint32_t sa[4], sb[4];
     i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
@@ -585,10 +590,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
       }
     };
     if constexpr (BF) {
-      prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh);
-      mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, sa, sb, fa1, fb1, sa, sb, sh, acc, reads1);
+      prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh, xsa, xsb);
+      mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, xsa, xsb, fa1, fb1, sa, sb, sh, acc, reads1);
       gemm::lds_barrier();
-      mfma64_bf<CA, CB, 1, false, 0>(cva, cvb, fa1, fb1, sa, sb, fa0, fb0, sa, sb, sh, acc, [](int) {});
+      mfma64_bf<CA, CB, 1, false, 0>(cva, cvb, fa1, fb1, xsa, xsb, fa0, fb0, sa, sb, sh, acc, [](int) {});
     } else {
       mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, reads1);
       gemm::lds_barrier();
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     read_scales_ring(lds + L::RING, 0, 0, wa, lane, sa);
     read_scales_ring(lds + L::RING + 4096, 1, 0, wb, lane, sb);
     read_frags<CA, CB, AMN, BMN, BF, 0>(lds, lds + PA::TILE, wa, wb, lane, fa0, fb0);
-    if constexpr (BF) prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh);
+    if constexpr (BF) prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh, xsa, xsb);
     int cur = 0;                             // kt % NST
     for (int kt = 0; kt < nfull; kt++) {
       const uint8_t* st = lds + cur * L::STAGE;
@@ -656,8 +661,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
       if constexpr (BF) {
         // step 0 converts step 1's first part from fa1 / fb1 (read by side0), step 1 the next
         // tile's from fa0 / fb0 and its scale words na / nb (read by side1)
-        mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, sa, sb, fa1, fb1, sa, sb, sh, acc, side0);
-        mfma64_bf<CA, CB, 1, true, 0>(cva, cvb, fa1, fb1, sa, sb, fa0, fb0, na, nb, sh, acc, side1);
+        mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, xsa, xsb, fa1, fb1, sa, sb, sh, acc, side0);
+        mfma64_bf<CA, CB, 1, true, 0>(cva, cvb, fa1, fb1, xsa, xsb, fa0, fb0, na, nb, sh, acc, side1);
       } else {
         mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, side0);
         mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, side1);

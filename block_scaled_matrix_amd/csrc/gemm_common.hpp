@@ -45,8 +45,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // tile count divides by 8 the ids are renumbered so that each XCD owns one contiguous
 // range of tiles, then walked in groups of GROUP_M tile rows (column-major inside a
 // group) so that the workgroups resident on one XCD share A and B panels in its L2.
+// GROUP_M 4 measured best against 2, 8 and 16 on the 8192- and 16384-wide block-scaled and
+// bf16 GEMMs (BSM_GROUP_M overrides it at build time for such sweeps).
+#ifndef BSM_GROUP_M
+#define BSM_GROUP_M 4
+#endif
 __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 4;
+  constexpr int GROUP_M = BSM_GROUP_M;
   const int total = tiles_m * tiles_n;
   int lid = pid;
   if ((total & 7) == 0) lid = (pid & 7) * (total >> 3) + (pid >> 3);

@@ -21,7 +21,8 @@
 // LDS per copy) into three stages (two when an 8-bit operand meets a 6-bit one: three do
 // not fit), the copy of tile kt + NST issued as soon as every wave is done reading tile kt,
 // so the copies have NST - 1 K tiles of multiplies to land in (one K tile of 6- or 4-bit
-// operands is only 1024 MFMA cycles). Each row's 16-byte chunks are permuted (by the
+// operands is only 1024 MFMA cycles); on the scaled-MFMA route with three stages half of
+// them wait for the next step, which spreads the copies over the whole K tile. Each row's 16-byte chunks are permuted (by the
 // copies' global addresses) so that the 16 rows one 16-lane group reads at one offset fall
 // in distinct banks: chunk c of row r sits at c ^ ((r >> 1) & 7) for 128-byte rows,
 // (c + ((r >> 3) & 1)) % 6 for 96-byte rows and c ^ ((r >> 2) & 3) for 64-byte rows. The
@@ -571,6 +572,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     else copy(kb, stage, d - 2);
   };
   static_assert(DPW <= 32, "at most two copies per MFMA slot of step 1");
+  // With three stages on the scaled-MFMA route a batch goes out in two halves: its scale
+  // copies and the first DH data copies at every other MFMA slot of step 1 of iteration b,
+  // the other DD - DH at every other slot of step 0 of iteration b + 1 (its stage is still
+  // free then), so that the four waves' copies reach the shared copy path about one per 16
+  // cycles instead of all within one step (measured: 6-bit pairs 4-8% faster). With two
+  // stages the whole batch goes out in step 1 (a K tile would otherwise have only half a
+  // tile of lead), and so it does on the exact-products route, whose K tiles last twice as
+  // long (the split made it 1.5% slower).
+  constexpr bool SPLIT = NST >= 3 && !BF;
+  constexpr int DH = SPLIT ? DD / 2 : DD;
+  static_assert(!SPLIT || (2 + DH <= 8 && DD - DH <= 8), "one copy per two MFMA slots");
   // Multiply the partial last K tile, held in stage st with its scale words (one per row,
   // A's then B's) at `scales`: step 1's fragment reads go out between step 0's MFMAs.
   // Converted fragments and scale operands of the exact-products route (unused on the other).
@@ -624,8 +636,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
 #pragma unroll
     for (int i = 0; i < NST; i++)
 #pragma unroll
-      for (int d = 0; d < DD; d++) copy(min(i, nfull - 1), i, d);
-    gemm::stage_barrier<(NST - 1) * DD>();   // the scales and tile 0 have landed
+      for (int d = 0; d < (i == NST - 1 ? DH : DD); d++) copy(min(i, nfull - 1), i, d);
+    // the scales and tile 0 have landed (tiles 1 .. NST - 2 and the first DH copies of tile
+    // NST - 1 may still fly; the rest of that tile goes out in iteration 0, as in every one)
+    gemm::stage_barrier<(NST - 2) * DD + DH>();
     read_scales_ring(lds + L::RING, 0, 0, wa, lane, sa);
     read_scales_ring(lds + L::RING + 4096, 1, 0, wb, lane, sb);
     read_frags<CA, CB, AMN, BMN, BF, 0>(lds, lds + PA::TILE, wa, wb, lane, fa0, fb0);
@@ -636,10 +650,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
       const int nxt = cur + 1 == NST ? 0 : cur + 1;
       const uint8_t* nst = lds + nxt * L::STAGE;
       const int knext = min(kt + NST, nfull - 1);
+      // the second half of the previous iteration's batch: tile kt - 1 + NST into its stage
+      const int kprev = min(kt - 1 + NST, nfull - 1), prv = cur == 0 ? NST - 1 : cur - 1;
       auto side0 = [&](int i) {
         if (i < 8) {
           if (i & 1) fb1[i >> 1] = read_frag<CB, BMN, BF>(st + PA::TILE, wb, i >> 1, 1, lane);
           else fa1[i >> 1] = read_frag<CA, AMN, BF>(st, wa, i >> 1, 1, lane);
+        }
+        if constexpr (SPLIT) {
+          if ((i & 1) && (i >> 1) < DD - DH) copy(kprev, prv, DH + (i >> 1));
         }
       };
       auto side1 = [&](int i) {
@@ -655,8 +674,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
           if (i & 1) fb0[i >> 1] = read_frag<CB, BMN, BF>(nst + PA::TILE, wb, i >> 1, 0, lane);
           else fa0[i >> 1] = read_frag<CA, AMN, BF>(nst, wa, i >> 1, 0, lane);
         }
-        if (i < DPW) batch_copy(kt, knext, cur, i);
-        if (i + 16 < DPW) batch_copy(kt, knext, cur, i + 16);   // two 8-bit operands: 18 copies
+        if constexpr (SPLIT) {
+          if (!(i & 1) && (i >> 1) < 2 + DH) batch_copy(kt, knext, cur, i >> 1);
+        } else {
+          if (i < DPW) batch_copy(kt, knext, cur, i);
+          if (i + 16 < DPW) batch_copy(kt, knext, cur, i + 16);   // two 8-bit operands: 18 copies
+        }
       };
       if constexpr (BF) {
         // step 0 converts step 1's first part from fa1 / fb1 (read by side0), step 1 the next

@@ -307,6 +307,32 @@ def test_block_scale_exact_sums_bit_exact(O, fmt):
         assert np.array_equal(D[:, :N], ref.astype(np.float32))
 
 
+# Scale codes bounding the range in which every scaled 8-bit element is exact in bf16, its
+# subnormals included (the exact-products route forms element * 2^(code - 127) in bf16).
+SCALE_EDGES = {"e4m3": (3, 246), "e5m2": (10, 239)}
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2")])
+def test_block_scale_scale_range_edges(O, a_fmt, b_fmt):
+    """Every A block at the top scale code of its format and every B block at the bottom one,
+    then the reverse: the largest and the smallest (subnormal) scaled elements the route
+    claims to form exactly, with products inside float32's range. Strict bound against the
+    oracle, ragged K included."""
+    for i, (M, N, K) in enumerate([(300, 260, 288), (256, 256, 1056)]):
+        for top_a in (True, False):
+            g = mx_case(a_fmt, 90 + i, M, N, K, b_fmt=b_fmt)
+            (alo, ahi), (blo, bhi) = SCALE_EDGES[a_fmt], SCALE_EDGES[b_fmt]
+            g["SFA"][:] = ahi if top_a else alo
+            g["SFB"][:] = blo if top_a else bhi
+            say("mx scale edges", a_fmt, b_fmt, M, N, K, "A top" if top_a else "B top")
+            D = run_mx(M, N, K, a_fmt, g, b_fmt=b_fmt)
+            ref, bound = O.gemm_block_scale(M, N, K, a_fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], b_fmt, g["B"],
+                                            g["ldb"], g["SFB"], g["ld_sfb"])
+            assert np.isfinite(ref).all() and (bound > 0).any()
+            nb, worst = check_strict(O, D, ref, bound, name=f"{a_fmt} x {b_fmt} scale-range edges")
+            assert nb == 0, (M, N, K, top_a, worst)
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 def test_block_scale_nan_scale_poisons_row(O, fmt):
     M, N, K = 64, 64, 128

@@ -1,6 +1,6 @@
 // oracle.cpp - reference CPU implementation of the block-scaled tile-matrix hot path.
 //
-// TEST INFRASTRUCTURE ONLY. This file is the checker the HIP library is measured
+// TEST INFRASTRUCTURE ONLY. This file is the reference the HIP library is compared
 // against. Only the test-suite, the smoke check and the CPU-baseline leg of the
 // benchmark may load it. It shares no code, header, table or constant with the
 // library under block_scaled_matrix_amd/: it is plain, slow, serial-per-output C++

@@ -242,7 +242,7 @@ def test_block_scale_points_match_full(O):
     assert np.array_equal(pr, ref[pm, pn]) and np.array_equal(pb, bound[pm, pn])
 
 
-# ----------------------------------------------------------------------------- checker
+# ----------------------------------------------------------------------------- comparison (check_gemm)
 def test_check_gemm_flags_planted_errors(O):
     rng = np.random.default_rng(0)
     ref = rng.standard_normal((8, 8))

@@ -125,6 +125,31 @@ def test_dense_accum_zero_A_and_determinism(O):
     assert np.array_equal(Dn[:, :N], -Dp[:, :N])
 
 
+@pytest.mark.parametrize("amaj,bmaj", [("k", "k"), ("k", "n"), ("m", "k"), ("m", "n")])
+def test_dense_accum_long_k(O, amaj, bmaj):
+    """Accumulation with 32 or more whole K tiles of 64, where D joins the accumulators inside
+    the K loop (one 32 x 32 block per two or more K tiles): ragged M and N edges, a ragged K
+    tail, both signs; then A = 0, where D must come back bit for bit under either sign."""
+    rng = np.random.default_rng([7, ord(amaj), ord(bmaj)])
+    for i, (M, N, K) in enumerate([(300, 260, 2088), (256, 512, 2048), (130, 300, 4112)]):
+        A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", amaj, bmaj)
+        d0 = rng.standard_normal((M, N)).astype(np.float32)
+        neg_a, neg_b = i & 1, (i >> 1) & 1
+        say("dense accum long K", amaj, bmaj, M, N, K, neg_a, neg_b)
+        D = run_dense(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj, d0, neg_a, neg_b, 1)
+        ref, bound = O.gemm(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj, d0, N, neg_a, neg_b, 1)
+        nb, first, worst = O.check_gemm(D, ref, bound, TOL_DENSE)
+        assert nb == 0, (M, N, K, first, worst)
+        assert np.isnan(D[:, N:]).all()
+    M, N, K = 300, 260, 2048
+    A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", amaj, bmaj)
+    d0 = rng.standard_normal((M, N)).astype(np.float32)
+    for neg_a in (0, 1):
+        say("dense accum long K with A = 0", amaj, bmaj, neg_a)
+        D = run_dense(M, N, K, "bf16", np.zeros_like(A), lda, amaj, B, ldb, bmaj, d0, neg_a, 0, 1)
+        assert np.array_equal(D[:, :N], d0)
+
+
 def test_dense_k_zero():
     say("dense K = 0")
     D = run_dense(5, 6, 0, "bf16", np.zeros((5, 8), np.uint16), 8, "k", np.zeros((6, 8), np.uint16), 8, "k")

@@ -98,6 +98,75 @@ def test_box_load_store_vs_oracle(O, dtype, rank):
         assert np.array_equal(host(dst, NPDT[dtype], mem.shape), exp)
 
 
+# The contract's limits: box extents up to 256, element strides up to 8 (outer dimensions),
+# an inner box of 16 << s bytes when swizzled, and an unswizzled (256, 256) bf16 box whose
+# 128 KiB image is the largest the general kernel stages in LDS.
+LIMIT_CASES = [
+    ("bf16", (1000, 300), (256, 256), (1, 1), 0),
+    ("f32", (2100, 40), (256, 32), (8, 1), 3),
+    ("u8", (40, 9, 600), (5, 256, 64), (8, 1, 1), 2),
+    ("e4m3", (3, 4, 5, 6, 300), (2, 3, 2, 3, 256), (2, 1, 3, 1, 1), 0),
+    ("f16", (7, 5, 4, 33, 70), (4, 4, 4, 8, 64), (8, 2, 8, 4, 1), 3),
+]
+
+
+@pytest.mark.parametrize("dtype,dims,box,estr,swz", LIMIT_CASES)
+def test_box_limits_vs_oracle(O, dtype, dims, box, estr, swz):
+    """Boxes at the contract's limits, loaded at coordinates inside, straddling and past the
+    tensor (zero and, for float formats, NaN fill), then stored and add-reduced back."""
+    rng = np.random.default_rng(sum(dims) + 7 * sum(box))
+    esz = bsm.ESIZE[dtype]
+    rank = len(dims)
+    pitch_b = (dims[-1] * esz + 15) // 16 * 16 + 16
+    mem = rng.integers(0, 2 ** (8 * esz), dims[:-1] + (pitch_b // esz,), dtype=np.uint64).astype(NPDT[dtype])
+    if dtype in ("f32", "f16", "bf16"):   # finite values, so that the reduce-add sums are defined
+        mem = W.to_half_bits(rng.standard_normal(mem.shape).astype(np.float32), dtype) if esz == 2 else \
+            rng.standard_normal(mem.shape).astype(np.float32).view(np.uint32)
+    strides = [mem.strides[i] for i in range(rank)]
+    ext = O.image_extents(box, estr)
+    coords = np.array([[0] * rank,
+                       [d - (b - 1) * e // 2 for d, b, e in zip(dims, box, estr)],
+                       [-(b - 1) * e // 2 for b, e in zip(box, estr)],
+                       [d + 1 for d in dims]], np.int32)
+    nb = len(coords)
+    fill = 1 if dtype in ("f32", "f16", "bf16", "e4m3") else 0
+    say("box limits", dtype, dims, box, estr, swz, fill, "image", int(np.prod(ext)) * esz)
+    stride = O.image_stride(dtype, box, estr, swz)
+    bd = bsm.box_desc(box, estr, swz, fill)
+    assert bsm.bsm_image_stride(bd, dtype) == stride
+    dsrc = dev(mem)
+    dimg = dev_like(nb * stride, 0xA5)
+    dco = torch.from_numpy(coords.reshape(-1)).cuda()
+    bsm.bsm_tile_box_load(bsm.tensor_desc(dsrc, dtype, dims, strides), bd, dco, nb, dimg)
+    got = host(dimg, np.uint8).reshape(nb, stride)
+    nbytes = int(np.prod(ext)) * esz
+    written = np.zeros(stride, bool)
+    written[[O.swizzle(o, swz) for o in range(nbytes)]] = True
+    for t in range(nb):
+        exp = O.box_load(mem, dtype, dims, strides, box, estr, coords[t], swz, fill)
+        assert np.array_equal(got[t][written], exp[written]), (t, coords[t])
+        assert (got[t][~written] == 0xA5).all()
+    # store every image back into a sentinel tensor (clipped; overlapping boxes carry the same
+    # source values there), then reduce-add the straddling box's image into a copy of the
+    # source (one box: overlapping reduce-adds would race)
+    say("box limits store", dtype)
+    sent = np.full_like(mem, 0x3C if esz == 1 else 0x3C00)
+    dst = dev(sent)
+    bsm.bsm_tile_box_store(bsm.tensor_desc(dst, dtype, dims, strides), bd, dco, nb, dimg, 0)
+    exp = sent.copy()
+    for t in range(nb):
+        O.box_store(exp, dtype, dims, strides, box, estr, coords[t], got[t], swz, 0)
+    assert np.array_equal(host(dst, NPDT[dtype], mem.shape), exp)
+    if dtype in ("f32", "f16", "bf16"):
+        say("box limits reduce-add", dtype)
+        dacc = dev(mem)
+        d1 = torch.from_numpy(coords[1].copy()).cuda()
+        bsm.bsm_tile_box_store(bsm.tensor_desc(dacc, dtype, dims, strides), bd, d1, 1, dimg[stride:2 * stride], 1)
+        exp = mem.copy()
+        O.box_store(exp, dtype, dims, strides, box, estr, coords[1], got[1], swz, 1)
+        assert np.array_equal(host(dacc, NPDT[dtype], mem.shape), exp)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_box_reduce_add_vs_oracle(O, dtype):
     rng = np.random.default_rng(77 + bsm.DTYPE[dtype])

@@ -150,6 +150,22 @@ def test_dense_accum_long_k(O, amaj, bmaj):
         assert np.array_equal(D[:, :N], d0)
 
 
+@pytest.mark.parametrize("M,N,K,amaj,bmaj", [(1, 300, 131112, "k", "n"), (300, 1, 131072, "m", "k"),
+                                             (3, 5, 262144, "k", "k")])
+def test_dense_long_k_thin(O, M, N, K, amaj, bmaj):
+    """Degenerate widths (one row or column: every workgroup but one masked away) with K in the
+    hundreds of thousands (2048 to 4096 K tiles, one with a ragged tail), accumulating."""
+    rng = np.random.default_rng(K + M)
+    A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", amaj, bmaj)
+    d0 = rng.standard_normal((M, N)).astype(np.float32)
+    say("dense long K thin", M, N, K, amaj, bmaj)
+    D = run_dense(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj, d0, 1, 0, 1)
+    ref, bound = O.gemm(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj, d0, N, 1, 0, 1)
+    nb, first, worst = O.check_gemm(D, ref, bound, TOL_DENSE)
+    assert nb == 0, (first, worst)
+    assert np.isnan(D[:, N:]).all()
+
+
 def test_dense_k_zero():
     say("dense K = 0")
     D = run_dense(5, 6, 0, "bf16", np.zeros((5, 8), np.uint16), 8, "k", np.zeros((6, 8), np.uint16), 8, "k")
@@ -409,6 +425,20 @@ def _window_pair(O, run, small_a, small_b):
     D = run(1, 1, 32, "e4m3", g)
     ref, _ = O.gemm_block_scale(1, 1, 32, "e4m3", A, 32, sf, 4, "e4m3", B, 32, sf, 4)
     return float(D[0, 0]), float(ref[0, 0])
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("e4m3", 1, 257, 131072), ("e2m1", 257, 1, 131104), ("e4m3", 2, 3, 262144)])
+def test_block_scale_long_k_thin(O, fmt, M, N, K):
+    """One row or column of output with 4096 to 8192 scale blocks per row (a ragged K tail for
+    E2M1): the exact-products route and the scaled MFMA over the longest K the tests run."""
+    g = mx_case(fmt, 31, M, N, K)
+    say("mx long K thin", fmt, M, N, K)
+    D = run_mx(M, N, K, fmt, g)
+    ref, bound = O.gemm_block_scale(M, N, K, fmt, g["A"], g["lda"], g["SFA"], g["ld_sfa"], fmt, g["B"], g["ldb"],
+                                    g["SFB"], g["ld_sfb"])
+    nb, worst = check_strict(O, D, ref, bound, name=f"{fmt} x {fmt} long K, one row or column")
+    assert nb == 0, worst
+    assert np.isnan(D[:, N:]).all()
 
 
 def test_e4m3_block_window_characterization(O):

@@ -471,6 +471,44 @@ __device__ __forceinline__ void mfma64_bf(Conv<CA>& ca, Conv<CB>& cb, i32x8 (&fa
   part(std::integral_constant<int, 3>{});
 }
 
+// All four parts (elements 8j .. 8j + 7, j < 4) of one fragment as bf16 times its scale.
+template <int C>
+__device__ __forceinline__ void cvt_whole(const i32x8& v, uint32_t sbits, uint4 (&o)[4]) {
+  if constexpr (fmt_bits(C) == 6) {
+    cvt_all6<C>(v, sbits, o);
+  } else {
+    o[0] = cvt_part<C, 0>(v, sbits);
+    o[1] = cvt_part<C, 1>(v, sbits);
+    o[2] = cvt_part<C, 2>(v, sbits);
+    o[3] = cvt_part<C, 3>(v, sbits);
+  }
+}
+
+// 64-K step S of the exact-products route with nothing in flight beside it, for the partial
+// last K tile: each A fragment converted once, each B fragment once per A fragment, the four
+// bf16 MFMAs of an accumulator in part order j = 0..3 as in mfma64_bf. Few registers live at
+// once, so this code, which runs once per tile, does not raise the whole kernel's register
+// pressure.
+template <int CA, int CB, int S>
+__device__ __forceinline__ void step_bf_plain(const i32x8 (&fa)[4], const i32x8 (&fb)[4], const uint32_t (&sa)[4],
+                                              const uint32_t (&sb)[4], int sh, f32x16 (&acc)[4][4]) {
+  uint32_t xa[4], xb[4];
+  scale_bits<CA, S>(sa, sh, xa);
+  scale_bits<CB, S>(sb, sh, xb);
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    uint4 pa[4];
+    cvt_whole<CA>(fa[mt], xa[mt], pa);
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+      uint4 pb[4];
+      cvt_whole<CB>(fb[nt], xb[nt], pb);
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[mt][nt] = mfma_bf16(pb[j], pa[j], acc[mt][nt]);
+    }
+  }
+}
+
 // The 16 MFMAs of 64-K step S (accumulator rows mt-major). The MFMA takes B first (its
 // format code and scales as src0); after the per-lane shift by 8 (l/32), op_sel byte 2S
 // holds the scale of the lane's 32-K block of this step. side(i) runs after MFMA i: the
@@ -589,27 +627,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   Conv<CA> cva;
   Conv<CB> cvb;
   uint32_t xsa[4], xsb[4];
+  // The partial last K tile, one step at a time with only that step's fragments live: the
+  // pipelined form of the loop, with two steps' fragments and the conversion buffers live at
+  // once, made the compiler spill the accumulators around it (a kilobyte of scratch per lane,
+  // written and read back on every tile, tail or not).
   auto multiply = [&](const uint8_t* st, const uint8_t* scales) {
     uint32_t sa[4], sb[4];
-    i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
     read_scales(scales, wa, lane, sa);
     read_scales(scales + 1024, wb, lane, sb);
-    read_frags<CA, CB, AMN, BMN, BF, 0>(st, st + PA::TILE, wa, wb, lane, fa0, fb0);
-    auto reads1 = [&](int i) {
-      if (i < 8) {
-        if (i & 1) fb1[i >> 1] = read_frag<CB, BMN, BF>(st + PA::TILE, wb, i >> 1, 1, lane);
-        else fa1[i >> 1] = read_frag<CA, AMN, BF>(st, wa, i >> 1, 1, lane);
-      }
-    };
-    if constexpr (BF) {
-      prepare_first<CA, CB, 0>(cva, cvb, fa0, fb0, sa, sb, sh, xsa, xsb);
-      mfma64_bf<CA, CB, 0, true, 1>(cva, cvb, fa0, fb0, xsa, xsb, fa1, fb1, sa, sb, sh, acc, reads1);
-      gemm::lds_barrier();
-      mfma64_bf<CA, CB, 1, false, 0>(cva, cvb, fa1, fb1, xsa, xsb, fa0, fb0, sa, sb, sh, acc, [](int) {});
-    } else {
-      mfma16<CA, CB, 0>(fa0, fb0, sa, sb, sh, acc, reads1);
-      gemm::lds_barrier();
-      mfma16<CA, CB, 1>(fa1, fb1, sa, sb, sh, acc, [](int) {});
+    {
+      i32x8 fa[4], fb[4];
+      read_frags<CA, CB, AMN, BMN, BF, 0>(st, st + PA::TILE, wa, wb, lane, fa, fb);
+      if constexpr (BF) step_bf_plain<CA, CB, 0>(fa, fb, sa, sb, sh, acc);
+      else mfma16<CA, CB, 0>(fa, fb, sa, sb, sh, acc, [](int) {});
+    }
+    {
+      i32x8 fa[4], fb[4];
+      read_frags<CA, CB, AMN, BMN, BF, 1>(st, st + PA::TILE, wa, wb, lane, fa, fb);
+      if constexpr (BF) step_bf_plain<CA, CB, 1>(fa, fb, sa, sb, sh, acc);
+      else mfma16<CA, CB, 1>(fa, fb, sa, sb, sh, acc, [](int) {});
     }
   };
 
@@ -729,8 +765,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     multiply(st, scales);
     __syncthreads();
   }
-  gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, a.accum != 0,
-                         a.ew_op, a.ew_scale, a.ew_bias);
+  // (accumulation as a constant in each branch: the fresh-D path then holds no registers for
+  // D's values, which made the compiler spill accumulators here)
+  if (a.accum)
+    gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, true, a.ew_op,
+                           a.ew_scale, a.ew_bias);
+  else
+    gemm::store_tile_lines(a.D, a.ldd, a.M, a.N, m0 + wa, n0 + wb, lane, sgn, acc, lds + 32768 * w, false, a.ew_op,
+                           a.ew_scale, a.ew_bias);
 }
 
 // Launch of one (A format, B format, major orders) instance on the route the call asks for:

@@ -621,16 +621,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   constexpr bool SPLIT = NST >= 3 && !BF;
   constexpr int DH = SPLIT ? DD / 2 : DD;
   static_assert(!SPLIT || (2 + DH <= 8 && DD - DH <= 8), "one copy per two MFMA slots");
-  // Multiply the partial last K tile, held in stage st with its scale words (one per row,
-  // A's then B's) at `scales`: step 1's fragment reads go out between step 0's MFMAs.
   // Converted fragments and scale operands of the exact-products route (unused on the other).
   Conv<CA> cva;
   Conv<CB> cvb;
   uint32_t xsa[4], xsb[4];
-  // The partial last K tile, one step at a time with only that step's fragments live: the
-  // pipelined form of the loop, with two steps' fragments and the conversion buffers live at
-  // once, made the compiler spill the accumulators around it (a kilobyte of scratch per lane,
-  // written and read back on every tile, tail or not).
+  // Multiply the partial K tile, held in stage st with its scale words (one per row, A's then
+  // B's) at `scales`, one step at a time with only that step's fragments live (the pipelined
+  // form of the loop, with two steps' fragments and the conversion buffers live at once, made
+  // the compiler spill accumulators around it).
   auto multiply = [&](const uint8_t* st, const uint8_t* scales) {
     uint32_t sa[4], sb[4];
     read_scales(scales, wa, lane, sa);
@@ -649,6 +647,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     }
   };
 
+  // The partial K tile past the whole ones (K not a multiple of 128), loaded with zeros past
+  // K, goes first, into the zeroed accumulators. Multiplied after the loop, it joined the
+  // no-tail path just before the epilogue, and the compiler kept the accumulators in scratch
+  // across that join on every tile, tail or not (for an 8192 x 8192 fp32 D, 144 MiB more
+  // written per launch than D itself, and read back).
+  if (a.K % KT) {
+    uint4 va[PA::LPC], vb[PB::LPC];
+    uint8_t* st = lds;
+    if constexpr (AMN) {
+      load_chunks_tail_mn<CA>(A, lda_b, mlima, nfull, a.K, q, va);
+    } else {
+      uint32_t roa[PA::LPC];
+      row_offsets<CA>(lda_b, rows_a, q, roa);
+      load_chunks_tail<CA>(A, roa, nfull, ka, q, va);
+    }
+    if constexpr (BMN) {
+      load_chunks_tail_mn<CB>(B, ldb_b, mlimb, nfull, a.K, q, vb);
+    } else {
+      uint32_t rob[PB::LPC];
+      row_offsets<CB>(ldb_b, rows_b, q, rob);
+      load_chunks_tail<CB>(B, rob, nfull, kb, q, vb);
+    }
+    const uint32_t wsa = mask_scale_word(load_scale_word(a.SFA, a.ld_sfa, m0, a.M, q, nfull), nfull, nblk);
+    const uint32_t wsb = mask_scale_word(load_scale_word(a.SFB, a.ld_sfb, n0, a.N, q, nfull), nfull, nblk);
+    store_chunks<CA, AMN>(st, q, va);
+    store_chunks<CB, BMN>(st + PA::TILE, q, vb);
+    uint8_t* scales = lds + L::RING;          // one word per row: A's 256, then B's
+    *(BSM_LDS uint32_t*)(scales + 4 * q) = wsa;
+    *(BSM_LDS uint32_t*)(scales + 1024 + 4 * q) = wsb;
+    __syncthreads();
+    multiply(st, scales);
+    __syncthreads();
+  }
   // Whole K tiles; tile kt lives in stage kt % NST. One barrier per tile, at the start of
   // its step 1: every wave has then read the stage's step-1 fragments (issued between the
   // step-0 MFMAs) and the copies of tile kt + 1 have landed, so the copies of tile kt + NST
@@ -736,35 +767,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   }
   gemm::wait_dma();                          // the repeated copies too, before LDS is reused
   __syncthreads();
-  // A partial last K tile (K not a multiple of 128), loaded with zeros past K.
-  if (a.K % KT) {
-    uint4 va[PA::LPC], vb[PB::LPC];
-    uint8_t* st = lds;                       // every copy has landed: any stage will do
-    if constexpr (AMN) {
-      load_chunks_tail_mn<CA>(A, lda_b, mlima, nfull, a.K, q, va);
-    } else {
-      uint32_t roa[PA::LPC];
-      row_offsets<CA>(lda_b, rows_a, q, roa);
-      load_chunks_tail<CA>(A, roa, nfull, ka, q, va);
-    }
-    if constexpr (BMN) {
-      load_chunks_tail_mn<CB>(B, ldb_b, mlimb, nfull, a.K, q, vb);
-    } else {
-      uint32_t rob[PB::LPC];
-      row_offsets<CB>(ldb_b, rows_b, q, rob);
-      load_chunks_tail<CB>(B, rob, nfull, kb, q, vb);
-    }
-    const uint32_t wsa = mask_scale_word(load_scale_word(a.SFA, a.ld_sfa, m0, a.M, q, nfull), nfull, nblk);
-    const uint32_t wsb = mask_scale_word(load_scale_word(a.SFB, a.ld_sfb, n0, a.N, q, nfull), nfull, nblk);
-    store_chunks<CA, AMN>(st, q, va);
-    store_chunks<CB, BMN>(st + PA::TILE, q, vb);
-    uint8_t* scales = lds + L::RING;          // one word per row: A's 256, then B's
-    *(BSM_LDS uint32_t*)(scales + 4 * q) = wsa;
-    *(BSM_LDS uint32_t*)(scales + 1024 + 4 * q) = wsb;
-    __syncthreads();
-    multiply(st, scales);
-    __syncthreads();
-  }
   // (accumulation as a constant in each branch: the fresh-D path then holds no registers for
   // D's values, which made the compiler spill accumulators here)
   if (a.accum)

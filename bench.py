@@ -87,12 +87,17 @@ EPILOGUE_ARGS = (2.0, 1.0)   # silu_affine scale, bias
 
 
 def source_hash(kernel):
+    """Hash of a kernel's sources with comments and blank lines removed: an edit to the code
+    makes the committed counter figures stale, an edit to its comments does not."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, _CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, _CSRC, f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        lines = [ln.rstrip() for ln in re.sub(r"//[^\n]*", "", text).split("\n") if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
@@ -625,7 +630,8 @@ def summarize(dirs, steps, calib=None):
                   " | " + "; ".join(der) + " |")
         if machine:
             print("\nMachine-readable rows for bench.py (mfma: kernel, MFMA busy, clock GHz, source hash; traffic: "
-                  "kernel, HBM bytes per launch, source hash):\n\n```")
+                  "kernel, HBM bytes per launch, source hash; the hash covers the kernel's sources without "
+                  "comments):\n\n```")
             print("\n".join(machine))
             print("```")
 

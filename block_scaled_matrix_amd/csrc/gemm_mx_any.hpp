@@ -33,7 +33,8 @@
 // four times as long. One barrier per K tile, at the start of its step 1; step 1's
 // fragment reads go out between step 0's MFMAs, the next tile's scales and step-0
 // fragments between step 1's, so no K tile starts by waiting for the LDS. A partial last
-// K tile goes through registers with zero elements and unit scales past K.
+// K tile goes through registers with zero elements and unit scales past K, multiplied
+// before the whole tiles (its sum is added first).
 //
 // Two ways to multiply a step's fragments (template parameter BF):
 //  - the scaled f8f6f4 MFMA (BF false). It sums the products of one 32-K scale block on a grid

@@ -28,6 +28,10 @@ reported under `widened` (not part of `value`):
              strides (1, 2, 1), the 32 x 32 x 16 boxes given as repeat axes (one call)
   gemm_e4m3_e2m1   block-scaled M=N=8192, K=16384, A E4M3, B E2M1 (mixed widths), fresh D
   gemm_e2m3_e2m3   block-scaled M=N=8192, K=16384, both FP6 E2M3, fresh D
+  box_copy_only    the box-copy workload's call with the store alone (dst only: read src and
+             write dst, 2 x 268 320 780 bytes)
+  box_reduce_only  the same call with the reduce-add alone (dst_add only: read src, read and
+             write dst_add, 3 x 268 320 780 bytes)
 (the mixed pair runs at the 8-bit MFMA rate, peak 5033.2 TFLOP/s; FP6 pairs at the 4-bit
 rate, peak 10066.3 TFLOP/s)
 
@@ -44,6 +48,7 @@ rest of the step is unchanged, and config.epilogue names it.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -79,6 +84,8 @@ KERNEL_SOURCES = {
     "box_load_rank3": ["k_tile.hip", "bsm_device.hpp"],
     "gemm_e4m3_e2m1": ["k_gemm_mx_any.hip", "gemm_mx_any.hpp", "gemm_common.hpp", "bsm_device.hpp"],
     "gemm_e2m3_e2m3": ["k_gemm_mx_any.hip", "gemm_mx_any.hpp", "gemm_common.hpp", "bsm_device.hpp"],
+    "box_copy_only": ["k_tile.hip", "bsm_device.hpp"],
+    "box_reduce_only": ["k_tile.hip", "bsm_device.hpp"],
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.md")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_busy_bench_step.md")
@@ -89,7 +96,6 @@ EPILOGUE_ARGS = (2.0, 1.0)   # silu_affine scale, bias
 def source_hash(kernel):
     """Hash of a kernel's sources with comments and blank lines removed: an edit to the code
     makes the committed counter figures stale, an edit to its comments does not."""
-    import hashlib
     import re
 
     h = hashlib.sha256()
@@ -170,26 +176,34 @@ def make_inputs():
 
     from block_scaled_matrix_amd import workloads as W
 
-    def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sha = {}
+
+    def dev(a, name=None):
+        a = np.ascontiguousarray(a)
+        if name is not None:
+            sha[name] = hashlib.sha256(a.view(np.uint8).reshape(-1)).hexdigest()[:16]
+        return torch.from_numpy(a).cuda()
+
+    def put(prefix, g):
+        return {k: (dev(v, f"{prefix}.{k}") if isinstance(v, np.ndarray) else v) for k, v in g.items()}
 
     t0 = time.time()
-    inp = {}
+    inp = {"sha256": sha}
     bc = W.box_copy_bf16()
-    inp["box"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in bc.items()}
+    inp["box"] = put("box_copy", bc)
     log(f"box_copy inputs {time.time() - t0:.1f}s")
     g = W.gemm_bf16()
-    inp["bf16"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    inp["bf16"] = put("gemm_bf16", g)
     log(f"gemm_bf16 inputs {time.time() - t0:.1f}s")
     g = W.mxfp8()
-    inp["fp8"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    inp["fp8"] = put("mxfp8", g)
     inp["fp8"]["D"] = torch.empty((g["M"], g["N"]), dtype=torch.float32, device="cuda")
     log(f"mxfp8 inputs {time.time() - t0:.1f}s")
     g = W.mxfp4()
-    inp["fp4"] = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    inp["fp4"] = put("mxfp4", g)
     inp["fp4"]["D"] = torch.empty((g["M"], g["N"]), dtype=torch.float32, device="cuda")
     log(f"mxfp4 inputs {time.time() - t0:.1f}s")
-    inp["add"] = dev(W.add_one_tile())
+    inp["add"] = dev(W.add_one_tile(), "add_one.A")
     inp["add_out"] = torch.empty_like(inp["add"])
     g = W.gather4_bf16()
     n = len(g["gather"])
@@ -277,7 +291,16 @@ def widened(inp):
     t3 = bsm.tensor_desc(b3["x"], "bf16", d3, (d3[1] * d3[2] * 2, d3[2] * 2, 2))
     bx3 = bsm.box_desc(b3["box"], b3["estr"], 0, 0)
     bytes3 = 2 * (d3[0] * d3[1] // 2 * d3[2] * 2)   # the sampled half of the rows read, written as images
+    b = inp["box"]
+    brows, bcols, bpitch = b["rows"], b["cols"], b["pitch"]
+    btd = lambda t: bsm.tensor_desc(t, "bf16", (brows, bcols), (bpitch * 2, 2))
+    bbox = bsm.box_desc(b["box"], (1, 1), 3, 0)
+    belem = brows * bcols * 2                    # bytes of one tensor's logical elements
     return [
+        ("box_copy_only", lambda: bsm.bsm_tile_box_copy(btd(b["src"]), btd(b["dst"]), None, bbox), 2 * belem, "GB/s",
+         PEAK["hbm_GBs"]),
+        ("box_reduce_only", lambda: bsm.bsm_tile_box_copy(btd(b["src"]), None, btd(b["dst_add"]), bbox), 3 * belem,
+         "GB/s", PEAK["hbm_GBs"]),
         ("box_load_rank3", lambda: bsm.bsm_tile_box_load_steps(t3, bx3, b3["coords"], b3["repeats"], b3["steps"],
                                                                b3["images"]), bytes3, "GB/s", PEAK["hbm_GBs"]),
         ("gather4", lambda: bsm.bsm_tile_gather4(src, box, g["gather"], n, g["images"]), nbytes, "GB/s",
@@ -373,6 +396,10 @@ def cpu_baseline(inp):
     flops = 0.0
     t_gemm = 0.0
     parity = {}
+    per_cfg = {}
+
+    def timed(name, rows, fl, t):
+        per_cfg[name] = {"rows": rows, "s": round(t, 2), "TFLOP/s": fl / t / 1e12}
 
     def gemm_parity(name, D, ref, bound, tol, sample):
         nb, _, worst = O.check_gemm(np.ascontiguousarray(D, np.float32), ref, bound, tol)
@@ -385,8 +412,10 @@ def cpu_baseline(inp):
     t0 = time.perf_counter()
     ref, bound = O.gemm(g["M"], g["N"], g["K"], "bf16", g["A"], g["K"], "k", g["B"], g["N"], "n", g["D0"], g["N"], 0,
                         0, 1, 0, rows)
-    t_gemm += time.perf_counter() - t0
+    dt = time.perf_counter() - t0
+    t_gemm += dt
     flops += 2.0 * rows * g["N"] * g["K"]
+    timed("gemm_bf16", rows, 2.0 * rows * g["N"] * g["K"], dt)
     x = inp["bf16"]
     D = torch.from_numpy(g["D0"][:rows].copy()).cuda()   # the first rows of D0, accumulated once
     bsm.bsm_gemm(rows, x["N"], x["K"], "bf16", x["A"], x["K"], "k", x["B"], x["N"], "n", D, x["N"], 0, 0, 1)
@@ -397,8 +426,10 @@ def cpu_baseline(inp):
     t0 = time.perf_counter()
     ref, bound = O.gemm_block_scale(g["M"], g["N"], g["K"], "e4m3", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e4m3",
                                     g["B"], g["K"], g["SFB"], g["ld_sfb"], None, 0, 0, 0, 0, 0, rows)
-    t_gemm += time.perf_counter() - t0
+    dt = time.perf_counter() - t0
+    t_gemm += dt
     flops += 2.0 * rows * g["N"] * g["K"]
+    timed("gemm_mxfp8", rows, 2.0 * rows * g["N"] * g["K"], dt)
     x = inp["fp8"]
     x["D"].fill_(float("nan"))
     bsm.bsm_gemm_block_scale(x["M"], x["N"], x["K"], "e4m3", x["A"], x["lda"], x["SFA"], x["ld_sfa"], "e4m3", x["B"],
@@ -415,8 +446,10 @@ def cpu_baseline(inp):
     t0 = time.perf_counter()
     ref, bound = O.gemm_block_scale(g["M"], g["N"], g["K"], "e2m1", g["A"], g["K"], g["SFA"], g["ld_sfa"], "e2m1",
                                     g["B"], g["K"], g["SFB"], g["ld_sfb"], None, 0, 1, 0, 0, 0, rows)
-    t_gemm += time.perf_counter() - t0
+    dt = time.perf_counter() - t0
+    t_gemm += dt
     flops += 2.0 * rows * g["N"] * g["K"]
+    timed("gemm_mxfp4", rows, 2.0 * rows * g["N"] * g["K"], dt)
     x = inp["fp4"]
     x["D"].fill_(float("nan"))
     bsm.bsm_gemm_block_scale(x["M"], x["N"], x["K"], "e2m1", x["A"], x["lda"], x["SFA"], x["ld_sfa"], "e2m1", x["B"],
@@ -441,7 +474,8 @@ def cpu_baseline(inp):
             "sample": f"GEMM rows: bf16 {rows_bf16} of 8192, mxfp8 {rows_fp8} of 8192, mxfp4 {rows_fp4} of 16384 "
                       f"(full N and K), "
                       f"{t_gemm:.1f} s; box copy on a 1024x8190 band: {box_gbs:.3f} GB/s in {t_box:.1f} s",
-            "box_copy_GBs": box_gbs}
+            "box_copy_GBs": box_gbs,
+            "per_config": dict(per_cfg, box_copy={"rows": 1024, "s": round(t_box, 2), "GB/s": box_gbs})}
     return base, parity
 
 
@@ -463,7 +497,9 @@ NAME_RULES = [
     (r"k_mfma_loop<4>", "mfma_loop_bf16"),
     (r"k_mfma_loop<6>", "mfma_loop_e4m3"),
     (r"k_mfma_loop<7>", "mfma_loop_e2m1"),
-    (r"k_box_copy2d", "box_copy*"),
+    (r"k_box_copy2d<0, true>", "box_copy_only"),
+    (r"k_box_copy2d<4, false>", "box_reduce_only"),
+    (r"k_box_copy2d<4, true>", "box_copy*"),
 ]
 # Algorithmic HBM bytes per launch of the GEMMs: operands once, D written (and read when
 # accumulating), scales once.
@@ -479,6 +515,8 @@ ALG_BYTES = {
 STATIC_WORK = {
     "box_copy": (4 * 16381 * 8190 * 2, "GB/s", PEAK["hbm_GBs"]),
     "box_copy_unragged": (4 * UNRAGGED_ROWS * 8192 * 2, "GB/s", PEAK["hbm_GBs"]),
+    "box_copy_only": (2 * 16381 * 8190 * 2, "GB/s", PEAK["hbm_GBs"]),
+    "box_reduce_only": (3 * 16381 * 8190 * 2, "GB/s", PEAK["hbm_GBs"]),
     "stream_mix_bf16": (4 * 2 * 16381 * 8192, "GB/s", PEAK["hbm_GBs"]),
     "gemm_bf16": (2.0 * 8192 ** 3, "TFLOP/s", PEAK["bf16_TFs"]),
     "gemm_mxfp8": (2.0 * 8192 * 8192 * 16384, "TFLOP/s", PEAK["fp8_TFs"]),
@@ -783,6 +821,7 @@ def main():
                    "seeds": {"box_copy": 2, "gemm_bf16": 3, "mxfp8": 4, "mxfp4": 5},
                    "epilogue": args.epilogue if args.epilogue == "none" else
                    f"{args.epilogue}(scale {EPILOGUE_ARGS[0]:g}, bias {EPILOGUE_ARGS[1]:g})"},
+        "inputs_sha256": inp["sha256"],
         "per_kernel": per,
         "widened": wide,
         "context": context,

@@ -397,9 +397,12 @@ constexpr int kCopyPasses = 2;
 // ADDT: 0 for a plain copy, else the reduce-add element type (BSM_F32, BSM_BF16, BSM_F16),
 // fixed at compile time so that the add is straight-line code: a run-time type switch
 // between the stores makes the compiler wait for every outstanding store before each add.
-template <int ADDT>
+// DST: whether the image is also stored to dst (a reduce-add alone passes no dst), likewise
+// a compile-time choice, so that each of the three forms is its own kernel.
+template <int ADDT, bool DST>
 __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
   constexpr bool ADD = ADDT != 0;
+  static_assert(ADD || DST, "a copy stores, reduce-adds, or both");
   extern __shared__ __attribute__((aligned(1024))) uint8_t image[];
   const uint32_t g1 = blockIdx.x % a.groups1, rest = blockIdx.x / a.groups1;
   const uint32_t sl = rest % a.slices, t0 = rest / a.slices;
@@ -464,12 +467,12 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
     if (!rin[k] || !(whole || part)) continue;
     const uint4 x = lds_read_b128(region + image_swizzle((uint32_t)(rr * a.row_bytes + cc * 16), a.swizzle));
     if (__builtin_expect(whole, 1)) {
-      if (a.dst) stream_store16(a.dst + row * a.s_dst + k0 * a.esize, x);
+      if (DST) stream_store16(a.dst + row * a.s_dst + k0 * a.esize, x);
       if (ADD) stream_store16(a.add + row * a.s_add + k0 * a.esize, add_chunk(ADDT, d[k], x));
     } else {
       // the straddling chunk: its in-range head only
       const int nb = (int)(a.dims1 - k0) * a.esize;
-      if (a.dst) store_head16(a.dst + row * a.s_dst + k0 * a.esize, x, nb);
+      if (DST) store_head16(a.dst + row * a.s_dst + k0 * a.esize, x, nb);
       if (ADD) {
         uint8_t* q = a.add + row * a.s_add + k0 * a.esize;
         if (!last[k]) {
@@ -532,16 +535,25 @@ hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const i
     // every box's slice region is rs * row_bytes = 8 KiB / 2^lg_nb >= 1 KiB, a whole number
     // of swizzle periods (the swizzle stays inside aligned 2^(7 + mode)-byte windows)
     const size_t lds_bytes = (size_t)kCopyPasses * 256 * 16;
-    if (!dst_add)
-      hipLaunchKernelGGL(k_box_copy2d<0>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
-    else if (g.dtype == BSM_F32)
-      hipLaunchKernelGGL(k_box_copy2d<BSM_F32>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
-    else if (g.dtype == BSM_BF16)
-      hipLaunchKernelGGL(k_box_copy2d<BSM_BF16>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
-    else if (g.dtype == BSM_F16)
-      hipLaunchKernelGGL(k_box_copy2d<BSM_F16>, dim3((unsigned)wgs), dim3(256), lds_bytes, st, a);
-    else
+    const dim3 grid((unsigned)wgs);
+#define BSM_COPY2D(ADDT)                                                                        \
+  do {                                                                                          \
+    if (dst) hipLaunchKernelGGL((k_box_copy2d<ADDT, true>), grid, dim3(256), lds_bytes, st, a);  \
+    else hipLaunchKernelGGL((k_box_copy2d<ADDT, false>), grid, dim3(256), lds_bytes, st, a);     \
+  } while (0)
+    if (!dst_add) {
+      if (!dst) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_box_copy2d<0, true>), grid, dim3(256), lds_bytes, st, a);
+    } else if (g.dtype == BSM_F32) {
+      BSM_COPY2D(BSM_F32);
+    } else if (g.dtype == BSM_BF16) {
+      BSM_COPY2D(BSM_BF16);
+    } else if (g.dtype == BSM_F16) {
+      BSM_COPY2D(BSM_F16);
+    } else {
       return hipErrorInvalidValue;
+    }
+#undef BSM_COPY2D
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_box_copy, dim3((unsigned)tiles), dim3(256), (size_t)g.image_stride, st, g, o,

@@ -15,7 +15,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 BF16_KERNEL = "void bsm::(anonymous namespace)::k_gemm_dense<4, true, false, true>(bsm::GemmArgs, int, int)"
 MX4_KERNEL = "void bsm::(anonymous namespace)::k_gemm_mx<4, 4, 4, false>(bsm::GemmArgs, int, int)"
-BOX_KERNEL = "void bsm::k_box_copy2d<4>(bsm::Copy2D)"
+BOX_KERNEL = "void bsm::k_box_copy2d<4, true>(bsm::Copy2D)"
+COPY_ONLY_KERNEL = "void bsm::k_box_copy2d<0, true>(bsm::Copy2D)"
+REDUCE_ONLY_KERNEL = "void bsm::k_box_copy2d<4, false>(bsm::Copy2D)"
 
 
 def test_more_than_one_gpu_is_refused():
@@ -48,9 +50,14 @@ def test_profile_groups_keep_the_timed_launches():
     rows = [(BF16_KERNEL, 1024 * 256, 10 * i, 10 * i + (1000 if i < 3 else 900), None) for i in range(8)]
     rows += [(BOX_KERNEL, 32768 * 256, 100 + i, 150 + i, None) for i in range(3)]
     rows += [(BOX_KERNEL, 32512 * 256, 200 + i, 240 + i, None) for i in range(3)]
+    # the store-only and reduce-add-only forms of the workload's call: same grid, own kernels
+    rows += [(COPY_ONLY_KERNEL, 32768 * 256, 300 + i, 330 + i, None) for i in range(2)]
+    rows += [(REDUCE_ONLY_KERNEL, 32768 * 256, 400 + i, 445 + i, None) for i in range(2)]
     rows += [("void other_kernel()", 64, 0, 5, None)]
     groups, names = bench._profile_groups(rows, 5)
-    assert sorted(groups) == ["box_copy", "box_copy_unragged", "gemm_bf16"]
+    assert sorted(groups) == ["box_copy", "box_copy_only", "box_copy_unragged", "box_reduce_only", "gemm_bf16"]
+    assert [e - s for s, e, _ in groups["box_copy_only"]] == [30] * 2
+    assert [e - s for s, e, _ in groups["box_reduce_only"]] == [45] * 2
     assert [e - s for s, e, _ in groups["gemm_bf16"]] == [900] * 5
     assert names["gemm_bf16"][2:] == (8, 5)
     assert [e - s for s, e, _ in groups["box_copy"]] == [50] * 3

@@ -13,6 +13,8 @@
 // element strides (the common case, chosen on the host) use a dedicated kernel that
 // issues every HBM read of the workgroup before its first use, uses streaming accesses
 // and handles ragged edges without per-element loads.
+#include <atomic>
+
 #include "bsm_device.hpp"
 #include "bsm_internal.hpp"
 #include "../../include/bsm.h"
@@ -490,12 +492,18 @@ __global__ __launch_bounds__(256) void k_box_copy2d(Copy2D a) {
 
 hipError_t launch_box_copy(const BoxGeom& g, const void* src, void* dst, const int64_t* dst_strides, void* dst_add,
                            const int64_t* add_strides, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_box_copy, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-
+  // The general kernel's image may take up to 160 KiB of dynamic LDS: raise the kernel's limit
+  // once per device (a bit per device id; concurrent first calls may both set it, which is
+  // harmless).
+  static std::atomic<uint64_t> attr_devices{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (!(attr_devices.load(std::memory_order_acquire) & bit) || !bit) {
+    e = hipFuncSetAttribute((const void*)k_box_copy, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_devices.fetch_or(bit, std::memory_order_release);
   }
   CopyOut o{};
   for (int i = 0; i < g.rank; i++) {

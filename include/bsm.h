@@ -8,7 +8,11 @@
  *     NULL = the default stream) and returns BSM_OK without synchronising;
  *   - never allocates, frees or keeps a pointer after it returns (other than in
  *     the enqueued work). The caller owns every buffer, keeps it alive until the
- *     stream work completes, and owns all synchronisation.
+ *     stream work completes, and owns all synchronisation;
+ *   - enqueues kernels only (no memory copy, memset or host synchronisation), so a
+ *     sequence of calls may be captured into a HIP graph on a capturing stream and
+ *     replayed; the first box-copy call on a device must run outside a capture (it
+ *     sets a kernel attribute once per device).
  * Device faults surface asynchronously at the caller's next synchronisation.
  *
  * Pages cited (web documentation of Apache TVM "TIRx"):

@@ -35,8 +35,10 @@ reported under `widened` (not part of `value`):
 (the mixed pair runs at the 8-bit MFMA rate, peak 5033.2 TFLOP/s; FP6 pairs at the 4-bit
 rate, peak 10066.3 TFLOP/s)
 
-`context` holds one reference point that is not part of the path: torch.mm (hipBLASLt) on the
-bf16 workload's shape with a fresh bf16 output, timed the same way after the step.
+`context` holds reference points that are not part of the path, timed the same way after the
+step: torch.mm (hipBLASLt) on the bf16 workload's shape with a fresh bf16 output, the vendor's fp8
+GEMMs through torch._scaled_mm on the MXFP8 workload's codes (per-tensor scales with a float32
+output, and E8M0 block scales with a bf16 output), and the ceilings the rows run against.
 
 --epilogue silu_affine fuses the scalar epilogue f(x) = x / (1 + exp(-x)) * 2 + 1 (the example call
 of "Explicit CUDA tile patterns", Scalar compositions) into the three GEMMs' stores (bsm_gemm_ewise, bsm_gemm_block_scale_ewise); the
@@ -314,6 +316,61 @@ def widened(inp):
         ("gemm_mxfp8_fastacc", mx("fp8", bsm.bsm_gemm_block_scale_fastacc), 2.0 * 8192 * 8192 * 16384, "TFLOP/s",
          PEAK["fp8_TFs"]),
     ]
+
+
+def vendor_fp8(inp, steps, stream):
+    """Context rows: the vendor library's fp8 GEMMs (torch._scaled_mm -> hipBLASLt) on the MXFP8
+    workload's operand codes, as reference points outside the path: per-tensor unit scales with a
+    float32 output, and the E8M0 block scales with a bfloat16 output (its block-scaled path writes
+    only bf16 or f16). The first also reports its sum on a 16-row sample against a float64 torch
+    (CPU) product of the decoded codes, under the 1e-5 * sum|ab| bound: the scaled fp8 MFMA's
+    block window shows there too. Rows whose call the installed torch does not support are left
+    out."""
+    import torch
+
+    f8 = inp["fp8"]
+    M, N, K = f8["M"], f8["N"], f8["K"]
+    try:
+        A = f8["A"].view(torch.float8_e4m3fn).reshape(M, K)
+        B = f8["B"].view(torch.float8_e4m3fn).reshape(N, K)
+        one = torch.ones((), device="cuda")
+        SA = f8["SFA"].view(torch.float8_e8m0fnu).reshape(M, -1)[:, :K // 32]
+        SB = f8["SFB"].view(torch.float8_e8m0fnu).reshape(N, -1)[:, :K // 32]
+    except (AttributeError, RuntimeError) as e:
+        log(f"vendor fp8 rows skipped: {e}")
+        return {}
+    rows = [("torch_scaled_mm_fp8", lambda: torch._scaled_mm(A, B.t(), scale_a=one, scale_b=one,
+                                                             out_dtype=torch.float32),
+             "hipBLASLt fp8 GEMM through torch._scaled_mm on the MXFP8 workload's E4M3 codes, per-tensor unit "
+             "scales (not block-scaled), float32 output"),
+            ("torch_scaled_mm_mxfp8", lambda: torch._scaled_mm(A, B.t(), scale_a=SA.contiguous(),
+                                                               scale_b=SB.contiguous(), out_dtype=torch.bfloat16),
+             "hipBLASLt block-scaled fp8 GEMM through torch._scaled_mm on the MXFP8 workload (E8M0 scales passed "
+             "as (rows, K/32)), bfloat16 output (the only widths its block-scaled path writes)")]
+    out = {}
+    flop = 2.0 * M * N * K
+    for name, fn, note in rows:
+        try:
+            fn()
+            torch.cuda.synchronize()
+        except (RuntimeError, ValueError, TypeError) as e:
+            log(f"{name} (context) skipped: {str(e)[:200]}")
+            continue
+        ms = time_launches([(name, fn, flop, "TFLOP/s", PEAK["fp8_TFs"])], steps, stream)[0]
+        out[name] = rate_entry(ms, flop, "TFLOP/s", PEAK["fp8_TFs"])
+        out[name]["note"] = note
+        log(f"{name} (context): {ms:.4f} ms  {out[name]['achieved']:.1f} TFLOP/s")
+    if "torch_scaled_mm_fp8" in out:
+        r = 16
+        D = rows[0][1]()[:r].double().cpu()
+        a = A[:r].cpu().to(torch.float64)
+        b = B.cpu().to(torch.float64)
+        ref, bound = a @ b.T, a.abs() @ b.abs().T
+        ratio = ((D - ref).abs() / bound)
+        out["torch_scaled_mm_fp8"]["parity_sample"] = {
+            "sample": f"rows 0..{r - 1}, all columns, against float64 torch (CPU) on the decoded codes",
+            "tol_sum_abs_ab": 1e-5, "n_bad": int((ratio > 1e-5).sum()), "worst_err_over_sum_abs_ab": ratio.max().item()}
+    return out
 
 
 MFMA_LOOP = {"bf16": (800, 32768), "e4m3": (400, 131072), "e2m1": (800, 131072)}   # iters, FLOP per MFMA
@@ -785,6 +842,7 @@ def main():
     context["torch_mm_bf16"]["note"] = ("hipBLASLt through torch.mm, bf16 8192^3, fresh bf16 output, no accumulation: "
                                         "a vendor-library reference point, not part of the step")
     log(f"torch_mm_bf16 (context): {context['torch_mm_bf16']['ms']:.4f} ms  {context['torch_mm_bf16']['achieved']:.1f} TFLOP/s")
+    context.update(vendor_fp8(inp, args.steps, stream))
     # the ceilings the rows run against, measured with the library's diagnostic kernels on the
     # same device in the same run (not part of the step)
     ck = ceilings(inp)

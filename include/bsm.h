@@ -333,10 +333,11 @@ int bsm_tile_add_scalar_f32(const float* src, float* dst, int64_t n, float s, vo
  * (major 'k': src[r*kdim + k]; major 'm': src[k*rows + r]), staged into LDS with
  * the GEMM's own loader and swizzle, and read back with the GEMM's own fragment
  * reads (16-byte reads for 'k', transposing 16-bit reads for 'm'). For every
- * 32-row block b, 16-wide K step s, lane l and element e, the value the lane holds
- * for operand (row 32b + l%32, k 16s + 8(l/32) + e) is written to
- * dump[((b * (kdim/16) + s) * 64 + l) * 8 + e]. rows/kdim must equal the shape
- * returned by bsm_debug_fragment_shape. */
+ * 16-row block b, 32-wide K step s, lane l and element e, the value the lane holds
+ * for operand (row 16b + l%16, k 32s + 8(l/16) + e) is written to
+ * dump[((b * (kdim/32) + s) * 64 + l) * 8 + e] (the operand layout of the GEMM's
+ * 16x16x32 MFMA). rows/kdim must equal the shape returned by
+ * bsm_debug_fragment_shape. */
 int bsm_debug_fragments(const uint16_t* src, int64_t rows, int64_t kdim, char major,
                         uint16_t* dump, void* stream);
 void bsm_debug_fragment_shape(int64_t* rows, int64_t* kdim);

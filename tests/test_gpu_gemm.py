@@ -202,17 +202,18 @@ def test_fragment_loads_vs_oracle_ldmatrix_image(O, major):
     rng = np.random.default_rng(3)
     op = rng.integers(0, 2 ** 16, (rows, kdim), dtype=np.uint64).astype(np.uint16)   # logical operand (row, k)
     stored = op if major == "k" else np.ascontiguousarray(op.T)                     # storage order
-    dump = torch.zeros((rows // 32) * (kdim // 16) * 64 * 8, dtype=torch.int16, device="cuda")
+    dump = torch.zeros((rows // 16) * (kdim // 32) * 64 * 8, dtype=torch.int16, device="cuda")
     say("fragments", major)
     bsm.bsm_debug_fragments(dev(stored), rows, kdim, major, dump)
-    got = host(dump, np.uint16).reshape(rows // 32, kdim // 16, 64, 8)
+    got = host(dump, np.uint16).reshape(rows // 16, kdim // 32, 64, 8)
     # oracle: 8x8 matrices of the stored array; with transpose for MN-major storage
     sb = stored.view(np.uint8).reshape(-1)
     row_pitch = stored.shape[1] * 2
-    for b in range(rows // 32):
-        for s in range(kdim // 16):
+    for b in range(rows // 16):
+        for s in range(kdim // 32):
             for lane in range(64):
-                r, kb = 32 * b + lane % 32, 16 * s + 8 * (lane // 32)
+                # the 16x16x32 MFMA operand: lane l holds row l%16 of the block, k 8(l/16)..+7 of the step
+                r, kb = 16 * b + lane % 16, 32 * s + 8 * (lane // 16)
                 if major == "k":   # matrix rows are operand rows r8..r8+7, columns k8..k8+7
                     r8, k8 = r - r % 8, kb
                     offs = [(r8 + j) * row_pitch + k8 * 2 for j in range(8)]

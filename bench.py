@@ -64,7 +64,7 @@ PEAK = {"hbm_GBs": 8000.0, "bf16_TFs": 2516.6, "fp8_TFs": 5033.2, "fp4_TFs": 100
 # with wide product ranges (any 8-bit operand) sum exact products with the bf16 MFMA, so
 # their rate is bounded by the bf16 peak; `frac` stays against the format's own MFMA peak.
 INSTRUCTION = {
-    "gemm_bf16": ("v_mfma_f32_32x32x16_bf16", "bf16_TFs"),
+    "gemm_bf16": ("v_mfma_f32_16x16x32_bf16", "bf16_TFs"),
     "gemm_mxfp8": ("v_mfma_f32_32x32x16_bf16 (exact products)", "bf16_TFs"),
     "gemm_mxfp4": ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", "fp4_TFs"),
     "gemm_mxfp8_fastacc": ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", "fp8_TFs"),

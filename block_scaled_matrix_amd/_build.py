@@ -17,13 +17,24 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# The GEMM kernels' LDS copies read SGPR operands that inline assembly pads for itself
+# (gemm_common.hpp, sgpr_base): that padding holds only if the compiler never spills and
+# restores an SGPR, so their per-kernel resource report is checked for SGPR spills.
+REPORT = "-Rpass-analysis=kernel-resource-usage"
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, REPORT, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    kernel = "?"
     for line in r.stderr.splitlines():
-        if "warning" in line and "packed-fp32-ops" not in line:
+        if "Function Name:" in line:
+            kernel = line.split("Function Name:")[1].split()[0]
+        elif src.startswith("k_gemm") and "SGPRs Spill:" in line and int(line.split("SGPRs Spill:")[1].split()[0]):
+            raise RuntimeError(f"{src}: kernel {kernel} spills SGPRs")
+        elif "warning" in line and "packed-fp32-ops" not in line:
             print(line)
 
 

@@ -7,19 +7,35 @@ namespace bsm {
 namespace gemm {
 
 // Direct HBM -> LDS copy of 16 bytes per lane: lane l copies base + voff (its own
-// 32-bit byte offset from the wave-uniform base) to LDS byte lds_addr + 16 * l
-// (lds_addr wave-uniform). Issued through inline assembly so that the compiler does
-// not serialise it against LDS reads of the other pipeline stage: the kernels wait for
-// these copies themselves (wait_dma) before the stage barrier.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t b = (uint64_t)base;
+// 32-bit byte offset from the wave-uniform base) to LDS byte lds_addr + 16 * l (lds_addr
+// wave-uniform). Issued through inline assembly so that the compiler does not serialise it
+// against LDS reads of the other pipeline stage: the kernels wait for these copies themselves
+// (wait_dma, stage barriers) before reading what they brought. The LDS address goes to M0 as
+// an operand bound to that register, so the compiler knows M0's contents at every point (a
+// clobber of M0, a reserved register, is not guaranteed to be honoured).
+// Hazards: the compiler pads its own instructions for the wait states the hardware needs
+// but cannot see inside inline assembly, so the copies pad for themselves. A vector-memory
+// instruction that reads an SGPR written by the VALU needs 5 wait states after that write:
+// the base reaches its SGPRs through v_readfirstlane, followed by an s_nop 4 that claims to
+// rewrite them (sgpr_base); that asm is not volatile, so the copies of one tile with the same
+// base share one (a schedule that left no wait state between the readfirstlane of a tile base
+// and its copy gave intermittent wrong values in a ragged MN-major dense GEMM). An SALU write
+// of M0 needs 1 wait state before an LDS-DMA instruction reads it: the s_nop 0 in the copy.
+// The SGPRs must not be spilled between the two (a restore is a VALU write): the build
+// checks that no kernel spills SGPRs.
+__device__ __forceinline__ uint64_t sgpr_base(const void* p) {
+  const uint64_t b = (uint64_t)p;
   // readfirstlane yields a signed int: widen through uint32_t so that the low word is
   // zero-extended (sign extension would corrupt the high half of the address).
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  asm("s_nop 4" : "+s"(lo), "+s"(hi));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t sb = sgpr_base(base);
   const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(a) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(a) : "memory");
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -27,14 +43,12 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // complete in issue order), i.e. every copy issued before the last N has landed.
 #define BSM_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 
-// Direct HBM -> LDS copy of 4 bytes per lane (lane l lands at lds_addr + 4 * l).
+// Direct HBM -> LDS copy of 4 bytes per lane (lane l lands at lds_addr + 4 * l), the same
+// way as dma16s.
 __device__ __forceinline__ void dma4s(const void* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t b = (uint64_t)base;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint64_t sb = sgpr_base(base);
   const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb), "s"(a) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb), "{m0}"(a) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -345,14 +345,15 @@ __device__ __forceinline__ uint4 cvt_part(const i32x8& v, uint32_t sbits) {
 // All 32 elements of a 6-bit operand (dwords 0..5, element i at bits 6i..6i+5) times
 // 2^(code - 127) as bf16, o[j] = elements 8j .. 8j + 7. Written as inline assembly with an
 // early-clobber 16-register result: the compiler's builtin for these conversions let the
-// result overlap live registers.
+// result overlap live registers. The compiler does not know the assembly is a VALU write, so
+// it ends with the 2 wait states an MFMA needs before reading VGPRs a VALU instruction wrote.
 template <int C>
 __device__ __forceinline__ void cvt_all6(const i32x8& v, uint32_t sbits, uint4 (&o)[4]) {
   const u32x6_t in = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3], (uint32_t)v[4], (uint32_t)v[5]};
   const float s = __uint_as_float(sbits);
   u32x16_t r;
-  if constexpr (C == 2) asm volatile("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2" : "=&v"(r) : "v"(in), "v"(s));
-  else asm volatile("v_cvt_scalef32_pk32_bf16_bf6 %0, %1, %2" : "=&v"(r) : "v"(in), "v"(s));
+  if constexpr (C == 2) asm volatile("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2\n\ts_nop 1" : "=&v"(r) : "v"(in), "v"(s));
+  else asm volatile("v_cvt_scalef32_pk32_bf16_bf6 %0, %1, %2\n\ts_nop 1" : "=&v"(r) : "v"(in), "v"(s));
 #pragma unroll
   for (int j = 0; j < 4; j++) o[j] = make_uint4(r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]);
 }

@@ -23,19 +23,28 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 REPORT = "-Rpass-analysis=kernel-resource-usage"
 
 
+def check_report(src: str, stderr: str) -> list:
+    """Reads hipcc's output for one source: raises if a GEMM kernel spills SGPRs, returns the
+    warnings worth showing (the host pass's note about the packed-fp32 feature excluded)."""
+    kernel, shown = "?", []
+    for line in stderr.splitlines():
+        if "Function Name:" in line:
+            kernel = line.split("Function Name:")[1].split()[0]
+        elif "SGPRs Spill:" in line:
+            if src.startswith("k_gemm") and int(line.split("SGPRs Spill:")[1].split()[0]):
+                raise RuntimeError(f"{src}: kernel {kernel} spills SGPRs")
+        elif "warning" in line and "packed-fp32-ops" not in line:
+            shown.append(line)
+    return shown
+
+
 def _compile(src: str, obj: str) -> None:
     cmd = [HIPCC, *FLAGS, REPORT, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-    kernel = "?"
-    for line in r.stderr.splitlines():
-        if "Function Name:" in line:
-            kernel = line.split("Function Name:")[1].split()[0]
-        elif src.startswith("k_gemm") and "SGPRs Spill:" in line and int(line.split("SGPRs Spill:")[1].split()[0]):
-            raise RuntimeError(f"{src}: kernel {kernel} spills SGPRs")
-        elif "warning" in line and "packed-fp32-ops" not in line:
-            print(line)
+    for line in check_report(src, r.stderr):
+        print(line)
 
 
 def build(jobs: int = min(8, os.cpu_count() or 4)) -> str:

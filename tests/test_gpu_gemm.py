@@ -127,9 +127,9 @@ def test_dense_accum_zero_A_and_determinism(O):
 
 @pytest.mark.parametrize("amaj,bmaj", [("k", "k"), ("k", "n"), ("m", "k"), ("m", "n")])
 def test_dense_accum_long_k(O, amaj, bmaj):
-    """Accumulation with 32 or more whole K tiles of 64, where D joins the accumulators inside
-    the K loop (one 32 x 32 block per two or more K tiles): ragged M and N edges, a ragged K
-    tail, both signs; then A = 0, where D must come back bit for bit under either sign."""
+    """Accumulation after a long K loop (32 or more whole K tiles of 64; the epilogue adds D to
+    the sum once): ragged M and N edges, a ragged K tail, both signs; then A = 0, where D must
+    come back bit for bit under either sign."""
     rng = np.random.default_rng([7, ord(amaj), ord(bmaj)])
     for i, (M, N, K) in enumerate([(300, 260, 2088), (256, 512, 2048), (130, 300, 4112)]):
         A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", amaj, bmaj)
@@ -148,6 +148,28 @@ def test_dense_accum_long_k(O, amaj, bmaj):
         say("dense accum long K with A = 0", amaj, bmaj, neg_a)
         D = run_dense(M, N, K, "bf16", np.zeros_like(A), lda, amaj, B, ldb, bmaj, d0, neg_a, 0, 1)
         assert np.array_equal(D[:, :N], d0)
+
+
+@pytest.mark.parametrize("amaj,bmaj", [("m", "n"), ("k", "n")])
+def test_dense_ragged_copies_repeated(O, amaj, bmaj):
+    """Regression for the copies' hardware wait states (the 5 a vector-memory read of a
+    VALU-written SGPR base needs, which inline assembly must pad for itself): without them,
+    ragged MN-major accumulating GEMMs came out wrong on some runs and right on others. Each
+    case runs five times; every run must meet the bound and match the first bit for bit."""
+    rng = np.random.default_rng([11, ord(amaj), ord(bmaj)])
+    for M, N, K in [(300, 520, 200), (96, 272, 1000), (513, 130, 456)]:
+        A, lda, B, ldb = dense_case(rng, M, N, K, "bf16", amaj, bmaj)
+        d0 = rng.standard_normal((M, N)).astype(np.float32)
+        ref, bound = O.gemm(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj, d0, N, 1, 0, 1)
+        first_run = None
+        for rep in range(5):
+            say("dense ragged repeated", amaj, bmaj, M, N, K, "run", rep)
+            D = run_dense(M, N, K, "bf16", A, lda, amaj, B, ldb, bmaj, d0, 1, 0, 1)
+            nb, first, worst = O.check_gemm(D, ref, bound, TOL_DENSE)
+            assert nb == 0, (M, N, K, rep, first, worst)
+            if first_run is None:
+                first_run = D
+            assert np.array_equal(D.view(np.uint32), first_run.view(np.uint32)), (M, N, K, rep)
 
 
 @pytest.mark.parametrize("M,N,K,amaj,bmaj", [(1, 300, 131112, "k", "n"), (300, 1, 131072, "m", "k"),

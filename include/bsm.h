@@ -351,7 +351,8 @@ void bsm_debug_fragment_shape(int64_t* rows, int64_t* kdim);
 int bsm_debug_stream_mix_bf16(const void* src, void* dst, void* add, int64_t n, void* stream);
 
 /* Diagnostic: workgroups x 256 lanes of back-to-back MFMAs on random register operands,
- * 16 independent 32x32 accumulators per wave (the GEMMs' layout), iters x 16 MFMAs per wave,
+ * 16 independent 32x32 accumulators per wave (the block-scaled GEMMs' layout; the dense GEMM
+ * runs 16x16x32 blocks, which hold a slightly higher clock), iters x 16 MFMAs per wave,
  * no memory or LDS traffic: the matrix-pipe rate the device holds under that load ([MMA]
  * "Example: four K16 issues": the MMA issue stream alone). kind: BSM_BF16 (v_mfma_f32_32x32x16_bf16,
  * 32768 FLOP each), BSM_E4M3 or BSM_E2M1 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales,

@@ -528,12 +528,27 @@ def cpu_baseline(inp):
     parity["box_copy"] = {"sample": "a 1024x8190 band (128 boxes wide), store and reduce-add, padding included",
                           "bit_exact": bool(all(same))}
     base = {"value": flops / t_gemm / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"GEMM rows: bf16 {rows_bf16} of 8192, mxfp8 {rows_fp8} of 8192, mxfp4 {rows_fp4} of 16384 "
                       f"(full N and K), "
                       f"{t_gemm:.1f} s; box copy on a 1024x8190 band: {box_gbs:.3f} GB/s in {t_box:.1f} s",
             "box_copy_GBs": box_gbs,
             "per_config": dict(per_cfg, box_copy={"rows": 1024, "s": round(t_box, 2), "GB/s": box_gbs})}
     return base, parity
+
+
+def host_cpu():
+    """The host CPU the oracle ran on: its model name and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cores_allowed": len(os.sched_getaffinity(0))}
 
 
 # rocprofv3 kernel names -> bench row names (first match wins). Two k_box_copy2d groups are

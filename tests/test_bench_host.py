@@ -123,3 +123,9 @@ def test_committed_profiles_match_the_sources(bench_name):
         rows = [l.split() for l in fh if l.startswith("traffic: ")]
     hashes = {r[1]: r[3] for r in rows}
     assert hashes.get(bench_name) == bench.source_hash(bench_name)
+
+
+def test_host_cpu_names_the_model_and_the_allowed_cores():
+    h = bench.host_cpu()
+    assert isinstance(h["model"], str) and h["model"]
+    assert h["cores_allowed"] == len(os.sched_getaffinity(0)) >= 1

@@ -6,6 +6,11 @@ import os
 import subprocess
 import tempfile
 
+try:
+    from . import _asm_audit
+except ImportError:  # run as a script
+    import _asm_audit
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsm.so")
@@ -39,12 +44,23 @@ def check_report(src: str, stderr: str) -> list:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, REPORT, "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-    for line in check_report(src, r.stderr):
-        print(line)
+    """Compiles one source. The GEMM sources keep their gfx950 assembly (-save-temps, which
+    leaves the generated code unchanged), and the build stops if it misses a wait state that
+    inline assembly must provide itself (_asm_audit)."""
+    audit = src.startswith("k_gemm")
+    with tempfile.TemporaryDirectory(prefix="bsm_asm_") as tmp:
+        cmd = [HIPCC, *FLAGS, REPORT, *(["-save-temps"] if audit else []), "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=tmp)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        for line in check_report(src, r.stderr):
+            print(line)
+        if audit:
+            asm = os.path.join(tmp, src[:-len(".hip")] + "-hip-amdgcn-amd-amdhsa-gfx950.s")
+            with open(asm) as f:
+                bad = _asm_audit.audit(f.read())
+            if bad:
+                raise RuntimeError(f"{src}: {len(bad)} missing wait state(s) in the assembly, e.g. {bad[0]}")
 
 
 def build(jobs: int = min(8, os.cpu_count() or 4)) -> str:

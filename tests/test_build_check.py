@@ -33,3 +33,52 @@ def test_spill_outside_the_gemm_sources_is_allowed():
 
 def test_build_asks_the_compiler_for_the_report():
     assert _build.REPORT == "-Rpass-analysis=kernel-resource-usage"
+
+
+# --- the assembly audit (block_scaled_matrix_amd/_asm_audit.py) on hand-written gfx950 snippets
+
+from block_scaled_matrix_amd import _asm_audit  # noqa: E402
+
+
+def kernel(*body):
+    return "\n".join(["\t.text", "kern:"] + ["\t" + x for x in body] + ["\ts_endpgm", ".Lfunc_end0:"])
+
+
+def test_copy_right_after_the_readfirstlane_of_its_base_is_flagged():
+    text = kernel("v_readfirstlane_b32 s4, v1", "v_readfirstlane_b32 s5, v2", "s_mov_b32 m0, s6",
+                  "global_load_lds_dwordx4 v3, s[4:5]")
+    bad = _asm_audit.audit(text)
+    assert any("1 wait states after a VALU write of its SGPR base" in x for x in bad), bad
+    assert any("no wait state after the write of M0" in x for x in bad), bad
+
+
+def test_padded_copy_passes():
+    text = kernel("v_readfirstlane_b32 s4, v1", "v_readfirstlane_b32 s5, v2", "s_nop 4", "s_mov_b32 m0, s6",
+                  "s_nop 0", "global_load_lds_dwordx4 v3, s[4:5]", "global_load_lds_dword v4, off")
+    assert _asm_audit.audit(text) == []
+
+
+def test_short_path_through_a_branch_is_found():
+    # the fall-through path is long enough, the branch to the label is not
+    text = kernel("v_readfirstlane_b32 s4, v1", "v_readfirstlane_b32 s5, v1", "s_cbranch_scc1 .LBB0_2",
+                  "s_nop 7", "s_nop 7", ".LBB0_2:", "s_mov_b32 m0, s6", "s_nop 0",
+                  "global_load_lds_dwordx4 v3, s[4:5]")
+    bad = _asm_audit.audit(text)
+    assert len(bad) == 1 and "3 wait states after a VALU write of its SGPR base" in bad[0], bad
+    # a loop back edge: the write at the bottom of the loop reaches the copy at its top
+    loop = [".LBB0_1:", "s_mov_b32 m0, s6", "s_nop 0", "global_load_lds_dwordx4 v3, s[4:5]", "s_nop 7",
+            "v_readfirstlane_b32 s4, v1", "s_cbranch_scc0 .LBB0_1"]
+    bad = _asm_audit.audit(kernel("s_nop 7", *loop))
+    assert len(bad) == 1 and "3 wait states after a VALU write of its SGPR base" in bad[0], bad
+    assert _asm_audit.audit(kernel("s_nop 7", loop[0], "s_nop 1", *loop[1:])) == []
+
+
+def test_mfma_reading_a_fresh_conversion_is_flagged_and_two_wait_states_pass():
+    cvt = "v_cvt_scalef32_pk32_bf16_fp6 v[0:15], v[16:21], v22"
+    mfma = "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[24:27], a[0:15]"
+    bad = _asm_audit.audit(kernel(cvt, mfma))
+    assert len(bad) == 1 and "0 wait states after a VALU write of its A/B VGPRs" in bad[0], bad
+    assert len(_asm_audit.audit(kernel(cvt, "s_nop 0", mfma))) == 1
+    assert _asm_audit.audit(kernel(cvt, "s_nop 1", mfma)) == []
+    # an MFMA writing the registers is not a VALU write for this rule
+    assert _asm_audit.audit(kernel("v_mfma_f32_16x16x32_bf16 v[4:7], v[8:11], v[12:15], v[4:7]", mfma)) == []

@@ -7,7 +7,11 @@ Checked along every control-flow path into the instruction (fall-through and bra
     instruction last wrote one of those SGPRs, at least 1 since M0 was last written by the
     SALU (5 if the VALU wrote it);
   - an MFMA: at least 2 wait states since a VALU instruction (other than an MFMA) last wrote a
-    VGPR of its A or B operand.
+    VGPR of its A or B operand;
+  - any other instruction reading an MFMA's result registers (accumulator reads, VALU, stores):
+    at least passes + 3 wait states after that MFMA, with the passes of its shape (4 for
+    16x16x32 bf16/f16, 8 for 32x32x16 bf16/f16, 16 for the 32x32x64 block-scaled MFMA with an
+    8-bit operand and 8 without, half that for the 16x16x128 one; 16 for any other MFMA).
 A wait state is one issued instruction; s_nop N counts N + 1.
 """
 from __future__ import annotations
@@ -116,6 +120,36 @@ def _min_since(f, i: int, hit, need: int) -> int:
     return best
 
 
+def _passes(ins) -> int:
+    """Passes of an MFMA: the block-scaled shapes run at half length when neither operand is
+    8-bit (format codes cbsz / blgp: 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1)."""
+    op, ops = ins
+    if op.startswith("v_mfma_f32_16x16x32_"):
+        return 4
+    if op.startswith("v_mfma_f32_32x32x16_"):
+        return 8
+    if op.startswith("v_mfma_scale_f32_"):
+        mods = " ".join(ops)
+        codes = [int(m) for m in re.findall(r"(?:cbsz|blgp):(\d+)", mods)]
+        narrow = len(codes) == 2 and min(codes) >= 2
+        full = 8 if op.startswith("v_mfma_scale_f32_16x16x128") else 16
+        return full // 2 if narrow else full
+    return 16
+
+
+def _reads(ins) -> set:
+    """Registers an instruction reads (every operand but the destination; stores read all)."""
+    op, ops = ins
+    if op.startswith(("global_store", "buffer_store", "scratch_store", "flat_store", "ds_write")):
+        toks = ops
+    else:
+        toks = ops[1:]
+    r = set()
+    for t in toks:
+        r |= _regs(t)
+    return r
+
+
 def audit(text: str) -> list:
     """Violations as strings (empty when the assembly keeps every wait state above)."""
     out = []
@@ -142,4 +176,27 @@ def audit(text: str) -> list:
                                and bool(_writes(x) & src), 2)
                 if w < 2:
                     out.append(f"{f['name']}: {op} #{i}: {w} wait states after a VALU write of its A/B VGPRs")
+            if not op.startswith("v_mfma"):
+                rd = {r for r in _reads((op, ops)) if r[0] in "va"}
+                if not rd:
+                    continue
+                hit = lambda x: x[0].startswith("v_mfma") and bool(_writes(x) & rd)
+                w = _min_since(f, i, hit, 19)
+                if w < 19:
+                    # the nearest MFMA writing what this reads: its shape sets the requirement
+                    need = _min_need(f, i, rd)
+                    if w < need:
+                        out.append(f"{f['name']}: {op} #{i}: {w} wait states after an MFMA wrote what it reads "
+                                   f"(needs {need})")
     return out
+
+
+def _min_need(f, i: int, rd: set) -> int:
+    """passes + 3 of the MFMA that last wrote any of rd on the fall-through path before i
+    (the largest such requirement among the nearest writers, 19 if none is found nearby)."""
+    ins = f["ins"]
+    for j in range(i - 1, max(i - 200, -1), -1):
+        op = ins[j][0]
+        if op.startswith("v_mfma") and _writes(ins[j]) & rd:
+            return _passes(ins[j]) + 3
+    return 19

@@ -82,3 +82,27 @@ def test_mfma_reading_a_fresh_conversion_is_flagged_and_two_wait_states_pass():
     assert _asm_audit.audit(kernel(cvt, "s_nop 1", mfma)) == []
     # an MFMA writing the registers is not a VALU write for this rule
     assert _asm_audit.audit(kernel("v_mfma_f32_16x16x32_bf16 v[4:7], v[8:11], v[12:15], v[4:7]", mfma)) == []
+
+
+def test_reading_an_mfma_result_too_soon_is_flagged():
+    mfma = "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]"   # 8 passes: 11 wait states
+    bad = _asm_audit.audit(kernel(mfma, "s_nop 7", "v_accvgpr_read_b32 v0, a3"))
+    assert len(bad) == 1 and "8 wait states after an MFMA wrote what it reads (needs 11)" in bad[0], bad
+    assert _asm_audit.audit(kernel(mfma, "s_nop 7", "s_nop 2", "v_accvgpr_read_b32 v0, a3")) == []
+    # a store of the result counts as a read; an untouched register does not
+    assert len(_asm_audit.audit(kernel(mfma, "ds_write_b128 v1, a[0:3]"))) == 1
+    assert _asm_audit.audit(kernel(mfma, "v_accvgpr_read_b32 v0, a16")) == []
+    # the 16x16x32 shape (4 passes) needs 7
+    m16 = "v_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], a[0:3]"
+    assert len(_asm_audit.audit(kernel(m16, "s_nop 5", "v_accvgpr_read_b32 v0, a1"))) == 1
+    assert _asm_audit.audit(kernel(m16, "s_nop 6", "v_accvgpr_read_b32 v0, a1")) == []
+
+
+def test_block_scaled_mfma_passes_follow_the_operand_formats():
+    fp8 = "v_mfma_scale_f32_32x32x64_f8f6f4 a[0:15], v[0:7], v[8:15], a[0:15], v16, v17 op_sel_hi:[0,0,0]"
+    fp4 = "v_mfma_scale_f32_32x32x64_f8f6f4 a[0:15], v[0:3], v[8:11], a[0:15], v16, v17 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+    mixed = "v_mfma_scale_f32_32x32x64_f8f6f4 a[0:15], v[0:7], v[8:11], a[0:15], v16, v17 op_sel_hi:[0,0,0] blgp:4"
+    wait = ["s_nop 7", "s_nop 7", "s_nop 1"]                      # 18 wait states
+    assert len(_asm_audit.audit(kernel(fp8, *wait, "v_accvgpr_read_b32 v0, a3"))) == 1   # needs 19
+    assert _asm_audit.audit(kernel(fp4, *wait, "v_accvgpr_read_b32 v0, a3")) == []       # needs 11
+    assert len(_asm_audit.audit(kernel(mixed, *wait, "v_accvgpr_read_b32 v0, a3"))) == 1

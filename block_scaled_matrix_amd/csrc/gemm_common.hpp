@@ -32,10 +32,24 @@ __device__ __forceinline__ uint64_t sgpr_base(const void* p) {
   asm("s_nop 4" : "+s"(lo), "+s"(hi));
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
-__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t sb = sgpr_base(base);
+// Two bases pinned with one s_nop 4 (the A and B tiles of one K tile).
+__device__ __forceinline__ void sgpr_base2(const void* p, const void* q, uint64_t& sp, uint64_t& sq) {
+  const uint64_t bp = (uint64_t)p, bq = (uint64_t)q;
+  uint32_t plo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+  uint32_t phi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32));
+  uint32_t qlo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bq);
+  uint32_t qhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bq >> 32));
+  asm("s_nop 4" : "+s"(plo), "+s"(phi), "+s"(qlo), "+s"(qhi));
+  sp = ((uint64_t)phi << 32) | (uint64_t)plo;
+  sq = ((uint64_t)qhi << 32) | (uint64_t)qlo;
+}
+// The copy from a base that sgpr_base / sgpr_base2 produced (or SALU arithmetic on one).
+__device__ __forceinline__ void dma16u(uint64_t sb, uint32_t voff, uint32_t lds_addr) {
   const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(a) : "memory");
+}
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  dma16u(sgpr_base(base), voff, lds_addr);
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -45,10 +59,12 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 
 // Direct HBM -> LDS copy of 4 bytes per lane (lane l lands at lds_addr + 4 * l), the same
 // way as dma16s.
-__device__ __forceinline__ void dma4s(const void* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t sb = sgpr_base(base);
+__device__ __forceinline__ void dma4u(uint64_t sb, uint32_t voff, uint32_t lds_addr) {
   const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb), "{m0}"(a) : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  dma4u(sgpr_base(base), voff, lds_addr);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

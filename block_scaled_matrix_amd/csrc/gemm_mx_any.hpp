@@ -583,6 +583,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
   }
   const uint8_t* SA = a.SFA + m0 * a.ld_sfa;
   const uint8_t* SB = a.SFB + n0 * a.ld_sfb;
+  uint64_t sSA, sSB;                       // the scale bases pinned once for the slice copies
+  gemm::sgpr_base2(SA, SB, sSA, sSB);
   const uint32_t lds0 = gemm::lds_addr(lds);
   const int nfull = (int)(a.K / KT);
   // Data copy d (of DD) of tile kt into stage `stage`.
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx_any(GemmArgs a, int tiles_m,
     const int64_t rows = op ? rows_b : rows_a;
     const uint32_t off = (uint32_t)(min((int64_t)R, rows - 1) * (op ? a.ld_sfb : a.ld_sfa)) +
                          4u * (uint32_t)min(4 * g + qw, nfull - 1);
-    gemm::dma4s(op ? SB : SA, off, lds0 + L::RING + (g & 1) * L::RING_BUF + op * 4096 + 16 * (64 * j + 16 * (k & 3)));
+    gemm::dma4u(op ? sSB : sSA, off, lds0 + L::RING + (g & 1) * L::RING_BUF + op * 4096 + 16 * (64 * j + 16 * (k & 3)));
   };
   // Batch b (issued once tile b's stage has been read): quarter (b + 5) % 4 of scale group
   // (b + 5) / 4, then the data of tile kb into stage `stage`. Group g's buffer is free once

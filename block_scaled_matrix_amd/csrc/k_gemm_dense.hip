@@ -284,11 +284,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dense(GemmArgs a, int tiles_m, 
     const uint8_t* na = lds + ((kt + 1) & 1) * STAGE_BYTES;
     const uint32_t stage = lds0 + (kt & 1) * STAGE_BYTES;
     const int64_t k2 = (int64_t)min(kt + 2, nfull - 1) * BK;
-    const uint16_t* ga = tile_base<AK>(A, a.lda, m0, k2);
-    const uint16_t* gb = tile_base<BKM>(B, a.ldb, n0, k2);
+    uint64_t ga, gb;
+    gemm::sgpr_base2(tile_base<AK>(A, a.lda, m0, k2), tile_base<BKM>(B, a.ldb, n0, k2), ga, gb);
     auto copy = [&](int d) {
-      if (d < 8) gemm::dma16s(ga, aoff[d], stage + 1024 * (w + 4 * d));
-      else gemm::dma16s(gb, boff[d - 8], stage + TILE_BYTES + 1024 * (w + 4 * (d - 8)));
+      if (d < 8) gemm::dma16u(ga, aoff[d], stage + 1024 * (w + 4 * d));
+      else gemm::dma16u(gb, boff[d - 8], stage + TILE_BYTES + 1024 * (w + 4 * (d - 8)));
     };
     // Side work by MFMA slot g (0..63 step 0, 64..127 step 1): step 1's 16 fragment reads at
     // every second slot from 0; barrier once every wave has read the stage; the 16 copies of

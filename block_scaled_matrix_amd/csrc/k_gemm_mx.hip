@@ -66,14 +66,15 @@ struct Ops {
   const uint8_t* B; uint32_t boff[8];
   const uint8_t* SFA; uint32_t ld_sfa; int lim_a;  // lim: last valid tile row (<= 255)
   const uint8_t* SFB; uint32_t ld_sfb; int lim_b;
+  uint64_t sfa, sfb;                               // SFA, SFB as pinned copy bases (gemm::sgpr_base2)
   int ldw;                                         // scale words per row that may be read
 };
 
-// Copy d of the 16 operand copies of one K tile (8 of A, then 8 of B) into `stage`.
-__device__ __forceinline__ void issue_data(const Ops& o, const uint8_t* ga, const uint8_t* gb, int d, uint32_t stage,
-                                           int w) {
-  if (d < 8) gemm::dma16s(ga, o.aoff[d], stage + 1024 * (w + 4 * d));
-  else gemm::dma16s(gb, o.boff[d - 8], stage + TILE_BYTES + 1024 * (w + 4 * (d - 8)));
+// Copy d of the 16 operand copies of one K tile (8 of A, then 8 of B) into `stage`, from the
+// tile's A and B bases pinned together (gemm::sgpr_base2).
+__device__ __forceinline__ void issue_data(const Ops& o, uint64_t ga, uint64_t gb, int d, uint32_t stage, int w) {
+  if (d < 8) gemm::dma16u(ga, o.aoff[d], stage + 1024 * (w + 4 * d));
+  else gemm::dma16u(gb, o.boff[d - 8], stage + TILE_BYTES + 1024 * (w + 4 * (d - 8)));
 }
 
 // Scale ring. Row R of an operand's group buffer holds the 8 scale words of K tiles
@@ -97,9 +98,9 @@ __device__ __forceinline__ void issue_slice(const Ops& o, int g, int j, int c, u
   const int p = lane & 7;  // physical word
   const int q = 2 * ((p >> 1) ^ ring_s2(R)) + (p & 1);
   const uint32_t word = (uint32_t)min(8 * g + q, o.ldw - 1);
-  const uint8_t* base = op ? o.SFB : o.SFA;
+  const uint64_t base = op ? o.sfb : o.sfa;
   const uint32_t off = (uint32_t)min(R, op ? o.lim_b : o.lim_a) * (op ? o.ld_sfb : o.ld_sfa) + 4 * word;
-  gemm::dma4s(base, off, ring + (g & 1) * RING_GROUP + op * RING_OP + 32 * (j * F::SLICE_ROWS + 8 * ii));
+  gemm::dma4u(base, off, ring + (g & 1) * RING_GROUP + op * RING_OP + 32 * (j * F::SLICE_ROWS + 8 * ii));
 }
 
 // Raw scale words for this lane's rows (wave base + 32t + l%32): the pair holding K tile kt's
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
   o.lim_a = (int)min(a.M - 1 - m0, (int64_t)255);
   o.lim_b = (int)min(a.N - 1 - n0, (int64_t)255);
   o.ldw = (int)(min(a.ld_sfa, a.ld_sfb) / 4);
+  gemm::sgpr_base2(o.SFA, o.SFB, o.sfa, o.sfb);
 
   const int nfull = (int)(a.K / F::KT);
   const int tail = (int)(a.K % F::KT);
@@ -283,10 +285,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
 #pragma unroll
     for (int c = 0; c < F::SLICE_COPIES; c++) issue_slice<FMT>(o, 1, 0, c, ring, w, lane);
     const int k1 = min(1, nfull - 1);
+    uint64_t sa0, sb0, sa1, sb1;
+    gemm::sgpr_base2(o.A, o.B, sa0, sb0);
 #pragma unroll
-    for (int d = 0; d < 16; d++) issue_data(o, o.A, o.B, d, lds0, w);
+    for (int d = 0; d < 16; d++) issue_data(o, sa0, sb0, d, lds0, w);
+    gemm::sgpr_base2(o.A + k1 * ROWB, o.B + k1 * ROWB, sa1, sb1);
 #pragma unroll
-    for (int d = 0; d < 16; d++) issue_data(o, o.A + k1 * ROWB, o.B + k1 * ROWB, d, lds0 + STAGE, w);
+    for (int d = 0; d < 16; d++) issue_data(o, sa1, sb1, d, lds0 + STAGE, w);
     gemm::stage_barrier<16>();
     read_frags<FMT>(lds, 0, wa, wb, lane, f0);
     read_scales<FMT>(lds, 0, wa, wb, lane, ra, rb);
@@ -305,8 +310,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(GemmArgs a, int tiles_m, int
     const uint8_t* nst = lds + ((kt + 1) & 1) * STAGE;
     const uint32_t stage = lds0 + (kt & 1) * STAGE;
     const int64_t k2 = (int64_t)min(kt + 2, nfull - 1) * ROWB;
-    const uint8_t* ga = o.A + k2;
-    const uint8_t* gb = o.B + k2;
+    uint64_t ga, gb;
+    gemm::sgpr_base2(o.A + k2, o.B + k2, ga, gb);
     const int sg = (kt + 1) / F::G + 1, sj = (kt + 1) % F::G;
     // copy d of this iteration: operand copies 0..15, then the scale slice copies
     auto copy = [&](int d) {
